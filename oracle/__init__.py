@@ -1,0 +1,29 @@
+"""fp64 CPU oracle for paged decode attention and the KV-cache operations.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only the tests, the smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+(no kernels, headers, tables or helpers) and does not import it.
+
+What it computes, and from where:
+
+* ``attention.paged_decode`` -- PagedAttention computes exactly the result of
+  ordinary attention over each sequence's own tokens; only the storage is
+  paged.  So the oracle gathers each sequence's keys and values through its
+  block table into dense arrays (the "gather then concat" route the mlqm.cn
+  explainer describes for nano-vLLM) and evaluates
+  softmax(scale * q K^T) V in float64 (the attention formula of the "Vllm"
+  agent-guide page, section "transformer").
+* ``attention.partitioned_decode`` -- the same result computed partition by
+  partition and combined with the log-sum-exp rule (the KV-splitting idea of
+  FlashDecoding / TurboMind split-K decoding, "Prefill vs decoding" item 5 of
+  the "Vllm" page and the LMDeploy section of the AIGC interview book).
+* ``cache_ops`` -- the three cache-maintenance operations: the slot scatter
+  of nano-vLLM's KV-cache write (cybasar.com nano-vLLM article, section
+  5.2.3) in the block layout of the "Vllm" page's "CacheEngine" section, and
+  CacheEngine's copy_blocks / swap_blocks.
+
+Parity pins (tests/test_oracle_*.py) tie every function to something other
+than itself: a library SDPA on dense inputs, closed forms, invariants, and the
+worked examples the pages print.
+"""

@@ -1,0 +1,159 @@
+"""fp64 oracle for single-query decode attention over a block-paged KV cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources for each step:
+
+* Block layout -- "Vllm" agent-guide page, section "CacheEngine": a key block
+  has shape [num_heads, head_size // x, block_size, x] with
+  x = 16 // sizeof(dtype); a value block has shape [num_heads, head_size,
+  block_size].  The pool of blocks is the outer dimension (the pages give
+  only the per-block shape; the plainest reading puts the block index first).
+* Addressing -- mlqm.cn vLLM explainer, section "1、PagedAttention": a
+  sequence's block table lists its physical blocks in logical order, 16
+  tokens per block, so token t sits in table[t // block_size] at offset
+  t % block_size.
+* Attention -- "Vllm" page, section "transformer":
+  softmax(Q K^T / sqrt(d_k)) V.  The caller's ``scale`` replaces
+  1 / sqrt(d_k) (every workload passes 1 / sqrt(head_size)).
+* Decode -- "Vllm" page, section "transformer" (decoding paragraph): the new
+  token's K, V are appended to the cache and its query attends to the whole
+  cache, so ``context_lens`` counts the new token.
+* Gather-then-dense -- mlqm.cn explainer, nano-vLLM "Attention 计算的妥协
+  Gather 机制": collect the blocks named by the block table into one dense
+  tensor, then run ordinary attention.
+* Grouped-query attention (GQA is only named on the pages, "推理优化" on the
+  "Vllm" page): query head h reads KV head h // (num_heads // num_kv_heads).
+* A sequence of length 0 attends to nothing; its output is defined as 0.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored elements given as raw bits.
+
+    ``dtype`` is 'f32' (uint32 bits), 'f16' (uint16, IEEE binary16) or
+    'bf16' (uint16: the upper half of an IEEE binary32, so shifting the bits
+    left by 16 gives the binary32 with the same value).
+    """
+    if dtype == "f32":
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def chunk_width(bits: np.ndarray) -> int:
+    """x = 16 bytes / element size."""
+    return 16 // bits.dtype.itemsize
+
+
+def gather_kv(key_bits: np.ndarray, value_bits: np.ndarray, dtype: str, table_row: np.ndarray,
+              L: int, kv_head: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense K[t, d], V[t, d] (float64, t < L) of one sequence and one KV head.
+
+    K[t, d] = key_cache[table[t // bs], kv_head, d // x, t % bs, d % x]
+    V[t, d] = value_cache[table[t // bs], kv_head, d, t % bs]
+    """
+    bs = key_bits.shape[3]
+    x = key_bits.shape[4]
+    D = value_bits.shape[2]
+    assert x == chunk_width(key_bits) and key_bits.shape[2] * x == D
+    t = np.arange(L)
+    d = np.arange(D)
+    blk = np.asarray(table_row, dtype=np.int64)[t // bs]
+    off = t % bs
+    K = key_bits[blk[:, None], kv_head, (d // x)[None, :], off[:, None], (d % x)[None, :]]
+    V = value_bits[blk[:, None], kv_head, d[None, :], off[:, None]]
+    return widen(K, dtype), widen(V, dtype)
+
+
+def dense_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * K q) V for one query vector, in float64.  Empty context -> 0."""
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    s = scale * (K @ q)
+    m = s.max()
+    p = np.exp(s - m)
+    return (p @ V) / p.sum()
+
+
+def as_scale(scale: float) -> float:
+    """The float32 value the kernel receives, widened exactly."""
+    return float(np.float32(scale))
+
+
+def paged_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
+                 dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
+                 pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """Output [B, Hq, D] in float64 (or only the (b, h) in ``pairs``; other rows stay NaN).
+
+    ``query_bits`` [B, Hq, D], ``key_bits`` [NB, Hkv, D/x, bs, x],
+    ``value_bits`` [NB, Hkv, D, bs] hold raw storage bits of ``dtype``.
+    """
+    B, Hq, D = query_bits.shape
+    Hkv = key_bits.shape[1]
+    assert Hq % Hkv == 0
+    group = Hq // Hkv
+    sc = as_scale(scale)
+    out = np.full((B, Hq, D), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(Hq)]
+    by_seq_head = {}
+    for b, h in pairs:
+        by_seq_head.setdefault((b, h // group), []).append(h)
+    for (b, g), heads in sorted(by_seq_head.items()):
+        L = int(context_lens[b])
+        K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, g)
+        for h in heads:
+            q = widen(query_bits[b, h], dtype)
+            out[b, h] = dense_decode(q, K, V, sc)
+    return out
+
+
+def partition_stats(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, start: int,
+                    stop: int) -> Tuple[float, float, np.ndarray]:
+    """(m_p, l_p, acc_p) of tokens [start, stop): max logit, sum of exp(s - m_p), sum of exp(s - m_p) V."""
+    s = scale * (K[start:stop] @ q)
+    m = s.max()
+    p = np.exp(s - m)
+    return float(m), float(p.sum()), p @ V[start:stop]
+
+
+def combine_partitions(stats) -> np.ndarray:
+    """Log-sum-exp combination of per-partition (m_p, l_p, acc_p):
+    out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p."""
+    M = max(m for m, _, _ in stats)
+    num = sum(np.exp(m - M) * acc for m, _, acc in stats)
+    den = sum(np.exp(m - M) * l for m, l, _ in stats)
+    return num / den
+
+
+def partitioned_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
+                       dtype: str, block_tables: np.ndarray, context_lens: np.ndarray,
+                       scale: float, partition_size: int) -> np.ndarray:
+    """The same output computed over ``partition_size``-token slices of each context, then combined."""
+    B, Hq, D = query_bits.shape
+    Hkv = key_bits.shape[1]
+    group = Hq // Hkv
+    sc = as_scale(scale)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, g)
+            for h in range(g * group, (g + 1) * group):
+                q = widen(query_bits[b, h], dtype)
+                stats = [partition_stats(q, K, V, sc, s0, min(s0 + partition_size, L))
+                         for s0 in range(0, L, partition_size)]
+                out[b, h] = combine_partitions(stats)
+    return out
