@@ -1,0 +1,195 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: reshape_and_cache of each sequence's newest
+token into its slot, then paged decode attention (partition kernel + split-K reduce).
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line.  `value` is the step's algorithmic bytes (every context token's K
+and V for all KV heads, q in, out, block ids, lengths, plus the new tokens' K/V read and
+written) divided by the step time: achieved GB/s.  `roofline` covers the dominant kernel
+(the partition kernel), timed with HIP events on the stream it is launched on;
+`cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E spec peak
+WORKLOADS = {
+    "c1": "tiny paged decode: batch 4, 8 heads, head 64, block 16, fp32",
+    "c2": "MHA decode, 7B-like layer: batch 64, 32 heads, head 128, block 16, fp16",
+    "c3": "GQA decode: batch 256, 32 q heads / 8 KV heads, head 128, block 16, bf16, lognormal lengths",
+    "c4": "long-context split-K: batch 8, 64 q / 8 KV heads, head 128, block 32, bf16, 131072 tokens",
+}
+KERNEL_SOURCES = ["attention_valu.hip", "attention_mfma.hip", "pkv_device.h", "pkv_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "paged_kv_cache_164_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the partition kernel from committed rocprofv3 counter runs, or
+    None when absent or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"partition_kernel_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The fp64 oracle (unchanged) on the first sequences of the same workload, until the
+    time budget is spent; throughput in the metric's unit (algorithmic GB/s)."""
+    from threadpoolctl import threadpool_info
+
+    import paged_kv_cache_164_amd as pkv
+    from oracle import attention as OA
+    from oracle import cache_ops as OC
+    from workloads import storage_bits
+
+    cfg = case.cfg
+    kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+    lens = case.context_lens.numpy()
+    tables = case.block_tables.numpy()
+    qbits = storage_bits(case.query)
+    nk, nv = storage_bits(case.new_key), storage_bits(case.new_value)
+    slots = case.slot_mapping.numpy()
+    Hq, D = case.query.shape[1], case.query.shape[2]
+    Hkv = case.key_cache.shape[1]
+    eb = case.query.element_size()
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    while done < len(lens) and (time.perf_counter() - t0) < budget_s:
+        b = done
+        OC.reshape_and_cache(kb, vb, nk[b:b + 1], nv[b:b + 1], slots[b:b + 1])
+        OA.paged_decode(qbits[b:b + 1], kb, vb, cfg.dtype, tables[b:b + 1], lens[b:b + 1], case.scale)
+        nbytes += pkv.decode_bytes(lens[b:b + 1], Hq, Hkv, D, cfg.block_size, eb) + 4 * Hkv * D * eb + 8
+        done += 1
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done} of {len(lens)} sequences ({int(lens[:done].sum())} KV tokens, "
+                      f"all {Hq} query heads), {dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_164_amd as pkv
+    from workloads import make_decode_case
+
+    t_gen = time.perf_counter()
+    case = make_decode_case(args.workload)
+    print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    q = case.query.to(dev)
+    kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
+    bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
+    nk, nv, slots = case.new_key.to(dev), case.new_value.to(dev), case.slot_mapping.to(dev)
+    out = torch.empty_like(q)
+    B, Hq, D = q.shape
+    Hkv, bs = kc.shape[1], kc.shape[3]
+    eb = q.element_size()
+    lmax = case.max_context_len
+    P = args.partition
+    need = pkv.paged_attention_workspace_size(B, Hq, D, lmax, P)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, case.scale, lmax, P, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = [a.elapsed_time(b) for a, b in events]
+    k_avg = float(np.mean(k_ms))
+
+    lens = case.context_lens.numpy()
+    dec_bytes = pkv.decode_bytes(lens, Hq, Hkv, D, bs, eb)
+    write_bytes = 2 * 2 * int((lens > 0).sum()) * Hkv * D * eb + 8 * B
+    step_bytes = dec_bytes + write_bytes
+    gbs = step_bytes / (ms_step / 1e3) / 1e9
+    kernel_gbs = dec_bytes / (k_avg / 1e3) / 1e9
+    traffic = traffic_from_profile(args.workload)
+    rec = {
+        "metric": "paged decode attention achieved HBM GB/s (% of peak) and KV-tokens/s, 1 GPU",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
+                   "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
+                   "partition_size": P or 512, "kv_tokens": int(lens.sum()), "max_context_len": lmax,
+                   "step_bytes": step_bytes},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "partition kernel (phase 1)",
+                     "kernel_ms": round(k_avg, 5), "kernel_ms_p10_p90":
+                         [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
+                     "algorithmic_bytes_per_launch": dec_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,203 @@
+/*
+ * pkv -- paged KV-cache decode attention and cache maintenance for MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; no C++ or framework types cross it.
+ *
+ * Storage layout of the KV cache (the "Vllm" page of the yang20150702 agent
+ * guide, section "CacheEngine"): with x = 16 / sizeof(element),
+ *   key block   [num_kv_heads, head_size / x, block_size, x]
+ *   value block [num_kv_heads, head_size, block_size]
+ * and the pool of physical blocks is the outermost dimension:
+ *   key_cache   [num_blocks, num_kv_heads, head_size / x, block_size, x]
+ *   value_cache [num_blocks, num_kv_heads, head_size, block_size]
+ * Token t of sequence b is at physical block block_tables[b][t / block_size],
+ * offset t % block_size (the mlqm.cn vLLM explainer, "PagedAttention"
+ * block-table description).  A slot is block * block_size + offset (the
+ * tiemojia.cn vLLM 0.10 article, section 3.3 "KV Manager").
+ *
+ * Common rules for every call:
+ *  - Every pointer named "device" must be device memory of the current HIP
+ *    device; the caller owns all buffers.  The library allocates and frees
+ *    nothing during a call and keeps no device state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work on it and return; nothing waits for the GPU, except that
+ *    pkv_swap_blocks reads its host-side block list before returning.
+ *  - Return value: PKV_OK (0) or a negative PKV_ERR_* code; then nothing was
+ *    enqueued and pkv_last_error() gives a message for the calling thread.
+ *  - No exception crosses the ABI.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types; x = 16 / sizeof: 4 for PKV_F32, 8 for PKV_F16 and PKV_BF16 */
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* a size or id out of range, or inconsistent */
+  PKV_ERR_UNSUPPORTED = -2,   /* valid but not built: head_size, block_size, group size */
+  PKV_ERR_NULL_POINTER = -3,
+  PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -5,           /* a HIP runtime call failed (message has the HIP error) */
+  PKV_ERR_NOT_PINNED = -6     /* swap_blocks host side is not page-locked host memory */
+};
+
+enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1 /* device -> host */ };
+
+/*
+ * Single-query decode attention over the paged cache (PagedAttention).
+ *
+ * Computes, for every sequence b and query head h (the "Vllm" page, section
+ * "transformer": softmax(Q K^T / sqrt(d_k)) V, one query row per sequence at
+ * decode time):
+ *   g = h / (num_heads / num_kv_heads)           (grouped-query head map)
+ *   s_t = scale * sum_d query[b][h][d] * K_b[t][g][d],  t < context_lens[b]
+ *   out[b][h][:] = sum_t softmax(s)_t * V_b[t][g][:]
+ * where K_b, V_b are the sequence's tokens reached through block_tables.
+ * Accumulation is fp32; out is rounded to the element type (round to nearest
+ * even).  context_lens[b] == 0 gives out[b] = 0.
+ *
+ * Long contexts are split into partitions of `partition_size` tokens, each
+ * handled by its own workgroup; sequences with more than one partition are
+ * combined by a second kernel with the log-sum-exp rule (split-K decoding,
+ * the "Vllm" page, "Prefill vs decoding" item 5 on FlashDecoding).
+ *
+ * Arguments (device unless stated):
+ *   out          [num_seqs, num_heads, head_size] element type, written
+ *   query        [num_seqs, num_heads, head_size] element type
+ *   key_cache    [num_blocks, num_kv_heads, head_size/x, block_size, x]
+ *   value_cache  [num_blocks, num_kv_heads, head_size, block_size]
+ *   block_tables int32 [num_seqs, max_num_blocks_per_seq]; entries past
+ *                ceil(context_lens[b] / block_size) are never read
+ *   context_lens int32 [num_seqs]; each must be <= max_context_len and
+ *                <= max_num_blocks_per_seq * block_size (larger values are
+ *                clamped to those bounds: no fault, but the result is then
+ *                that of the clamped length)
+ *   scale        host float, usually 1/sqrt(head_size)
+ *   head_size    64 or 128;  block_size 8, 16 or 32
+ *   num_heads    a multiple of num_kv_heads; group size num_heads/num_kv_heads
+ *                in {1, 2, 4, 8} for PKV_F32, 1..16 for PKV_F16/PKV_BF16
+ *   max_context_len  host upper bound of context_lens (sizes the grid)
+ *   partition_size   0 = 512; otherwise a multiple of block_size in
+ *                [block_size, 1024]
+ *   workspace    device scratch of at least
+ *                pkv_paged_attention_workspace_size(...) bytes (may be NULL
+ *                when that size is 0), 256-byte aligned
+ * Physical block ids in block_tables must be valid pool indices: they are
+ * not checked on the device.
+ */
+int pkv_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               const int32_t* context_lens, float scale, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t block_size, int32_t max_num_blocks_per_seq,
+                               int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of split-K scratch needed by the call above (0 when max_context_len
+ * fits one partition): per (sequence, query head, partition) one fp32 running
+ * max, one fp32 running sum and head_size fp32 partial outputs.  Returns 0 for
+ * invalid arguments. */
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                          int32_t max_context_len, int32_t partition_size);
+
+/* The first of the two kernels of pkv_paged_attention_decode, alone: every
+ * (sequence, KV head, partition) workgroup.  Sequences that fit one partition
+ * get their final output in `out`; longer ones leave per-partition partial
+ * results in `workspace` for pkv_paged_attention_reduce.  Same arguments and
+ * rules as pkv_paged_attention_decode. */
+int pkv_paged_attention_partitions(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t block_size, int32_t max_num_blocks_per_seq,
+                                   int32_t max_context_len, int32_t dtype,
+                                   int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* The second kernel alone: for each sequence with more than one partition,
+ * out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p.
+ * Sequences with one partition are left untouched.  Must follow
+ * pkv_paged_attention_partitions on the same stream with the same sizes;
+ * nothing is enqueued when max_context_len fits one partition. */
+int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t head_size, int32_t max_context_len,
+                               int32_t dtype, int32_t partition_size, const void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Scatter new tokens' keys and values into their cache slots (the KV-cache
+ * write of the cybasar.com nano-vLLM article, section 5.2.3, in the block
+ * layout above):
+ *   blk = slot_mapping[i] / block_size, off = slot_mapping[i] % block_size
+ *   key_cache[blk][h][d / x][off][d % x] = key[i][h][d]
+ *   value_cache[blk][h][d][off]          = value[i][h][d]
+ * A negative slot means "skip this token" (the article's -1 sentinel).  Slots
+ * >= num_blocks * block_size are also skipped (never written).
+ *   key, value   device, token i's row starts at element i * key_stride
+ *                (value_stride); inside a row heads are contiguous, then dims
+ *                (the article's stride asserts: stride(-1) == 1,
+ *                stride(1) == head_size)
+ *   slot_mapping device int64 [num_tokens]
+ * Bit-exact copy; no arithmetic on the values.  Distinct tokens must name
+ * distinct slots (otherwise which one lands is unspecified).
+ */
+int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_size, int32_t block_size, int64_t num_blocks,
+                          int64_t key_stride, int64_t value_stride, int32_t dtype, void* stream);
+
+/*
+ * Copy whole blocks inside the device cache, for every layer (CacheEngine
+ * "copy", the "Vllm" page, section "CacheEngine"; the pairs come from the
+ * block manager's copy-on-write, the AIGC interview book section 23,
+ * append_slots).
+ *   key_cache_ptrs, value_cache_ptrs  device uint64 [num_layers]: the base
+ *                address of each layer's key / value cache
+ *   block_mapping device int64 [num_pairs, 2] = (src, dst)
+ *   block_bytes   bytes of one block of one cache (a multiple of 16); the
+ *                 same for keys and values
+ *   num_blocks    blocks per layer cache; pairs with an id outside
+ *                 [0, num_blocks) are skipped
+ * dst ids must be distinct and no dst may also be a src in the same call
+ * (a copy-on-write destination is always a fresh block); otherwise the
+ * result is unspecified.  Bit-exact.
+ */
+int pkv_copy_blocks(const uint64_t* key_cache_ptrs, const uint64_t* value_cache_ptrs,
+                    int32_t num_layers, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t block_bytes, int64_t num_blocks, void* stream);
+
+/*
+ * Move blocks between the device cache and a page-locked host cache
+ * (CacheEngine swap_in = host -> device, swap_out = device -> host; the
+ * host cache is pinned memory, the "Vllm" page, "CacheEngine").  Called once
+ * for keys and once for values.
+ *   dst, src       base addresses; for PKV_SWAP_IN src is pinned host memory
+ *                  and dst device memory, for PKV_SWAP_OUT the reverse
+ *   block_mapping  HOST int64 [num_pairs, 2] = (src block, dst block), read
+ *                  before the call returns
+ *   src_num_blocks, dst_num_blocks  pool sizes, for range checks
+ * Runs of consecutive ids become one asynchronous copy.  Returns
+ * PKV_ERR_NOT_PINNED if the host side is not page-locked host memory and
+ * PKV_ERR_INVALID_ARG for an id out of range.  The host buffer must stay
+ * alive and untouched until the stream reaches the copies.
+ */
+int pkv_swap_blocks(void* dst, const void* src, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
+                    int32_t direction, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,249 @@
+"""ctypes binding of libpkv (argument marshalling only; every step runs in the HIP kernels).
+
+The library is loaded after torch so that it binds to the same HIP runtime
+(``libamdhip64.so.7``) that torch already loaded: device pointers and stream
+handles from torch are then valid for the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Optional, Sequence
+
+import torch
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_SWAP_IN, PKV_SWAP_OUT = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
+_lib: Optional[ctypes.CDLL] = None
+
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+_c_int, _c_i64, _c_sz, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                     ctypes.c_void_p, ctypes.c_float)
+_DECODE_ARGTYPES = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_int, _c_int, _c_int, _c_int,
+                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_p]
+_SIGNATURES = {
+    "pkv_paged_attention_decode": (_c_int, _DECODE_ARGTYPES),
+    "pkv_paged_attention_partitions": (_c_int, _DECODE_ARGTYPES),
+    "pkv_paged_attention_reduce": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_p, _c_sz, _c_p]),
+    "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
+                                       _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
+    "pkv_copy_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p]),
+    "pkv_swap_blocks": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+}
+
+
+def _header_symbols() -> List[str]:
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pkv_\w+)\s*\(", text, re.M)))
+
+
+EXPORTED_SYMBOLS = _header_symbols() if os.path.exists(_HEADER) else sorted(_SIGNATURES)
+
+
+class PKVError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Load libpkv.so (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise PKVError(f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_164_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = library().pkv_last_error().decode(errors="replace")
+        raise PKVError(f"{what} failed with code {rc}: {msg}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _on_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise PKVError("pkv operates on GPU tensors only")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise PKVError(f"unsupported dtype {t.dtype}") from None
+
+
+def paged_attention_workspace_size(num_seqs: int, num_heads: int, head_size: int,
+                                   max_context_len: int, partition_size: int = 0) -> int:
+    return int(library().pkv_paged_attention_workspace_size(num_seqs, num_heads, head_size,
+                                                            max_context_len, partition_size))
+
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, partition_size, workspace, stream):
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
+    B, Hq, D = query.shape
+    NB, Hkv, Dx, bs, x = key_cache.shape
+    dt = _dtype_code(query)
+    if not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
+        raise PKVError("query, caches and out must share one dtype")
+    if x * query.element_size() != 16 or Dx * x != D:
+        raise PKVError(f"key_cache must be [num_blocks, Hkv, D/x, bs, x] with x = 16/sizeof ({tuple(key_cache.shape)})")
+    if tuple(value_cache.shape) != (NB, Hkv, D, bs):
+        raise PKVError(f"value_cache must be [num_blocks, Hkv, D, bs], got {tuple(value_cache.shape)}")
+    if tuple(out.shape) != (B, Hq, D):
+        raise PKVError("out must have the query's shape")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PKVError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(context_lens.shape) != (B,):
+        raise PKVError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    for t in (out, query, key_cache, value_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise PKVError("all decode tensors must be contiguous")
+    need = paged_attention_workspace_size(B, Hq, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), float(scale), B, Hq, Hkv, D, bs,
+            block_tables.shape[1], int(max_context_len), dt, int(partition_size), ws_ptr, ws_bytes,
+            _stream(stream)), workspace
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                           max_context_len, partition_size=0, workspace=None, stream=None):
+    """out[b, h] = softmax(scale * q K_b^T) V_b over the sequence's paged tokens (both kernels)."""
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream)
+    _check(library().pkv_paged_attention_decode(*args), "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
+                               scale, max_context_len, partition_size=0, workspace=None,
+                               stream=None):
+    """Phase 1 only; returns the workspace that pkv_paged_attention_reduce must be given."""
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream)
+    _check(library().pkv_paged_attention_partitions(*args), "pkv_paged_attention_partitions")
+    return ws
+
+
+def paged_attention_reduce(out, context_lens, max_context_len, workspace, partition_size=0,
+                           stream=None):
+    _on_gpu(out, context_lens)
+    B, Hq, D = out.shape
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().pkv_paged_attention_reduce(out.data_ptr(), context_lens.data_ptr(), B, Hq, D,
+                                                int(max_context_len), _dtype_code(out),
+                                                int(partition_size), ws_ptr, ws_bytes,
+                                                _stream(stream)),
+           "pkv_paged_attention_reduce")
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """key/value [N, Hkv, D] (token rows may be strided; heads and dims contiguous)."""
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping)
+    N, Hkv, D = key.shape
+    NB, Hkv2, Dx, bs, x = key_cache.shape
+    if Hkv2 != Hkv or Dx * x != D or tuple(value.shape) != (N, Hkv, D):
+        raise PKVError("key/value [N, Hkv, D] must match the cache layout")
+    if tuple(value_cache.shape) != (NB, Hkv, D, bs):
+        raise PKVError("value_cache must be [num_blocks, Hkv, D, bs]")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise PKVError("key, value and caches must share one dtype")
+    for t in (key, value):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise PKVError("key/value need stride(-1) == 1 and stride(1) == head_size")
+    if not (key_cache.is_contiguous() and value_cache.is_contiguous()):
+        raise PKVError("caches must be contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N or not slot_mapping.is_contiguous():
+        raise PKVError("slot_mapping must be contiguous int64 with one entry per token")
+    _check(library().pkv_reshape_and_cache(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                           value_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D,
+                                           bs, NB, key.stride(0), value.stride(0),
+                                           _dtype_code(key), _stream(stream)),
+           "pkv_reshape_and_cache")
+
+
+def copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],
+                block_mapping: torch.Tensor, stream=None, _ptr_buffers=None):
+    """Copy whole blocks (src, dst) in every layer's key and value cache (device mapping [n, 2] int64)."""
+    if len(key_caches) != len(value_caches) or not key_caches:
+        raise PKVError("one key and one value cache per layer")
+    ref = key_caches[0]
+    _on_gpu(block_mapping, *key_caches, *value_caches)
+    nb = ref.shape[0]
+    block_bytes = ref[0].numel() * ref.element_size()
+    for c in list(key_caches) + list(value_caches):
+        if c.shape[0] != nb or c[0].numel() * c.element_size() != block_bytes or not c.is_contiguous():
+            raise PKVError("all caches must be contiguous with equal block counts and block bytes")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise PKVError("block_mapping must be int64 [num_pairs, 2]")
+    if _ptr_buffers is None:
+        kp = torch.tensor([c.data_ptr() for c in key_caches], dtype=torch.int64, device=ref.device)
+        vp = torch.tensor([c.data_ptr() for c in value_caches], dtype=torch.int64, device=ref.device)
+    else:
+        kp, vp = _ptr_buffers
+    bm = block_mapping.contiguous()
+    _check(library().pkv_copy_blocks(kp.data_ptr(), vp.data_ptr(), len(key_caches), bm.data_ptr(),
+                                     bm.shape[0], block_bytes, nb, _stream(stream)),
+           "pkv_copy_blocks")
+    return kp, vp
+
+
+def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping, stream=None):
+    """dst[d] = src[s] for each (s, d) pair; one side is a GPU cache, the other pinned host memory."""
+    if src.is_cuda == dst.is_cuda:
+        raise PKVError("swap_blocks moves between a GPU cache and a pinned host cache")
+    direction = PKV_SWAP_OUT if src.is_cuda else PKV_SWAP_IN
+    if src[0].numel() * src.element_size() != dst[0].numel() * dst.element_size():
+        raise PKVError("block sizes differ")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise PKVError("caches must be contiguous")
+    m = torch.as_tensor(block_mapping, dtype=torch.int64).cpu().contiguous()
+    if m.dim() != 2 or m.shape[1] != 2:
+        raise PKVError("block_mapping must be [num_pairs, 2]")
+    block_bytes = src[0].numel() * src.element_size()
+    _check(library().pkv_swap_blocks(dst.data_ptr(), src.data_ptr(), m.data_ptr(), m.shape[0],
+                                     block_bytes, src.shape[0], dst.shape[0], direction,
+                                     _stream(stream)),
+           "pkv_swap_blocks")
+
+
+def decode_bytes(context_lens, num_heads: int, num_kv_heads: int, head_size: int, block_size: int,
+                 elem_bytes: int) -> int:
+    """Algorithmic HBM bytes of one decode call: every context token's K and V (all KV heads),
+    q in and out, one int32 block id per block and one int32 length per sequence."""
+    lens = [int(v) for v in context_lens]
+    kv = sum(lens) * num_kv_heads * head_size * 2 * elem_bytes
+    qo = 2 * len(lens) * num_heads * head_size * elem_bytes
+    ids = 4 * sum((L + block_size - 1) // block_size for L in lens)
+    return kv + qo + ids + 4 * len(lens)

@@ -1,0 +1,325 @@
+// C ABI of libpkv: argument validation, workspace layout and kernel dispatch.
+// The contracts are stated in include/pkv.h.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return PKV_ERR_HIP;
+}
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+  }
+  return 0;
+}
+
+int effective_partition(int partition_size) {
+  return partition_size == 0 ? pkv::kDefaultPartition : partition_size;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxPartitions = 8192;  // reduce kernel keeps one weight per partition in LDS (32 KiB)
+
+struct Resolved {
+  pkv::DecodeArgs args;
+  size_t ws_needed;
+  int group;
+  bool use_mfma;
+};
+
+// Shared validation of the decode entry points.
+int resolve_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                   const int32_t* block_tables, const int32_t* context_lens, float scale,
+                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                   int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                   int32_t dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                   Resolved* r) {
+  if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID_ARG, "dtype must be PKV_F32, PKV_F16 or PKV_BF16");
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      max_num_blocks_per_seq < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_heads must be a multiple of num_kv_heads");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  const int group = num_heads / num_kv_heads;
+  if (head_size != 64 && head_size != 128) return fail(PKV_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
+  const int P = effective_partition(partition_size);
+  if (P < block_size || P > pkv::kMaxPartition || P % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 1024]");
+  // Grouped heads of 16-bit types go to the matrix-core kernel; everything else to the VALU one.
+  const bool use_mfma = dtype != PKV_F32 && group > 1 &&
+                        pkv::mfma_supported(dtype, head_size, block_size, group);
+  if (!use_mfma && !pkv::valu_supported(dtype, head_size, block_size, group))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
+  const int64_t max_parts = ceil_div(max_context_len, P);
+  if (max_parts > kMaxPartitions)
+    return fail(PKV_ERR_UNSUPPORTED, "max_context_len / partition_size exceeds 8192 partitions");
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * std::max<int64_t>(max_parts, 1);
+  if (grid >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens))
+    return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+  const size_t need = max_parts > 1
+      ? pkv::workspace_layout(num_seqs, num_heads, head_size, (int)max_parts).total
+      : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(need) + " bytes");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  pkv::DecodeArgs& a = r->args;
+  a.out = out;
+  a.query = query;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  if (need > 0) {
+    const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)max_parts);
+    char* ws = static_cast<char*>(workspace);
+    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+  } else {
+    a.part_m = a.part_l = a.part_acc = nullptr;
+  }
+  a.scale_log2 = scale * pkv::kLog2e;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_num_blocks_per_seq;
+  a.len_limit = (int)std::min<int64_t>(max_context_len, (int64_t)max_num_blocks_per_seq * block_size);
+  a.partition_size = P;
+  // max_context_len == 0 still launches one workgroup per (sequence, KV head): it writes the
+  // zero output of an empty context.
+  a.max_partitions = (int)std::max<int64_t>(max_parts, 1);
+  r->ws_needed = need;
+  r->group = group;
+  r->use_mfma = use_mfma;
+  return PKV_OK;
+}
+
+int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
+  if (r.args.num_seqs == 0) return PKV_OK;
+  hipError_t e = r.use_mfma
+      ? pkv::launch_decode_mfma(r.args, dtype, head_size, block_size, r.group, s)
+      : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "attention kernel launch");
+}
+
+int launch_phase2(const Resolved& r, int dtype, int head_size, hipStream_t s) {
+  if (r.args.max_partitions <= 1 || r.args.num_seqs == 0) return PKV_OK;
+  hipError_t e = pkv::launch_reduce(r.args, dtype, head_size, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "reduce kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                                          int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
+  const int P = effective_partition(partition_size);
+  if (P <= 0) return 0;
+  const int64_t parts = ceil_div(max_context_len, P);
+  if (parts <= 1 || parts > kMaxPartitions) return 0;
+  return pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts).total;
+}
+
+#define PKV_DECODE_PARAMS                                                                     \
+  void *out, const void *query, const void *key_cache, const void *value_cache,               \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, int32_t num_seqs, \
+      int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,         \
+      int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,                 \
+      int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream
+#define PKV_DECODE_ARGS                                                                        \
+  out, query, key_cache, value_cache, block_tables, context_lens, scale, num_seqs, num_heads, \
+      num_kv_heads, head_size, block_size, max_num_blocks_per_seq, max_context_len, dtype,    \
+      partition_size, workspace, workspace_bytes
+
+int pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
+  try {
+    Resolved r;
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r);
+    if (rc != PKV_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = launch_phase1(r, dtype, head_size, block_size, s);
+    if (rc != PKV_OK) return rc;
+    return launch_phase2(r, dtype, head_size, s);
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_paged_attention_partitions(PKV_DECODE_PARAMS) {
+  try {
+    Resolved r;
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r);
+    if (rc != PKV_OK) return rc;
+    return launch_phase1(r, dtype, head_size, block_size, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t head_size, int32_t max_context_len,
+                               int32_t dtype, int32_t partition_size, const void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  try {
+    if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+    if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (head_size != 64 && head_size != 128) return fail(PKV_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+    const int P = effective_partition(partition_size);
+    if (P <= 0 || P > pkv::kMaxPartition) return fail(PKV_ERR_INVALID_ARG, "bad partition_size");
+    const int64_t parts = ceil_div(max_context_len, P);
+    if (parts > kMaxPartitions) return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
+    if (parts <= 1 || num_seqs == 0) return PKV_OK;
+    if (!out || !context_lens) return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts);
+    if (!workspace || workspace_bytes < w.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return fail(PKV_ERR_WORKSPACE, "workspace missing, misaligned or too small");
+    Resolved r{};
+    pkv::DecodeArgs& a = r.args;
+    char* ws = const_cast<char*>(static_cast<const char*>(workspace));
+    a.out = out;
+    a.context_lens = context_lens;
+    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.len_limit = max_context_len;
+    a.partition_size = P;
+    a.max_partitions = (int)parts;
+    return launch_phase2(r, dtype, head_size, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_size, int32_t block_size, int64_t num_blocks,
+                          int64_t key_stride, int64_t value_stride, int32_t dtype, void* stream) {
+  try {
+    const int eb = elem_bytes(dtype);
+    if (eb == 0) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    const int x = 16 / eb;
+    if (head_size % x != 0) return fail(PKV_ERR_INVALID_ARG, "head_size must be a multiple of x = 16/sizeof");
+    if (key_stride < (int64_t)num_kv_heads * head_size || value_stride < (int64_t)num_kv_heads * head_size)
+      return fail(PKV_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_size");
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    hipError_t e = pkv::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                                                 num_tokens, num_kv_heads, head_size, block_size,
+                                                 num_blocks, key_stride, value_stride, eb,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "reshape_and_cache launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_copy_blocks(const uint64_t* key_cache_ptrs, const uint64_t* value_cache_ptrs,
+                    int32_t num_layers, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t block_bytes, int64_t num_blocks, void* stream) {
+  try {
+    if (num_layers < 0 || num_pairs < 0 || block_bytes <= 0 || num_blocks < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (block_bytes % 16 != 0) return fail(PKV_ERR_INVALID_ARG, "block_bytes must be a multiple of 16");
+    if (num_layers > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 layers");
+    if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+    if (!key_cache_ptrs || !value_cache_ptrs || !block_mapping)
+      return fail(PKV_ERR_NULL_POINTER, "null pointer");
+    const int64_t chunks = (block_bytes / 16 + 2047) / 2048;
+    if ((int64_t)num_pairs * chunks >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    hipError_t e = pkv::launch_copy_blocks(key_cache_ptrs, value_cache_ptrs, num_layers, block_mapping,
+                                           num_pairs, block_bytes, num_blocks,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "copy_blocks launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_swap_blocks(void* dst, const void* src, const int64_t* block_mapping, int32_t num_pairs,
+                    int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
+                    int32_t direction, void* stream) {
+  try {
+    if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (direction != PKV_SWAP_IN && direction != PKV_SWAP_OUT)
+      return fail(PKV_ERR_INVALID_ARG, "direction must be PKV_SWAP_IN or PKV_SWAP_OUT");
+    if (num_pairs == 0) return PKV_OK;
+    if (!dst || !src || !block_mapping) return fail(PKV_ERR_NULL_POINTER, "null pointer");
+    const void* host = direction == PKV_SWAP_IN ? src : dst;
+    const void* dev = direction == PKV_SWAP_IN ? dst : src;
+    hipPointerAttribute_t attr{};
+    hipError_t e = hipPointerGetAttributes(&attr, host);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();  // clear the sticky error of an unregistered pointer
+      return fail(PKV_ERR_NOT_PINNED, "host side of swap_blocks is not page-locked host memory");
+    }
+    e = hipPointerGetAttributes(&attr, dev);
+    if (e != hipSuccess || attr.type != hipMemoryTypeDevice) {
+      (void)hipGetLastError();
+      return fail(PKV_ERR_INVALID_ARG, "device side of swap_blocks is not device memory");
+    }
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int64_t s = block_mapping[2 * i], d = block_mapping[2 * i + 1];
+      if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
+        return fail(PKV_ERR_INVALID_ARG, "block id out of range at pair " + std::to_string(i));
+    }
+    const hipMemcpyKind kind = direction == PKV_SWAP_IN ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // Coalesce runs where both ids advance by one into a single copy.
+    int32_t i = 0;
+    while (i < num_pairs) {
+      const int64_t s0 = block_mapping[2 * i], d0 = block_mapping[2 * i + 1];
+      int32_t n = 1;
+      while (i + n < num_pairs && block_mapping[2 * (i + n)] == s0 + n &&
+             block_mapping[2 * (i + n) + 1] == d0 + n)
+        ++n;
+      e = hipMemcpyAsync(static_cast<char*>(dst) + d0 * block_bytes,
+                         static_cast<const char*>(src) + s0 * block_bytes, (size_t)n * block_bytes,
+                         kind, st);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+      i += n;
+    }
+    return PKV_OK;
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Host-side declarations shared by the pkv translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kDefaultPartition = 512;
+constexpr int kMaxPartition = 1024;
+constexpr int kThreads = 256;  // every attention workgroup: 4 wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;  // logits are kept in base-2 units
+
+// Everything the attention kernels need, resolved on the host.
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_m;    // [num_seqs, num_heads, max_partitions] running max (log2 units)
+  float* part_l;    // [num_seqs, num_heads, max_partitions] sum of exp2(s - m)
+  float* part_acc;  // [num_seqs, num_heads, max_partitions, head_size] unnormalised output
+  float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int max_blocks;       // block_tables row length
+  int len_limit;        // min(max_context_len, max_blocks * block_size)
+  int partition_size;
+  int max_partitions;   // ceil(max_context_len / partition_size)
+};
+
+struct WorkspaceLayout {
+  size_t m_off, l_off, acc_off, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_size,
+                                        int max_partitions) {
+  WorkspaceLayout w{};
+  size_t stats = size_t(num_seqs) * num_heads * max_partitions * sizeof(float);
+  w.m_off = 0;
+  w.l_off = align256(stats);
+  w.acc_off = w.l_off + align256(stats);
+  w.total = w.acc_off + align256(stats * head_size);
+  return w;
+}
+
+// Kernel launchers: return hipSuccess or the launch error.  Shapes are validated by the caller.
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                              int group, hipStream_t stream);
+bool valu_supported(int dtype, int head_size, int block_size, int group);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                              int group, hipStream_t stream);
+bool mfma_supported(int dtype, int head_size, int block_size, int group);
+hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                    void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                                    int num_kv_heads, int head_size, int block_size,
+                                    int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                                    int elem_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(const uint64_t* key_ptrs, const uint64_t* value_ptrs, int num_layers,
+                              const int64_t* mapping, int num_pairs, int64_t block_bytes,
+                              int64_t num_blocks, hipStream_t stream);
+
+}  // namespace pkv

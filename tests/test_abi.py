@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every entry point of include/pkv.h, and rejects bad
+arguments on the host before touching the GPU (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_164_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(pkv.library_path()):
+        pytest.fail("libpkv.so is not built (run python -m paged_kv_cache_164_amd.build)")
+    return pkv.library()
+
+
+def test_exports_every_header_symbol():
+    lib = _lib()
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    declared = set(re.findall(r"\b(pkv_\w+)\s*\(", text))
+    assert declared == set(pkv.EXPORTED_SYMBOLS)
+    assert len(declared) == 8
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_single_hip_runtime_shared_with_torch():
+    _lib()
+    paths = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_workspace_size():
+    _lib()
+    # one partition: no scratch
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == 0
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == 0
+    # three partitions: m, l (256-byte aligned each) and acc
+    n = 4 * 8 * 3
+    stats = (n * 4 + 255) // 256 * 256
+    acc = (n * 64 * 4 + 255) // 256 * 256
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 512) == 2 * stats + acc
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 0) == 2 * stats + acc
+
+
+def _decode(lib, **over):
+    args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
+                scale=0.125, num_seqs=2, num_heads=8, num_kv_heads=8, head_size=64, block_size=16,
+                max_blocks=4, max_context_len=64, dtype=0, partition_size=0, workspace=None,
+                ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.pkv_paged_attention_decode(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_size=96), -2),
+    (dict(block_size=12), -2),
+    (dict(num_heads=12), -1),            # not a multiple of num_kv_heads
+    (dict(dtype=7), -1),
+    (dict(partition_size=24), -1),       # not a multiple of block_size
+    (dict(partition_size=2048), -1),     # above 1024
+    (dict(scale=float("nan")), -1),
+    (dict(query=None), -3),
+    (dict(max_context_len=4096), -4),    # needs a workspace
+    (dict(num_heads=24, num_kv_heads=8, dtype=0), -2),   # group 3 unsupported for fp32
+])
+def test_decode_argument_errors(over, code):
+    lib = _lib()
+    assert _decode(lib, **over) == code
+    assert lib.pkv_last_error().decode() != ""
+
+
+def test_cache_op_argument_errors():
+    lib = _lib()
+    # reshape: bad dtype, stride too small
+    assert lib.pkv_reshape_and_cache(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 128, 9, None) == -1
+    assert lib.pkv_reshape_and_cache(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 100, 128, 1, None) == -1
+    # copy: block bytes not a multiple of 16
+    assert lib.pkv_copy_blocks(1, 1, 1, 1, 1, 40, 10, None) == -1
+    # swap: bad direction; ids out of range are found before any copy is issued
+    m = (ctypes.c_int64 * 2)(0, 5)
+    assert lib.pkv_swap_blocks(1, 1, m, 1, 64, 4, 4, 3, None) == -1
+    # zero-sized calls are no-ops
+    assert lib.pkv_copy_blocks(None, None, 1, None, 0, 64, 10, None) == 0
+    assert lib.pkv_reshape_and_cache(None, None, None, None, None, 0, 2, 64, 16, 10, 128, 128, 1, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    q = torch.zeros(1, 8, 64)
+    with pytest.raises(pkv.PKVError):
+        pkv.paged_attention_decode(q, q, torch.zeros(1, 8, 16, 16, 4), torch.zeros(1, 8, 64, 16),
+                                   torch.zeros(1, 1, dtype=torch.int32),
+                                   torch.zeros(1, dtype=torch.int32), 0.125, 16)
+
+
+def test_decode_bytes_formula():
+    # two sequences of 17 and 16 tokens, MHA 2 heads, D 8, bs 16, 2-byte elements
+    b = pkv.decode_bytes([17, 16], 2, 2, 8, 16, 2)
+    assert b == 33 * 2 * 8 * 2 * 2 + 2 * 2 * 2 * 8 * 2 + 4 * 3 + 4 * 2

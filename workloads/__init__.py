@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 import torch
@@ -194,22 +194,25 @@ def poison_slots(key_cache: torch.Tensor, value_cache: torch.Tensor, block_id: i
 
 
 def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optional[int] = None,
-                     poison: bool = True) -> DecodeCase:
+                     lens: Optional[Sequence[int]] = None, poison: bool = True,
+                     **overrides) -> DecodeCase:
     """Build one decode step of config ``key`` (c1..c4).
 
     ``num_seqs`` keeps the first sequences of the full draw (same lengths);
-    ``len_cap`` clips lengths, for oracle-sized parity cases.
+    ``len_cap`` clips lengths, for oracle-sized parity cases; ``lens`` replaces
+    the drawn lengths outright; ``overrides`` replace config fields (shapes,
+    dtype, pool) for variants outside the five workloads.
     """
-    cfg = CONFIGS[key]
-    B_full = cfg.num_seqs
-    lens = draw_lengths(cfg, B_full)
-    B = B_full if num_seqs is None else int(num_seqs)
-    if B > B_full:
-        # more sequences than the config: continue the same distribution
-        lens = draw_lengths(dataclasses.replace(cfg, num_seqs=B), B)
-    lens = lens[:B]
+    cfg = dataclasses.replace(CONFIGS[key], **overrides) if overrides else CONFIGS[key]
+    if lens is not None:
+        lens = np.asarray(lens, dtype=np.int64)
+    else:
+        B_full = cfg.num_seqs
+        B = B_full if num_seqs is None else int(num_seqs)
+        lens = draw_lengths(cfg, max(B, B_full))[:B]
     if len_cap is not None:
         lens = np.minimum(lens, len_cap)
+    B = len(lens)
     bs, Hq, Hkv, D, x = cfg.block_size, cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.x
     nblk = (lens + bs - 1) // bs
     n_used = int(nblk.sum())
@@ -230,9 +233,11 @@ def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optio
     value_cache = torch.full((NB, Hkv, D, bs), fill, dtype=tdt)
     fill_pool(key_cache, value_cache, used, cfg)
 
-    slot = np.zeros(B, dtype=np.int64)
+    slot = np.full(B, -1, dtype=np.int64)   # an empty context gets no new token
     for b in range(B):
         L = int(lens[b])
+        if L == 0:
+            continue
         last = L - 1
         blk = int(tables[b, last // bs])
         slot[b] = blk * bs + last % bs
