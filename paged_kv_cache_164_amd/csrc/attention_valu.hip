@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
 template <class DT, int D, int BS, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (size_t(G) * a.partition_size + kWaves * G * D + 2 * G);
+  const size_t lds = valu_lds_bytes(G, D, a.partition_size);
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
   hipLaunchKernelGGL((decode_valu_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(kThreads), lds,
                      stream, a);

@@ -75,6 +75,10 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
                         pkv::mfma_supported(dtype, head_size, block_size, group);
   if (!use_mfma && !pkv::valu_supported(dtype, head_size, block_size, group))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
+  const size_t lds = use_mfma ? pkv::mfma_lds_bytes(group, block_size, P)
+                             : pkv::valu_lds_bytes(group, head_size, P);
+  if (lds > pkv::kMaxDynamicLds)
+    return fail(PKV_ERR_UNSUPPORTED, "group size x partition_size needs more than 64 KiB of LDS");
   const int64_t max_parts = ceil_div(max_context_len, P);
   if (max_parts > kMaxPartitions)
     return fail(PKV_ERR_UNSUPPORTED, "max_context_len / partition_size exceeds 8192 partitions");

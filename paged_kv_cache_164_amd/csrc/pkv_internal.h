@@ -51,6 +51,16 @@ inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_si
   return w;
 }
 
+// Dynamic LDS of the phase-1 kernels (must stay within the 64 KiB a launch gets by default).
+inline size_t valu_lds_bytes(int group, int head_size, int partition_size) {
+  return sizeof(float) * (size_t(group) * partition_size + kWaves * group * head_size + 2 * group);
+}
+inline size_t mfma_lds_bytes(int group, int block_size, int partition_size) {
+  const size_t pr = (partition_size + 31) / 32 * 32;
+  return sizeof(float) * (size_t(group) * pr + 2 * group) + sizeof(int) * (pr / block_size + 1);
+}
+constexpr size_t kMaxDynamicLds = 65536;
+
 // Kernel launchers: return hipSuccess or the launch error.  Shapes are validated by the caller.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
                               int group, hipStream_t stream);

@@ -74,6 +74,7 @@ def test_edge_lengths(dtype, heads):
 @pytest.mark.parametrize("dtype,D,bs,heads", [
     ("bf16", 64, 8, (8, 4)), ("f16", 128, 32, (6, 6)), ("f32", 128, 8, (4, 2)),
     ("f16", 64, 16, (16, 2)), ("bf16", 128, 32, (16, 2)), ("f32", 64, 32, (8, 8)),
+    ("f16", 64, 16, (16, 1)), ("bf16", 128, 8, (12, 4)), ("f16", 128, 16, (40, 8)),
 ])
 def test_shape_variants(dtype, D, bs, heads):
     case = make_decode_case("c3", num_seqs=5, len_cap=1800, dtype=dtype, head_size=D,
