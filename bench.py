@@ -7,7 +7,8 @@ Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (every context token's K
 and V for all KV heads, q in, out, block ids, lengths, plus the new tokens' K/V read and
 written) divided by the step time: achieved GB/s.  `roofline` covers the dominant kernel
-(the partition kernel), timed with HIP events on the stream it is launched on;
+(phase 1: the small work-list kernel and the partition kernel it feeds), timed with HIP
+events on the stream they are launched on;
 `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3]
@@ -33,7 +34,8 @@ WORKLOADS = {
     "c3": "GQA decode: batch 256, 32 q heads / 8 KV heads, head 128, block 16, bf16, lognormal lengths",
     "c4": "long-context split-K: batch 8, 64 q / 8 KV heads, head 128, block 32, bf16, 131072 tokens",
 }
-KERNEL_SOURCES = ["attention_valu.hip", "attention_mfma.hip", "pkv_device.h", "pkv_internal.h"]
+KERNEL_SOURCES = ["attention_valu.hip", "attention_gqa.hip", "work_plan.hip", "pkv_device.h",
+                  "pkv_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -180,7 +182,7 @@ def main() -> int:
         "kv_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "partition kernel (phase 1)",
+                     "traffic": traffic, "kernel": "phase 1: work-list kernel + partition kernel",
                      "kernel_ms": round(k_avg, 5), "kernel_ms_p10_p90":
                          [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
                      "algorithmic_bytes_per_launch": dec_bytes},

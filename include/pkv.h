@@ -84,12 +84,16 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *   head_size    64 or 128;  block_size 8, 16 or 32
  *   num_heads    a multiple of num_kv_heads; group size num_heads/num_kv_heads
  *                in {1, 2, 4, 8} for PKV_F32, 1..16 for PKV_F16/PKV_BF16
+ *   num_seqs     below 2^19
  *   max_context_len  host upper bound of context_lens (sizes the grid)
  *   partition_size   0 = 512; otherwise a multiple of block_size in
- *                [block_size, 1024]
+ *                [block_size, 1024]; at most 8192 partitions per sequence
  *   workspace    device scratch of at least
- *                pkv_paged_attention_workspace_size(...) bytes (may be NULL
- *                when that size is 0), 256-byte aligned
+ *                pkv_paged_attention_workspace_size(...) bytes, 256-byte
+ *                aligned, no initial contents required (it holds the list of
+ *                non-empty (sequence, partition) work items built by the
+ *                call, and the split-K partials); one call at a time per
+ *                workspace
  * Physical block ids in block_tables must be valid pool indices: they are
  * not checked on the device.
  */
@@ -101,18 +105,20 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                                int32_t max_context_len, int32_t dtype, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of split-K scratch needed by the call above (0 when max_context_len
- * fits one partition): per (sequence, query head, partition) one fp32 running
+/* Bytes of scratch needed by the call above: a 256-byte header, one uint32
+ * work item per (sequence, partition) and, when max_context_len spans more
+ * than one partition, per (sequence, query head, partition) one fp32 running
  * max, one fp32 running sum and head_size fp32 partial outputs.  Returns 0 for
- * invalid arguments. */
+ * num_seqs == 0 and for invalid arguments. */
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                           int32_t max_context_len, int32_t partition_size);
 
-/* The first of the two kernels of pkv_paged_attention_decode, alone: every
- * (sequence, KV head, partition) workgroup.  Sequences that fit one partition
- * get their final output in `out`; longer ones leave per-partition partial
- * results in `workspace` for pkv_paged_attention_reduce.  Same arguments and
- * rules as pkv_paged_attention_decode. */
+/* The first phase of pkv_paged_attention_decode, alone: the work-list kernel
+ * and then one workgroup per (sequence, KV head, non-empty partition).
+ * Sequences that fit one partition get their final output in `out`; longer
+ * ones leave per-partition partial results in `workspace` for
+ * pkv_paged_attention_reduce.  Same arguments and rules as
+ * pkv_paged_attention_decode. */
 int pkv_paged_attention_partitions(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,
                                    const int32_t* context_lens, float scale, int32_t num_seqs,

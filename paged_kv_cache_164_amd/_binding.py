@@ -17,7 +17,8 @@ PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_SWAP_IN, PKV_SWAP_OUT = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY may name another build of the same library (e.g. one compiled with other tuning knobs).
+_LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
 _lib: Optional[ctypes.CDLL] = None
 

@@ -1,0 +1,307 @@
+// Paged decode attention, phase 1, for grouped-query heads (fp16 / bf16) on the matrix cores.
+//
+// One wave handles one work item = (sequence, KV head, partition of partition_size tokens),
+// streaming it tile by tile (16 tokens) with an online softmax, so a wave needs no LDS and no
+// barrier; the next tile's loads are in flight while a tile is computed.  Per tile:
+//   S^T[t][g] = K[t][:] . Q[g][:]       v_mfma_f32_16x16x32 (bf16 / f16), G heads in N
+//   online softmax per column g (base-2 logits, running max m and sum l)
+//   O^T[d][g] += V^T[d][t] P^T[t][g]    v_mfma_f32_16x16x16, 16 dims x 16 heads tiles
+// The QK output layout (lane = column g, four consecutive tokens per lane) is exactly the
+// B-operand layout of the 16x16x16 product, so the weights never leave registers.
+//
+// Operands come straight from the paged layout of the "Vllm" page ("CacheEngine"):
+//   key tile [D/8][bs][8]: lane (token l%16, dims 8*(l/16)..) = one 16-byte load;
+//   value tile [D][bs]: lane (dim l%16, tokens 4*(l/16)..+4) = one 8-byte load, and the 64
+//   lanes of one load cover 16 whole value rows (512 contiguous bytes at bs 16).
+// Weights are rounded to the element type once; l accumulates the rounded weights.
+// Tokens past the context: logit -inf, weight 0, value entries zeroed before the product.
+//
+// Scheduling: workgroup t takes ticket t of the list that the plan kernel (work_plan.hip)
+// filled: work item t / num_kv_heads, KV head t % num_kv_heads.  Every real item is therefore
+// dispatched before any empty slot of the (upper-bound) grid, and full partitions run before
+// the partial last ones.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+#include <algorithm>
+
+
+namespace pkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma_k32(BF16, const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k32(F16, const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(BF16, const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(F16, const uint2& a, const uint2& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                               __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t to_bits(BF16, float v) { return f32_to_bf16_rne(v); }
+__device__ __forceinline__ float from_bits(BF16, uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ uint32_t to_bits(F16, float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+__device__ __forceinline__ float from_bits(F16, uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// Zero the 16-bit elements of an 8-byte value chunk whose token base + e is >= limit.
+__device__ __forceinline__ uint2 mask4(uint2 v, int base, int limit) {
+  const uint32_t m0 = ((base + 0 < limit) ? 0x0000ffffu : 0u) | ((base + 1 < limit) ? 0xffff0000u : 0u);
+  const uint32_t m1 = ((base + 2 < limit) ? 0x0000ffffu : 0u) | ((base + 3 < limit) ? 0xffff0000u : 0u);
+  return make_uint2(v.x & m0, v.y & m1);
+}
+
+template <class DT, int D, int BS>
+__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int kh, int p) {
+  static_assert(DT::X == 8, "matrix-core path is for 16-bit element types");
+
+  constexpr int KC = D / 32;   // 32-dim k-steps of the logit product
+  constexpr int NDT = D / 16;  // 16-dim output tiles
+  const int P = a.partition_size;
+  const int Hkv = a.num_kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks + (int64_t)p * (P / BS);
+  // The partition's block ids (at most 128) go to two lane registers, loaded together with the
+  // length (entries past the row's end are never read; entries past the context are unused).
+  const int row_left = a.max_blocks - p * (P / BS);
+  const int nmax = min(P / BS, row_left);
+  const int ids0 = (lane < nmax) ? bt[lane] : 0;
+  const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
+  const int L = min(max(a.context_lens[b], 0), a.len_limit);
+  const int tok0 = p * P;
+  const int h0 = kh * G;
+  if (tok0 >= L) {
+    if (p == 0) {
+      for (int i = lane; i < G * D; i += 64)
+        store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h0) * D + i, 0.f);
+    }
+    return;
+  }
+  const int ntok = min(P, L - tok0);
+  const int nslots = (ntok + BS - 1) / BS * BS;  // tokens covered by the partition's blocks
+  const int NP = (L + P - 1) / P;
+  const int col = lane & 15;   // query head within the group (MFMA column)
+  const int quad = lane >> 4;  // row group
+
+  const int64_t tile_bytes = (int64_t)D * BS * 2;
+  const int64_t block_bytes = tile_bytes * Hkv;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
+  auto block_of = [&](int j) -> int64_t {
+    j = min(j, 127);  // a lookahead past the last block is never used for a load
+    return (j < 64) ? __builtin_amdgcn_readlane(ids0, j) : __builtin_amdgcn_readlane(ids1, j - 64);
+  };
+  // One 16-token tile: KC 16-byte key chunks and NDT 8-byte value chunks per lane.  Lanes
+  // whose tokens lie past the partition's blocks load nothing.
+  struct Tile {
+    uint4 k[KC];
+    uint2 v[NDT];
+  };
+  // Loads are issued without branches (a load under a branch makes the compiler wait for every
+  // outstanding load at the next use, which would serialise the double buffering).  With
+  // block_size >= 16 every lane of a tile below ntok lies inside the partition's blocks; with
+  // block_size 8 a lane past the last block reads block 0 and masks the data to zero.
+  auto load_tile = [&](int t0, Tile& tl) {
+    int64_t kblk, vblk;
+    int koff, voff;
+    bool kvalid = true, vvalid = true;
+    if constexpr (BS >= 16) {
+      kblk = vblk = block_of(t0 / BS);
+      koff = t0 % BS + col;
+      voff = t0 % BS + quad * 4;
+    } else {
+      const int64_t lo = block_of(t0 / BS), hi = block_of(t0 / BS + 1);
+      kvalid = t0 + col < nslots;
+      vvalid = t0 + quad * 4 < nslots;
+      kblk = !kvalid ? 0 : (col < BS) ? lo : hi;
+      vblk = !vvalid ? 0 : (quad * 4 < BS) ? lo : hi;
+      koff = col % BS;
+      voff = (quad * 4) % BS;
+    }
+    const char* kp = kbase + kblk * block_bytes + koff * 16;
+    const char* vp = vbase + vblk * block_bytes + voff * 2;
+    const uint32_t km = kvalid ? ~0u : 0u, vm = vvalid ? ~0u : 0u;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      tl.k[kc] = *reinterpret_cast<const uint4*>(kp + (int64_t)(kc * 4 + quad) * BS * 16);
+      if constexpr (BS < 16) tl.k[kc] = make_uint4(tl.k[kc].x & km, tl.k[kc].y & km, tl.k[kc].z & km, tl.k[kc].w & km);
+    }
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      tl.v[i] = *reinterpret_cast<const uint2*>(vp + (int64_t)(i * 16 + col) * BS * 2);
+      if constexpr (BS < 16) tl.v[i] = make_uint2(tl.v[i].x & vm, tl.v[i].y & vm);
+    }
+  };
+
+  // Tiles that hold at least one token of the partition.  The loads of the next three tiles are
+  // in flight while a tile is being computed (a ring of four tile buffers); prefetches past the
+  // last tile re-read the last tile (an L2 hit) instead of branching around the load.
+  const int ntiles = (ntok + 15) / 16;
+  const int last = ntiles - 1;
+  Tile T0, T1, T2, T3;
+  load_tile(0, T0);
+  load_tile(min(1, last) * 16, T1);
+  load_tile(min(2, last) * 16, T2);
+  // Q^T as the B operand of the logit product: lane holds Q[g = col][32 kc + 8 quad .. +8].
+  uint4 qop[KC];
+  {
+    const uint4* qv = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(a.query) + ((int64_t)b * a.num_heads + h0) * D * 2);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      qop[kc] = (col < G) ? qv[col * (D / 8) + kc * 4 + quad] : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max of column col (base-2 units)
+  float l_run = 0.f;        // this lane's share of the running sum (its tokens only)
+
+  auto compute_tile = [&](int t0, Tile& tl) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) s = mma_k32(DT(), tl.k[kc], qop[kc], s);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r] = (t0 + quad * 4 + r < ntok) ? s[r] * a.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, s[r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // Every tile starts before ntok, so tmax is finite and alpha is never 2^(-inf + inf).
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+    // weights rounded once to the element type; the same values feed l and P.V
+    uint32_t h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = to_bits(DT(), exp2f(s[r] - m_new));
+      l_run += from_bits(DT(), h[r]);
+    }
+    const uint2 pop = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    const int tv = t0 + quad * 4;
+    if (tv + 4 > ntok) {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) tl.v[i] = mask4(tl.v[i], tv, ntok);
+    }
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i] = mma_k16(DT(), tl.v[i], pop, oacc[i]);
+  };
+
+  for (int i = 0; i < ntiles; i += 4) {
+    load_tile(min(i + 3, last) * 16, T3);
+    compute_tile(i * 16, T0);
+    load_tile(min(i + 4, last) * 16, T0);
+    if (i + 1 < ntiles) compute_tile((i + 1) * 16, T1);
+    load_tile(min(i + 5, last) * 16, T1);
+    if (i + 2 < ntiles) compute_tile((i + 2) * 16, T2);
+    load_tile(min(i + 6, last) * 16, T2);
+    if (i + 3 < ntiles) compute_tile((i + 3) * 16, T3);
+  }
+
+  // ---- epilogue: lane holds O[g = col][d = 16 i + 4 quad + r]
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (col < G) {
+    const int h = h0 + col;
+    if (NP == 1) {
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h) * D + i * 16 + quad * 4 + r,
+                     oacc[i][r] * inv);
+    } else {
+      const int64_t sp = ((int64_t)b * a.num_heads + h) * a.max_partitions + p;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+        *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) = oacc[i];
+      if (quad == 0) {
+        a.part_m[sp] = m_run;
+        a.part_l[sp] = l_tot;
+      }
+    }
+  }
+}
+
+// One workgroup per ticket of the plan's list (the grid is an upper bound: workgroups past the
+// list's end exit at once, after every real item has been dispatched).
+template <class DT, int D, int BS>
+__global__ __launch_bounds__(64) void gqa_grid_kernel(DecodeArgs a, int G) {
+  const int Hkv = a.num_kv_heads;
+  const int t = blockIdx.x;
+  if (t >= int(a.queue[1]) * Hkv) return;
+  const uint32_t pr = a.pairs[t / Hkv];
+  gqa_item<DT, D, BS>(a, G, int(pr / kMaxPartitions), t % Hkv, int(pr % kMaxPartitions));
+}
+
+template <class DT, int D, int BS>
+hipError_t launch_t(const DecodeArgs& a, int group, hipStream_t stream) {
+  hipError_t e = launch_plan(a, stream);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+  hipLaunchKernelGGL((gqa_grid_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream, a,
+                     group);
+  return hipGetLastError();
+}
+
+template <class DT, int D>
+hipError_t by_block(const DecodeArgs& a, int bs, int group, hipStream_t s) {
+  switch (bs) {
+    case 8: return launch_t<DT, D, 8>(a, group, s);
+    case 16: return launch_t<DT, D, 16>(a, group, s);
+    case 32: return launch_t<DT, D, 32>(a, group, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class DT>
+hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s) {
+  switch (D) {
+    case 64: return by_block<DT, 64>(a, bs, group, s);
+    case 128: return by_block<DT, 128>(a, bs, group, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool gqa_supported(int dtype, int head_size, int block_size, int group) {
+  return (dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 2 && group <= 16;
+}
+
+hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                               int group, hipStream_t stream) {
+  switch (dtype) {
+    case 1: return by_head<F16>(a, head_size, block_size, group, stream);
+    case 2: return by_head<BF16>(a, head_size, block_size, group, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

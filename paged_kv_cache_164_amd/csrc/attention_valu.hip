@@ -1,7 +1,8 @@
 // Paged decode attention, phase 1, vector-ALU variant (all element types).
 //
 // One workgroup (4 wave64s) per (sequence, KV head, partition of
-// partition_size tokens).  The cache layout is the one of the "Vllm" page,
+// partition_size tokens), taken from the plan kernel's list of non-empty
+// partitions (work_plan.hip).  The cache layout is the one of the "Vllm" page,
 // section "CacheEngine": a (block, KV head) key tile is
 // [head_size/x][block_size][x] and a value tile is [head_size][block_size],
 // each one contiguous run of head_size * block_size elements.  A wave
@@ -46,11 +47,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int U = 2;  // tiles in flight per wave
   const int P = a.partition_size;
   const int Hkv = a.num_kv_heads;
-  int id = blockIdx.x;
-  const int kh = id % Hkv;
-  id /= Hkv;
-  const int b = id % a.num_seqs;
-  const int p = id / a.num_seqs;
+  // Workgroup t takes ticket t of the plan's list: work item t / Hkv, KV head t % Hkv.
+  const int t = blockIdx.x;
+  if (t >= int(a.queue[1]) * Hkv) return;
+  const uint32_t pr = a.pairs[t / Hkv];
+  const int kh = t % Hkv;
+  const int b = int(pr / kMaxPartitions);
+  const int p = int(pr % kMaxPartitions);
   const int L = min(max(a.context_lens[b], 0), a.len_limit);
   const int tok0 = p * P;
   const int h0 = kh * G;
@@ -234,6 +237,8 @@ template <class DT, int D, int BS, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = valu_lds_bytes(G, D, a.partition_size);
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+  hipError_t e = launch_plan(a, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_valu_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(kThreads), lds,
                      stream, a);
   return hipGetLastError();

@@ -1,9 +1,10 @@
 // C ABI of libpkv: argument validation, workspace layout and kernel dispatch.
 // The contracts are stated in include/pkv.h.
-#include "../../include/pkv.h"
+#include "pkv.h"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -40,7 +41,8 @@ int effective_partition(int partition_size) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int64_t kMaxPartitions = 8192;  // reduce kernel keeps one weight per partition in LDS (32 KiB)
+// The reduce kernel keeps one weight per partition in LDS (32 KiB at the limit).
+constexpr int64_t kMaxPartitions = pkv::kMaxPartitions;
 
 struct Resolved {
   pkv::DecodeArgs args;
@@ -72,11 +74,10 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
     return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 1024]");
   // Grouped heads of 16-bit types go to the matrix-core kernel; everything else to the VALU one.
   const bool use_mfma = dtype != PKV_F32 && group > 1 &&
-                        pkv::mfma_supported(dtype, head_size, block_size, group);
+                        pkv::gqa_supported(dtype, head_size, block_size, group);
   if (!use_mfma && !pkv::valu_supported(dtype, head_size, block_size, group))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
-  const size_t lds = use_mfma ? pkv::mfma_lds_bytes(group, block_size, P)
-                             : pkv::valu_lds_bytes(group, head_size, P);
+  const size_t lds = use_mfma ? 0 : pkv::valu_lds_bytes(group, head_size, P);
   if (lds > pkv::kMaxDynamicLds)
     return fail(PKV_ERR_UNSUPPORTED, "group size x partition_size needs more than 64 KiB of LDS");
   const int64_t max_parts = ceil_div(max_context_len, P);
@@ -84,11 +85,12 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
     return fail(PKV_ERR_UNSUPPORTED, "max_context_len / partition_size exceeds 8192 partitions");
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * std::max<int64_t>(max_parts, 1);
   if (grid >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (num_seqs >= pkv::kMaxPlanSeqs) return fail(PKV_ERR_UNSUPPORTED, "more than 2^19 - 1 sequences");
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens))
     return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
-  const size_t need = max_parts > 1
-      ? pkv::workspace_layout(num_seqs, num_heads, head_size, (int)max_parts).total
-      : 0;
+  const pkv::WorkspaceLayout w =
+      pkv::workspace_layout(num_seqs, num_heads, head_size, (int)std::max<int64_t>(max_parts, 1));
+  const size_t need = num_seqs > 0 ? w.total : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -100,14 +102,17 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   a.value_cache = value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.queue = a.pairs = nullptr;
+  a.part_m = a.part_l = a.part_acc = nullptr;
   if (need > 0) {
-    const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)max_parts);
     char* ws = static_cast<char*>(workspace);
-    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
-    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
-    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
-  } else {
-    a.part_m = a.part_l = a.part_acc = nullptr;
+    a.queue = reinterpret_cast<uint32_t*>(ws);
+    a.pairs = reinterpret_cast<uint32_t*>(ws + w.pairs_off);
+    if (max_parts > 1) {
+      a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+      a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+      a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+    }
   }
   a.scale_log2 = scale * pkv::kLog2e;
   a.num_seqs = num_seqs;
@@ -128,7 +133,7 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
 int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
   if (r.args.num_seqs == 0) return PKV_OK;
   hipError_t e = r.use_mfma
-      ? pkv::launch_decode_mfma(r.args, dtype, head_size, block_size, r.group, s)
+      ? pkv::launch_decode_gqa(r.args, dtype, head_size, block_size, r.group, s)
       : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention kernel launch");
 }
@@ -147,11 +152,11 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                           int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs < 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
   const int P = effective_partition(partition_size);
   if (P <= 0) return 0;
-  const int64_t parts = ceil_div(max_context_len, P);
-  if (parts <= 1 || parts > kMaxPartitions) return 0;
+  const int64_t parts = std::max<int64_t>(ceil_div(max_context_len, P), 1);
+  if (parts > kMaxPartitions) return 0;
   return pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts).total;
 }
 

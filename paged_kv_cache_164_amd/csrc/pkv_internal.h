@@ -8,6 +8,8 @@
 namespace pkv {
 
 constexpr int kDefaultPartition = 512;
+constexpr int kMaxPartitions = 8192;      // per sequence; a work item packs b * kMaxPartitions + p
+constexpr int kMaxPlanSeqs = 1 << 19;     // sequences addressable by a packed work item
 constexpr int kMaxPartition = 1024;
 constexpr int kThreads = 256;  // every attention workgroup: 4 wave64s
 constexpr int kWaves = kThreads / 64;
@@ -21,6 +23,8 @@ struct DecodeArgs {
   const void* value_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  uint32_t* queue;  // [2]: (reserved, number of work items), written by the plan kernel
+  uint32_t* pairs;  // [num_seqs * max_partitions] work items b * kMaxPartitions + p
   float* part_m;    // [num_seqs, num_heads, max_partitions] running max (log2 units)
   float* part_l;    // [num_seqs, num_heads, max_partitions] sum of exp2(s - m)
   float* part_acc;  // [num_seqs, num_heads, max_partitions, head_size] unnormalised output
@@ -34,8 +38,9 @@ struct DecodeArgs {
   int max_partitions;   // ceil(max_context_len / partition_size)
 };
 
+// Workspace: [queue header | work items | split-K partials (only with several partitions)].
 struct WorkspaceLayout {
-  size_t m_off, l_off, acc_off, total;
+  size_t pairs_off, m_off, l_off, acc_off, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -43,9 +48,15 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_size,
                                         int max_partitions) {
   WorkspaceLayout w{};
-  size_t stats = size_t(num_seqs) * num_heads * max_partitions * sizeof(float);
-  w.m_off = 0;
-  w.l_off = align256(stats);
+  const int parts = max_partitions > 0 ? max_partitions : 1;
+  w.pairs_off = 256;
+  w.m_off = w.pairs_off + align256(size_t(num_seqs) * parts * sizeof(uint32_t));
+  if (parts == 1) {
+    w.l_off = w.acc_off = w.total = w.m_off;
+    return w;
+  }
+  const size_t stats = size_t(num_seqs) * num_heads * parts * sizeof(float);
+  w.l_off = w.m_off + align256(stats);
   w.acc_off = w.l_off + align256(stats);
   w.total = w.acc_off + align256(stats * head_size);
   return w;
@@ -55,19 +66,16 @@ inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_si
 inline size_t valu_lds_bytes(int group, int head_size, int partition_size) {
   return sizeof(float) * (size_t(group) * partition_size + kWaves * group * head_size + 2 * group);
 }
-inline size_t mfma_lds_bytes(int group, int block_size, int partition_size) {
-  const size_t pr = (partition_size + 31) / 32 * 32;
-  return sizeof(float) * (size_t(group) * pr + 2 * group) + sizeof(int) * (pr / block_size + 1);
-}
 constexpr size_t kMaxDynamicLds = 65536;
 
 // Kernel launchers: return hipSuccess or the launch error.  Shapes are validated by the caller.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
                               int group, hipStream_t stream);
 bool valu_supported(int dtype, int head_size, int block_size, int group);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_size, int block_size,
-                              int group, hipStream_t stream);
-bool mfma_supported(int dtype, int head_size, int block_size, int group);
+bool gqa_supported(int dtype, int head_size, int block_size, int group);
+hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                               int group, hipStream_t stream);
+hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,

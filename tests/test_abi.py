@@ -36,15 +36,18 @@ def test_single_hip_runtime_shared_with_torch():
 
 def test_workspace_size():
     _lib()
-    # one partition: no scratch
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == 0
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == 0
-    # three partitions: m, l (256-byte aligned each) and acc
+    a256 = lambda v: (v + 255) // 256 * 256
+    # one partition: queue header + one work item per sequence
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == 256 + a256(4 * 4)
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == 256 + a256(4 * 4)
+    assert pkv.paged_attention_workspace_size(0, 8, 64, 100, 0) == 0
+    # three partitions: header, work items, then m, l (256-byte aligned each) and acc
     n = 4 * 8 * 3
-    stats = (n * 4 + 255) // 256 * 256
-    acc = (n * 64 * 4 + 255) // 256 * 256
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 512) == 2 * stats + acc
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 0) == 2 * stats + acc
+    stats = a256(n * 4)
+    acc = a256(n * 64 * 4)
+    expect = 256 + a256(4 * 3 * 4) + 2 * stats + acc
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 512) == expect
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 0) == expect
 
 
 def _decode(lib, **over):
