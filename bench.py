@@ -12,6 +12,14 @@ events on the stream they are launched on;
 `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3]
+
+HBM traffic of the partition kernel (the `roofline.traffic` field) comes from rocprofv3 counter
+runs, scaled by the same counters read on a copy of known size:
+    rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --no-cpu-baseline        (then WRITE_SIZE)
+    rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --calibrate-copy-mib 512 (then WRITE_SIZE)
+    python bench.py --derive-traffic FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
+The last call writes profiles/partition_kernel_<workload>_traffic.json, stamped with a hash of
+the kernel sources; bench.py reports the traffic only while that hash still matches.
 """
 from __future__ import annotations
 
@@ -59,6 +67,63 @@ def traffic_from_profile(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+PARTITION_KERNELS = ("gqa_grid_kernel", "decode_valu_kernel")
+
+
+def _counter_means(path: str):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 counter_collection.csv."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def derive_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: str,
+                   cal_write_csv: str, cal_mib: int) -> dict:
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the partition kernel by what the same
+    counters read for one copy_blocks launch that moves cal_mib one-MiB blocks in each of its two
+    caches (2 * cal_mib MiB read, 2 * cal_mib MiB written)."""
+    known = 2 * cal_mib * 2 ** 20
+
+    def pick(means, names):
+        hits = [v for k, v in means.items() if any(n in k for n in names)]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one matching kernel for {names}, found {len(hits)}")
+        return hits[0]
+
+    f_cal = pick(_counter_means(cal_fetch_csv), ("copy_blocks_kernel",)) * 1024
+    w_cal = pick(_counter_means(cal_write_csv), ("copy_blocks_kernel",)) * 1024
+    f_k = pick(_counter_means(fetch_csv), PARTITION_KERNELS) * 1024
+    w_k = pick(_counter_means(write_csv), PARTITION_KERNELS) * 1024
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "fetch_scale": known / f_cal, "write_scale": known / w_cal,
+           "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
+           "hbm_bytes_per_launch": round(f_k * known / f_cal + w_k * known / w_cal)}
+    out = os.path.join(ROOT, "profiles", f"partition_kernel_{workload}_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+    return rec
+
+
+def calibrate_copy(mib: int, repeats: int = 5) -> None:
+    """copy_blocks of mib one-MiB blocks in each of two caches (reads and writes 2 * mib MiB per
+    launch), for counter scaling."""
+    import torch
+
+    import paged_kv_cache_164_amd as pkv
+
+    dev = torch.device("cuda:0")
+    cache = torch.zeros((2 * mib, 2 ** 20 // 2), dtype=torch.float16, device=dev)
+    other = torch.zeros((2 * mib, 2 ** 20 // 2), dtype=torch.float16, device=dev)
+    mapping = torch.stack([torch.arange(mib), torch.arange(mib, 2 * mib)], dim=1).to(dev)
+    for _ in range(repeats):
+        pkv.copy_blocks([cache], [other], mapping)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_mib": mib, "launches": repeats}))
+
+
 def cpu_baseline(case, budget_s: float = 12.0):
     """The fp64 oracle (unchanged) on the first sequences of the same workload, until the
     time budget is spent; throughput in the metric's unit (algorithmic GB/s)."""
@@ -102,11 +167,21 @@ def main() -> int:
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0)
+    ap.add_argument("--derive-traffic", nargs=4, metavar="CSV")
+    ap.add_argument("--calibration-mib", type=int, default=512)
     args = ap.parse_args()
+    if args.derive_traffic:
+        derive_traffic(args.workload, *args.derive_traffic, args.calibration_mib)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return 0
 
     import torch
 
