@@ -86,7 +86,7 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *                in {1, 2, 4, 8} for PKV_F32, 1..16 for PKV_F16/PKV_BF16
  *   num_seqs     below 2^19
  *   max_context_len  host upper bound of context_lens (sizes the grid)
- *   partition_size   0 = 512; otherwise a multiple of block_size in
+ *   partition_size   0 = auto (1024); otherwise a multiple of block_size in
  *                [block_size, 1024]; at most 8192 partitions per sequence
  *   workspace    device scratch of at least
  *                pkv_paged_attention_workspace_size(...) bytes, 256-byte
@@ -105,8 +105,9 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                                int32_t max_context_len, int32_t dtype, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of scratch needed by the call above: a 256-byte header, one uint32
- * work item per (sequence, partition) and, when max_context_len spans more
+/* Bytes of scratch needed by the call above: a 256-byte header, an 8 KiB
+ * prefetch pad, one uint32 work item per (sequence, partition) and, when
+ * max_context_len spans more
  * than one partition, per (sequence, query head, partition) one fp32 running
  * max, one fp32 running sum and head_size fp32 partial outputs.  Returns 0 for
  * num_seqs == 0 and for invalid arguments. */

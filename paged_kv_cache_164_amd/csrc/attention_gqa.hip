@@ -74,6 +74,10 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
 
   constexpr int KC = D / 32;   // 32-dim k-steps of the logit product
   constexpr int NDT = D / 16;  // 16-dim output tiles
+  // Streaming (non-temporal) loads when a tile consumes whole cache lines of the value rows
+  // (block_size <= 16); at block_size 32 a 16-token tile reads half of each 64-byte value row
+  // and the next tile must find the other half in L2.
+  constexpr bool kStream = BS <= 16;
   const int P = a.partition_size;
   const int Hkv = a.num_kv_heads;
   const int lane = threadIdx.x & 63;
@@ -114,6 +118,8 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
     uint4 k[KC];
     uint2 v[NDT];
   };
+  const int ntiles = (ntok + 15) / 16;  // tiles holding at least one token of the partition
+  const int last = ntiles - 1;
   // Loads are issued without branches (a load under a branch makes the compiler wait for every
   // outstanding load at the next use, which would serialise the double buffering).  With
   // block_size >= 16 every lane of a tile below ntok lies inside the partition's blocks; with
@@ -135,30 +141,30 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
       koff = col % BS;
       voff = (quad * 4) % BS;
     }
-    const char* kp = kbase + kblk * block_bytes + koff * 16;
-    const char* vp = vbase + vblk * block_bytes + voff * 2;
+    // Tiles past the last one (the ring's prefetches at the end of the item) read the small
+    // shared prefetch pad of the workspace instead, which stays in L2: no branch, no HBM re-read.
+    const bool pad = t0 > last * 16;
+    const char* kp = (pad ? a.prefetch_pad : kbase + kblk * block_bytes) + koff * 16;
+    const char* vp = (pad ? a.prefetch_pad : vbase + vblk * block_bytes) + voff * 2;
     const uint32_t km = kvalid ? ~0u : 0u, vm = vvalid ? ~0u : 0u;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      tl.k[kc] = *reinterpret_cast<const uint4*>(kp + (int64_t)(kc * 4 + quad) * BS * 16);
+      tl.k[kc] = kv_load<kStream>(reinterpret_cast<const uint4*>(kp + (int64_t)(kc * 4 + quad) * BS * 16));
       if constexpr (BS < 16) tl.k[kc] = make_uint4(tl.k[kc].x & km, tl.k[kc].y & km, tl.k[kc].z & km, tl.k[kc].w & km);
     }
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
-      tl.v[i] = *reinterpret_cast<const uint2*>(vp + (int64_t)(i * 16 + col) * BS * 2);
+      tl.v[i] = kv_load<kStream>(reinterpret_cast<const uint2*>(vp + (int64_t)(i * 16 + col) * BS * 2));
       if constexpr (BS < 16) tl.v[i] = make_uint2(tl.v[i].x & vm, tl.v[i].y & vm);
     }
   };
 
-  // Tiles that hold at least one token of the partition.  The loads of the next three tiles are
-  // in flight while a tile is being computed (a ring of four tile buffers); prefetches past the
-  // last tile re-read the last tile (an L2 hit) instead of branching around the load.
-  const int ntiles = (ntok + 15) / 16;
-  const int last = ntiles - 1;
+  // The loads of the next three tiles are in flight while a tile is being computed (a ring of
+  // four tile buffers); prefetches past the last tile read the prefetch pad.
   Tile T0, T1, T2, T3;
   load_tile(0, T0);
-  load_tile(min(1, last) * 16, T1);
-  load_tile(min(2, last) * 16, T2);
+  load_tile(16, T1);
+  load_tile(32, T2);
   // Q^T as the B operand of the logit product: lane holds Q[g = col][32 kc + 8 quad .. +8].
   uint4 qop[KC];
   {
@@ -212,13 +218,13 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
   };
 
   for (int i = 0; i < ntiles; i += 4) {
-    load_tile(min(i + 3, last) * 16, T3);
+    load_tile((i + 3) * 16, T3);
     compute_tile(i * 16, T0);
-    load_tile(min(i + 4, last) * 16, T0);
+    load_tile((i + 4) * 16, T0);
     if (i + 1 < ntiles) compute_tile((i + 1) * 16, T1);
-    load_tile(min(i + 5, last) * 16, T1);
+    load_tile((i + 5) * 16, T1);
     if (i + 2 < ntiles) compute_tile((i + 2) * 16, T2);
-    load_tile(min(i + 6, last) * 16, T2);
+    load_tile((i + 6) * 16, T2);
     if (i + 3 < ntiles) compute_tile((i + 3) * 16, T3);
   }
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       if (j < nblk) {
         const uint4* kp = reinterpret_cast<const uint4*>(kbase + (int64_t)bt[j] * block_bytes);
 #pragma unroll
-        for (int i = 0; i < NL; ++i) kv[u][i] = kp[i * kWave + lane];
+        for (int i = 0; i < NL; ++i) kv[u][i] = kv_load<true>(kp + i * kWave + lane);
       }
     }
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
       if (j < nblk) {
         const uint4* vp = reinterpret_cast<const uint4*>(vbase + (int64_t)bt[j] * block_bytes);
 #pragma unroll
-        for (int i = 0; i < NL; ++i) vv[u][i] = vp[i * kWave + lane];
+        for (int i = 0; i < NL; ++i) vv[u][i] = kv_load<true>(vp + i * kWave + lane);
       }
     }
 #pragma unroll

@@ -103,10 +103,12 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.queue = a.pairs = nullptr;
+  a.prefetch_pad = nullptr;
   a.part_m = a.part_l = a.part_acc = nullptr;
   if (need > 0) {
     char* ws = static_cast<char*>(workspace);
     a.queue = reinterpret_cast<uint32_t*>(ws);
+    a.prefetch_pad = ws + w.pad_off;
     a.pairs = reinterpret_cast<uint32_t*>(ws + w.pairs_off);
     if (max_parts > 1) {
       a.part_m = reinterpret_cast<float*>(ws + w.m_off);

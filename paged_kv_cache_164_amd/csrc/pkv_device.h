@@ -97,4 +97,29 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Loads of KV-cache data.  Each context token's keys and values are read once per decode
+// call, so STREAM = true issues them non-temporal: they then do not displace the small, reused
+// data (work list, block tables, queries) from the caches, and the dependent loads that start a
+// work item keep hitting in L2 instead of queueing behind the stream at HBM.
+template <bool STREAM>
+__device__ __forceinline__ uint4 kv_load(const uint4* p) {
+  if constexpr (STREAM) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
+}
+template <bool STREAM>
+__device__ __forceinline__ uint2 kv_load(const uint2* p) {
+  if constexpr (STREAM) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v[0], v[1]);
+  } else {
+    return *p;
+  }
+}
+
 }  // namespace pkv

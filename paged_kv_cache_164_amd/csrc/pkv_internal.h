@@ -7,7 +7,7 @@
 
 namespace pkv {
 
-constexpr int kDefaultPartition = 512;
+constexpr int kDefaultPartition = 1024;  // partition_size 0 ("auto")
 constexpr int kMaxPartitions = 8192;      // per sequence; a work item packs b * kMaxPartitions + p
 constexpr int kMaxPlanSeqs = 1 << 19;     // sequences addressable by a packed work item
 constexpr int kMaxPartition = 1024;
@@ -25,6 +25,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   uint32_t* queue;  // [2]: (reserved, number of work items), written by the plan kernel
   uint32_t* pairs;  // [num_seqs * max_partitions] work items b * kMaxPartitions + p
+  const char* prefetch_pad;  // kPrefetchPad bytes read by prefetches past a work item's end
   float* part_m;    // [num_seqs, num_heads, max_partitions] running max (log2 units)
   float* part_l;    // [num_seqs, num_heads, max_partitions] sum of exp2(s - m)
   float* part_acc;  // [num_seqs, num_heads, max_partitions, head_size] unnormalised output
@@ -38,9 +39,10 @@ struct DecodeArgs {
   int max_partitions;   // ceil(max_context_len / partition_size)
 };
 
-// Workspace: [queue header | work items | split-K partials (only with several partitions)].
+// Workspace: [queue header | prefetch pad | work items | split-K partials (several partitions)].
+constexpr size_t kPrefetchPad = 8192;  // >= the bytes of one (block, head) tile: D * bs * 2
 struct WorkspaceLayout {
-  size_t pairs_off, m_off, l_off, acc_off, total;
+  size_t pad_off, pairs_off, m_off, l_off, acc_off, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -49,7 +51,8 @@ inline WorkspaceLayout workspace_layout(int num_seqs, int num_heads, int head_si
                                         int max_partitions) {
   WorkspaceLayout w{};
   const int parts = max_partitions > 0 ? max_partitions : 1;
-  w.pairs_off = 256;
+  w.pad_off = 256;
+  w.pairs_off = w.pad_off + kPrefetchPad;
   w.m_off = w.pairs_off + align256(size_t(num_seqs) * parts * sizeof(uint32_t));
   if (parts == 1) {
     w.l_off = w.acc_off = w.total = w.m_off;

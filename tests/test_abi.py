@@ -37,17 +37,20 @@ def test_single_hip_runtime_shared_with_torch():
 def test_workspace_size():
     _lib()
     a256 = lambda v: (v + 255) // 256 * 256
-    # one partition: queue header + one work item per sequence
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == 256 + a256(4 * 4)
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == 256 + a256(4 * 4)
+    hdr = 256 + 8192  # queue header + prefetch pad
+    # one partition: header, pad, one work item per sequence
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == hdr + a256(4 * 4)
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == hdr + a256(4 * 4)
     assert pkv.paged_attention_workspace_size(0, 8, 64, 100, 0) == 0
     # three partitions: header, work items, then m, l (256-byte aligned each) and acc
     n = 4 * 8 * 3
     stats = a256(n * 4)
     acc = a256(n * 64 * 4)
-    expect = 256 + a256(4 * 3 * 4) + 2 * stats + acc
+    expect = hdr + a256(4 * 3 * 4) + 2 * stats + acc
     assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 512) == expect
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 0) == expect
+    # auto partition size is 1024: 2049 tokens need three partitions too
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 2049, 0) == expect
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 1024, 0) == hdr + a256(4 * 4)
 
 
 def _decode(lib, **over):

@@ -51,12 +51,14 @@ def test_c3_gqa_bf16_small():
     _run_and_check(make_decode_case("c3", num_seqs=16), tag="c3 small")
 
 
-def test_c4_long_splitk_bf16_small():
+@pytest.mark.parametrize("P", [0, 512])
+def test_c4_long_splitk_bf16_small(P):
+    """Long contexts, 1% outlier keys; 512-token partitions as the workload states, and auto."""
     case = make_decode_case("c4", num_seqs=2, len_cap=20000, pool=("fixed", 0))
-    _run_and_check(case, tag="c4 small")
+    _run_and_check(case, P, tag=f"c4 small P={P}")
 
 
-@pytest.mark.parametrize("P", [16, 256, 1024])
+@pytest.mark.parametrize("P", [16, 256, 512, 1024])
 def test_partition_sizes(P):
     _run_and_check(make_decode_case("c3", num_seqs=6, len_cap=5000), P, tag=f"c3 P={P}")
 
@@ -84,10 +86,10 @@ def test_shape_variants(dtype, D, bs, heads):
 
 # ---------------------------------------------------------------- full size, sampled outputs
 
-@pytest.mark.parametrize("key", ["c2", "c3", "c4"])
-def test_full_size_sampled(key):
+@pytest.mark.parametrize("key,P", [("c2", 0), ("c3", 0), ("c4", 0), ("c4", 512)])
+def test_full_size_sampled(key, P):
     case = make_decode_case(key)
-    _run_and_check(case, pairs=sample_pairs(case, 48, seed=1), tag=f"{key} full")
+    _run_and_check(case, P, pairs=sample_pairs(case, 48, seed=1), tag=f"{key} full P={P}")
 
 
 # ---------------------------------------------------------------- properties on the GPU
