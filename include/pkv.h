@@ -75,7 +75,8 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *   key_cache    [num_blocks, num_kv_heads, head_size/x, block_size, x]
  *   value_cache  [num_blocks, num_kv_heads, head_size, block_size]
  *   block_tables int32 [num_seqs, max_num_blocks_per_seq]; entries past
- *                ceil(context_lens[b] / block_size) are never read
+ *                ceil(context_lens[b] / block_size) are never used as block ids
+ *                (they may be read, inside the row)
  *   context_lens int32 [num_seqs]; each must be <= max_context_len and
  *                <= max_num_blocks_per_seq * block_size (larger values are
  *                clamped to those bounds: no fault, but the result is then
@@ -138,6 +139,61 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
                                int32_t num_heads, int32_t head_size, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size, const void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention for sequences that share a prompt prefix (beam search,
+ * parallel sampling): the same result as pkv_paged_attention_decode, but each
+ * shared block is read from memory once per group instead of once per
+ * sequence.  Sharing is what the block tables express: the members of a group
+ * point to the same physical blocks for their first tokens (PagedAttention's
+ * memory sharing with reference counts and copy-on-write, the mlqm.cn vLLM
+ * explainer, "PagedAttention" and its copy-on-write example; the AIGC
+ * interview book section 23, fork / append_slots).  The prefix is split into
+ * partitions that carry up to 16 / (num_heads / num_kv_heads) members' query
+ * rows at once; every member's own tokens follow in partitions of their own;
+ * all partial results of a sequence are merged with the log-sum-exp rule.
+ *
+ * Arguments as for pkv_paged_attention_decode, plus (device):
+ *   group_starts int32 [num_groups + 1]: group g holds sequences
+ *                [group_starts[g], group_starts[g + 1]); the groups must cover
+ *                0 .. num_seqs - 1 once, in order (group_starts[0] = 0,
+ *                non-decreasing, group_starts[num_groups] = num_seqs); a
+ *                sequence sharing nothing is a group of one
+ *   prefix_lens  int32 [num_groups]: tokens at the start of every member that
+ *                lie in the same physical blocks (table entries equal for
+ *                tokens below it).  Used as min(prefix_lens[g], each member's
+ *                context length) rounded down to a multiple of block_size;
+ *                ignored for a group of one.
+ *   num_groups   in [1, num_seqs] (any value when num_seqs == 0)
+ *   workspace    at least pkv_paged_attention_shared_workspace_size(...)
+ *                bytes, 256-byte aligned, no initial contents required
+ * PKV_F16 and PKV_BF16 only; any group size num_heads/num_kv_heads in 1..16.
+ * Group arrays that break the rules above cannot make the call read or write
+ * outside its buffers, but the output of a sequence that is not covered
+ * exactly once is then unspecified.  Results agree with
+ * pkv_paged_attention_decode within rounding; they are bit-identical to it
+ * when every prefix is a multiple of partition_size and the group size
+ * num_heads/num_kv_heads is at least 2.
+ */
+int pkv_paged_attention_decode_shared(void* out, const void* query, const void* key_cache,
+                                      const void* value_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const int32_t* group_starts,
+                                      const int32_t* prefix_lens, int32_t num_groups, float scale,
+                                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_size, int32_t block_size,
+                                      int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                      int32_t dtype, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch needed by pkv_paged_attention_decode_shared: a 256-byte
+ * header, an 8 KiB prefetch pad, one int32 per sequence, and per sequence
+ * S = ceil(max_context_len / partition_size) + 1 work items of 16 bytes and,
+ * per (sequence, query head), S fp32 running maxima, S fp32 running sums and
+ * S * head_size fp32 partial outputs.  0 for num_seqs == 0 or invalid
+ * arguments. */
+size_t pkv_paged_attention_shared_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                                 int32_t head_size, int32_t max_context_len,
+                                                 int32_t partition_size);
 
 /*
  * Scatter new tokens' keys and values into their cache slots (the KV-cache

@@ -157,3 +157,54 @@ def partitioned_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits:
                          for s0 in range(0, L, partition_size)]
                 out[b, h] = combine_partitions(stats)
     return out
+
+
+def shared_prefix_length(context_lens: np.ndarray, start: int, stop: int, prefix_len: int,
+                         block_size: int) -> int:
+    """Tokens that the sequences [start, stop) read from shared blocks: the caller's prefix
+    length, capped by every member's context length and rounded down to whole blocks (a
+    block is either shared by all members or owned by one, as with copy-on-write in the
+    mlqm.cn explainer's example); a group of one shares nothing."""
+    if stop - start < 2:
+        return 0
+    pre = min([max(int(prefix_len), 0)] + [int(L) for L in context_lens[start:stop]])
+    return pre - pre % block_size
+
+
+def shared_prefix_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
+                         dtype: str, block_tables: np.ndarray, context_lens: np.ndarray,
+                         scale: float, group_starts, prefix_lens, partition_size: int) -> np.ndarray:
+    """Decode of sequences grouped by a shared prompt prefix, with the prefix read once.
+
+    Group g is the sequences [group_starts[g], group_starts[g + 1]).  Its shared tokens
+    [0, pre) are gathered from the first member's block table only and cut into partitions
+    [p P, min((p + 1) P, pre)); each member's own tokens [pre, L) are gathered from its own
+    table and cut into [pre + j P, ...).  Every member's partition statistics are combined
+    with the log-sum-exp rule (split-K, "Vllm" page, "Prefill vs decoding" item 5).  When the
+    members' tables really hold the same blocks for the prefix, this equals paged_decode.
+    """
+    B, Hq, D = query_bits.shape
+    Hkv = key_bits.shape[1]
+    group = Hq // Hkv
+    bs = key_bits.shape[3]
+    sc = as_scale(scale)
+    P = partition_size
+    out = np.zeros((B, Hq, D))
+    for g in range(len(prefix_lens)):
+        s0, s1 = int(group_starts[g]), int(group_starts[g + 1])
+        pre = shared_prefix_length(context_lens, s0, s1, int(prefix_lens[g]), bs)
+        for kvh in range(Hkv):
+            Kp, Vp = gather_kv(key_bits, value_bits, dtype, block_tables[s0], pre, kvh)
+            for b in range(s0, s1):
+                L = int(context_lens[b])
+                if L == 0:
+                    continue
+                K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, kvh)
+                for h in range(kvh * group, (kvh + 1) * group):
+                    q = widen(query_bits[b, h], dtype)
+                    stats = [partition_stats(q, Kp, Vp, sc, t0, min(t0 + P, pre))
+                             for t0 in range(0, pre, P)]
+                    stats += [partition_stats(q, K, V, sc, t0, min(t0 + P, L))
+                              for t0 in range(pre, L, P)]
+                    out[b, h] = combine_partitions(stats)
+    return out

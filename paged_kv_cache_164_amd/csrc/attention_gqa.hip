@@ -20,6 +20,13 @@
 // filled: work item t / num_kv_heads, KV head t % num_kv_heads.  Every real item is therefore
 // dispatched before any empty slot of the (upper-bound) grid, and full partitions run before
 // the partial last ones.
+//
+// Shared-prefix decode uses the same item code with up to 16 / G sequences per item: when
+// several sequences (beams, parallel samples) hold the same physical blocks for their first
+// tokens, their query rows become the columns of one item over those tokens, so each shared
+// block is read once per group rather than once per sequence (the memory sharing of
+// PagedAttention, the mlqm.cn explainer, "PagedAttention" sharing and copy-on-write example).
+// Column c is query head (c % G) of KV head kh in sequence b0 + c / G.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -68,8 +75,13 @@ __device__ __forceinline__ uint2 mask4(uint2 v, int base, int limit) {
   return make_uint2(v.x & m0, v.y & m1);
 }
 
-template <class DT, int D, int BS>
-__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int kh, int p) {
+// One item: tokens [tok0, end) of the sequences b0 .. b0 + nseq - 1 (same blocks for all of
+// them: table row b0 is used), KV head kh, partial slot `slot`.  end_and_np() gives the end
+// token and, when nonzero, the number of partial slots shared by every column's sequence (zero:
+// read each column's count from np_of); it is called after the block-id loads are issued.
+template <class DT, int D, int BS, class EndFn>
+__device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int b0, int nseq,
+                                         int tok0, int slot, EndFn end_and_np) {
   static_assert(DT::X == 8, "matrix-core path is for 16-bit element types");
 
   constexpr int KC = D / 32;   // 32-dim k-steps of the logit product
@@ -81,28 +93,29 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
   const int P = a.partition_size;
   const int Hkv = a.num_kv_heads;
   const int lane = threadIdx.x & 63;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks + (int64_t)p * (P / BS);
-  // The partition's block ids (at most 128) go to two lane registers, loaded together with the
+  const int32_t* bt = a.block_tables + (int64_t)b0 * a.max_blocks + tok0 / BS;
+  // The item's block ids (at most 128) go to two lane registers, loaded together with the
   // length (entries past the row's end are never read; entries past the context are unused).
-  const int row_left = a.max_blocks - p * (P / BS);
+  const int row_left = a.max_blocks - tok0 / BS;
   const int nmax = min(P / BS, row_left);
   const int ids0 = (lane < nmax) ? bt[lane] : 0;
   const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
-  const int L = min(max(a.context_lens[b], 0), a.len_limit);
-  const int tok0 = p * P;
+  int tok_end, np_all;
+  end_and_np(tok_end, np_all);
   const int h0 = kh * G;
-  if (tok0 >= L) {
-    if (p == 0) {
-      for (int i = lane; i < G * D; i += 64)
-        store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h0) * D + i, 0.f);
-    }
+  if (tok0 >= tok_end) {  // the sole item of an empty context
+    for (int i = lane; i < G * D; i += 64)
+      store_elem(DT(), a.out, ((int64_t)b0 * a.num_heads + h0) * D + i, 0.f);
     return;
   }
-  const int ntok = min(P, L - tok0);
-  const int nslots = (ntok + BS - 1) / BS * BS;  // tokens covered by the partition's blocks
-  const int NP = (L + P - 1) / P;
-  const int col = lane & 15;   // query head within the group (MFMA column)
+  const int ntok = tok_end - tok0;
+  const int nslots = (ntok + BS - 1) / BS * BS;  // tokens covered by the item's blocks
+  const int col = lane & 15;   // MFMA column: query head col % G of sequence b0 + col / G
   const int quad = lane >> 4;  // row group
+  const int ncols = nseq * G;
+  const int cseq = col / G;               // column's sequence, relative to b0
+  const int chead = h0 + col - cseq * G;  // column's query head
+  const int64_t crow = ((int64_t)b0 + cseq) * a.num_heads + chead;  // its row of q / out
 
   const int64_t tile_bytes = (int64_t)D * BS * 2;
   const int64_t block_bytes = tile_bytes * Hkv;
@@ -165,15 +178,15 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
   load_tile(0, T0);
   load_tile(16, T1);
   load_tile(32, T2);
-  // Q^T as the B operand of the logit product: lane holds Q[g = col][32 kc + 8 quad .. +8].
+  // Q^T as the B operand of the logit product: lane holds Q[col][32 kc + 8 quad .. +8].
   uint4 qop[KC];
   {
-    const uint4* qv = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(a.query) + ((int64_t)b * a.num_heads + h0) * D * 2);
+    const uint4* qv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.query) + crow * D * 2);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      qop[kc] = (col < G) ? qv[col * (D / 8) + kc * 4 + quad] : make_uint4(0, 0, 0, 0);
+      qop[kc] = (col < ncols) ? qv[kc * 4 + quad] : make_uint4(0, 0, 0, 0);
   }
+  const int np_col = (np_all > 0 || col >= ncols) ? np_all : a.np_of[b0 + cseq];
 
   f32x4 oacc[NDT];
 #pragma unroll
@@ -228,21 +241,19 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int b, int 
     if (i + 3 < ntiles) compute_tile((i + 3) * 16, T3);
   }
 
-  // ---- epilogue: lane holds O[g = col][d = 16 i + 4 quad + r]
+  // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r]
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  if (col < G) {
-    const int h = h0 + col;
-    if (NP == 1) {
+  if (col < ncols) {
+    if (np_col <= 1) {  // the column's sequence has no other item: final output
       const float inv = 1.f / l_tot;
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h) * D + i * 16 + quad * 4 + r,
-                     oacc[i][r] * inv);
+          store_elem(DT(), a.out, crow * D + i * 16 + quad * 4 + r, oacc[i][r] * inv);
     } else {
-      const int64_t sp = ((int64_t)b * a.num_heads + h) * a.max_partitions + p;
+      const int64_t sp = crow * a.max_partitions + slot;
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
         *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) = oacc[i];
@@ -262,7 +273,27 @@ __global__ __launch_bounds__(64) void gqa_grid_kernel(DecodeArgs a, int G) {
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
   const uint32_t pr = a.pairs[t / Hkv];
-  gqa_item<DT, D, BS>(a, G, int(pr / kMaxPartitions), t % Hkv, int(pr % kMaxPartitions));
+  const int b = int(pr / kMaxPartitions), p = int(pr % kMaxPartitions);
+  const int P = a.partition_size;
+  gqa_item<DT, D, BS>(a, G, t % Hkv, b, 1, p * P, p, [&](int& end, int& np) {
+    const int L = min(max(a.context_lens[b], 0), a.len_limit);
+    end = min(p * P + P, L);
+    np = max((L + P - 1) / P, 1);
+  });
+}
+
+// Shared-prefix decode: one workgroup per ticket of the items that the shared plan listed.
+template <class DT, int D, int BS>
+__global__ __launch_bounds__(64) void shared_grid_kernel(DecodeArgs a, int G) {
+  const int Hkv = a.num_kv_heads;
+  const int t = blockIdx.x;
+  if (t >= int(a.queue[1]) * Hkv) return;
+  const uint4 it = a.items[t / Hkv];
+  gqa_item<DT, D, BS>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.y >> 8),
+                      [&](int& end, int& np) {
+                        end = int(it.w);
+                        np = 0;
+                      });
 }
 
 template <class DT, int D, int BS>
@@ -275,21 +306,31 @@ hipError_t launch_t(const DecodeArgs& a, int group, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <class DT, int D, int BS>
+hipError_t launch_shared_t(const DecodeArgs& a, int group, hipStream_t stream) {
+  hipError_t e = launch_plan_shared(a, BS, 16 / group, stream);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+  hipLaunchKernelGGL((shared_grid_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream,
+                     a, group);
+  return hipGetLastError();
+}
+
 template <class DT, int D>
-hipError_t by_block(const DecodeArgs& a, int bs, int group, hipStream_t s) {
+hipError_t by_block(const DecodeArgs& a, int bs, int group, bool shared, hipStream_t s) {
   switch (bs) {
-    case 8: return launch_t<DT, D, 8>(a, group, s);
-    case 16: return launch_t<DT, D, 16>(a, group, s);
-    case 32: return launch_t<DT, D, 32>(a, group, s);
+    case 8: return shared ? launch_shared_t<DT, D, 8>(a, group, s) : launch_t<DT, D, 8>(a, group, s);
+    case 16: return shared ? launch_shared_t<DT, D, 16>(a, group, s) : launch_t<DT, D, 16>(a, group, s);
+    case 32: return shared ? launch_shared_t<DT, D, 32>(a, group, s) : launch_t<DT, D, 32>(a, group, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <class DT>
-hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s) {
+hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, bool shared, hipStream_t s) {
   switch (D) {
-    case 64: return by_block<DT, 64>(a, bs, group, s);
-    case 128: return by_block<DT, 128>(a, bs, group, s);
+    case 64: return by_block<DT, 64>(a, bs, group, shared, s);
+    case 128: return by_block<DT, 128>(a, bs, group, shared, s);
   }
   return hipErrorInvalidValue;
 }
@@ -304,8 +345,23 @@ bool gqa_supported(int dtype, int head_size, int block_size, int group) {
 hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
                                int group, hipStream_t stream) {
   switch (dtype) {
-    case 1: return by_head<F16>(a, head_size, block_size, group, stream);
-    case 2: return by_head<BF16>(a, head_size, block_size, group, stream);
+    case 1: return by_head<F16>(a, head_size, block_size, group, false, stream);
+    case 2: return by_head<BF16>(a, head_size, block_size, group, false, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Every group size fits: an item holds 16 / G sequences (one for G = 16).
+bool shared_supported(int dtype, int head_size, int block_size, int group) {
+  return (dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 1 && group <= 16;
+}
+
+hipError_t launch_decode_shared(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                                int group, hipStream_t stream) {
+  switch (dtype) {
+    case 1: return by_head<F16>(a, head_size, block_size, group, true, stream);
+    case 2: return by_head<BF16>(a, head_size, block_size, group, true, stream);
   }
   return hipErrorInvalidValue;
 }

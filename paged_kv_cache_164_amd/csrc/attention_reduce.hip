@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   const int b = blockIdx.x / a.num_heads;
   const int L = min(max(a.context_lens[b], 0), a.len_limit);
   const int P = a.partition_size;
-  const int NP = (L + P - 1) / P;
+  // shared-prefix decode: the plan kernel counted each sequence's partial results
+  const int NP = a.np_of ? min(a.np_of[b], a.max_partitions) : (L + P - 1) / P;
   if (NP <= 1) return;  // written directly by phase 1
   const int64_t base = ((int64_t)b * a.num_heads + h) * a.max_partitions;
 

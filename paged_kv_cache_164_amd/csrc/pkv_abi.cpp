@@ -51,13 +51,20 @@ struct Resolved {
   bool use_mfma;
 };
 
+// Prefix groups of the shared-prefix decode (null for the plain decode).
+struct Groups {
+  const int32_t* starts;
+  const int32_t* prefix_lens;
+  int32_t count;
+};
+
 // Shared validation of the decode entry points.
 int resolve_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
                    const int32_t* block_tables, const int32_t* context_lens, float scale,
                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len,
                    int32_t dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   Resolved* r) {
+                   Resolved* r, const Groups* groups = nullptr) {
   if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID_ARG, "dtype must be PKV_F32, PKV_F16 or PKV_BF16");
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
       max_num_blocks_per_seq < 0)
@@ -73,8 +80,12 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   if (P < block_size || P > pkv::kMaxPartition || P % block_size != 0)
     return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 1024]");
   // Grouped heads of 16-bit types go to the matrix-core kernel; everything else to the VALU one.
-  const bool use_mfma = dtype != PKV_F32 && group > 1 &&
-                        pkv::gqa_supported(dtype, head_size, block_size, group);
+  // The shared-prefix decode always runs on the matrix cores (16-bit types only).
+  const bool shared = groups != nullptr;
+  const bool use_mfma = shared || (dtype != PKV_F32 && group > 1 &&
+                                   pkv::gqa_supported(dtype, head_size, block_size, group));
+  if (shared && !pkv::shared_supported(dtype, head_size, block_size, group))
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs PKV_F16 or PKV_BF16 and a group size <= 16");
   if (!use_mfma && !pkv::valu_supported(dtype, head_size, block_size, group))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
   const size_t lds = use_mfma ? 0 : pkv::valu_lds_bytes(group, head_size, P);
@@ -83,14 +94,22 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   const int64_t max_parts = ceil_div(max_context_len, P);
   if (max_parts > kMaxPartitions)
     return fail(PKV_ERR_UNSUPPORTED, "max_context_len / partition_size exceeds 8192 partitions");
-  const int64_t grid = (int64_t)num_seqs * num_kv_heads * std::max<int64_t>(max_parts, 1);
+  // partial slots per (sequence, head); a shared prefix may end inside a partition
+  const int64_t slots = shared ? max_parts + 1 : std::max<int64_t>(max_parts, 1);
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * slots;
   if (grid >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   if (num_seqs >= pkv::kMaxPlanSeqs) return fail(PKV_ERR_UNSUPPORTED, "more than 2^19 - 1 sequences");
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens))
     return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
-  const pkv::WorkspaceLayout w =
-      pkv::workspace_layout(num_seqs, num_heads, head_size, (int)std::max<int64_t>(max_parts, 1));
-  const size_t need = num_seqs > 0 ? w.total : 0;
+  if (shared && num_seqs > 0) {
+    if (!groups->starts || !groups->prefix_lens) return fail(PKV_ERR_NULL_POINTER, "null group array");
+    if (groups->count < 1 || groups->count > num_seqs)
+      return fail(PKV_ERR_INVALID_ARG, "num_groups must be in [1, num_seqs]");
+  }
+  const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)slots);
+  const pkv::SharedWorkspaceLayout sw =
+      pkv::shared_workspace_layout(num_seqs, num_heads, head_size, (int)slots);
+  const size_t need = num_seqs > 0 ? (shared ? sw.total : w.total) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -104,8 +123,22 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   a.context_lens = context_lens;
   a.queue = a.pairs = nullptr;
   a.prefetch_pad = nullptr;
+  a.group_starts = shared ? groups->starts : nullptr;
+  a.prefix_lens = shared ? groups->prefix_lens : nullptr;
+  a.num_groups = shared ? groups->count : 0;
+  a.items = nullptr;
+  a.np_of = nullptr;
   a.part_m = a.part_l = a.part_acc = nullptr;
-  if (need > 0) {
+  if (need > 0 && shared) {
+    char* ws = static_cast<char*>(workspace);
+    a.queue = reinterpret_cast<uint32_t*>(ws);
+    a.prefetch_pad = ws + sw.pad_off;
+    a.np_of = reinterpret_cast<int32_t*>(ws + sw.np_off);
+    a.items = reinterpret_cast<uint4*>(ws + sw.items_off);
+    a.part_m = reinterpret_cast<float*>(ws + sw.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + sw.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + sw.acc_off);
+  } else if (need > 0) {
     char* ws = static_cast<char*>(workspace);
     a.queue = reinterpret_cast<uint32_t*>(ws);
     a.prefetch_pad = ws + w.pad_off;
@@ -125,7 +158,7 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   a.partition_size = P;
   // max_context_len == 0 still launches one workgroup per (sequence, KV head): it writes the
   // zero output of an empty context.
-  a.max_partitions = (int)std::max<int64_t>(max_parts, 1);
+  a.max_partitions = (int)slots;
   r->ws_needed = need;
   r->group = group;
   r->use_mfma = use_mfma;
@@ -134,7 +167,9 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
 
 int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
   if (r.args.num_seqs == 0) return PKV_OK;
-  hipError_t e = r.use_mfma
+  hipError_t e = r.args.np_of
+      ? pkv::launch_decode_shared(r.args, dtype, head_size, block_size, r.group, s)
+      : r.use_mfma
       ? pkv::launch_decode_gqa(r.args, dtype, head_size, block_size, r.group, s)
       : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention kernel launch");
@@ -162,6 +197,17 @@ size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, i
   return pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts).total;
 }
 
+size_t pkv_paged_attention_shared_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                                 int32_t head_size, int32_t max_context_len,
+                                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
+  const int P = effective_partition(partition_size);
+  if (P <= 0) return 0;
+  const int64_t parts = ceil_div(max_context_len, P);
+  if (parts > kMaxPartitions) return 0;
+  return pkv::shared_workspace_layout(num_seqs, num_heads, head_size, (int)parts + 1).total;
+}
+
 #define PKV_DECODE_PARAMS                                                                     \
   void *out, const void *query, const void *key_cache, const void *value_cache,               \
       const int32_t *block_tables, const int32_t *context_lens, float scale, int32_t num_seqs, \
@@ -182,6 +228,29 @@ int pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
     rc = launch_phase1(r, dtype, head_size, block_size, s);
     if (rc != PKV_OK) return rc;
     return launch_phase2(r, dtype, head_size, s);
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_paged_attention_decode_shared(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Resolved r;
+    const Groups groups{group_starts, prefix_lens, num_groups};
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r, &groups);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs == 0) return PKV_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = launch_phase1(r, dtype, head_size, block_size, s);
+    if (rc != PKV_OK) return rc;
+    hipError_t e = pkv::launch_reduce(r.args, dtype, head_size, s);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "reduce kernel launch");
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }

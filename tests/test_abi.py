@@ -23,7 +23,7 @@ def test_exports_every_header_symbol():
     text = open(os.path.join(ROOT, "include", "pkv.h")).read()
     declared = set(re.findall(r"\b(pkv_\w+)\s*\(", text))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 8
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -51,6 +51,42 @@ def test_workspace_size():
     # auto partition size is 1024: 2049 tokens need three partitions too
     assert pkv.paged_attention_workspace_size(4, 8, 64, 2049, 0) == expect
     assert pkv.paged_attention_workspace_size(4, 8, 64, 1024, 0) == hdr + a256(4 * 4)
+
+
+def test_shared_workspace_size():
+    _lib()
+    a256 = lambda v: (v + 255) // 256 * 256
+    # header, pad, one int32 per sequence, then S = parts + 1 items of 16 B and partial slots
+    for L, P, parts in [(2049, 0, 3), (512, 512, 1), (0, 0, 0)]:
+        S = parts + 1
+        n = 4 * 8 * S
+        expect = 256 + 8192 + a256(4 * 4) + a256(4 * S * 16) + 2 * a256(n * 4) + a256(n * 64 * 4)
+        assert pkv.paged_attention_shared_workspace_size(4, 8, 64, L, P) == expect
+    assert pkv.paged_attention_shared_workspace_size(0, 8, 64, 100, 0) == 0
+
+
+def _shared(lib, **over):
+    args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
+                group_starts=1, prefix_lens=1, num_groups=1, scale=0.125, num_seqs=2, num_heads=8,
+                num_kv_heads=8, head_size=64, block_size=16, max_blocks=4, max_context_len=64,
+                dtype=1, partition_size=0, workspace=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.pkv_paged_attention_decode_shared(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=0), -2),                          # fp32 has no matrix-core path
+    (dict(num_heads=8 * 17, num_kv_heads=8), -2),  # group size above 16
+    (dict(group_starts=None), -3),
+    (dict(prefix_lens=None), -3),
+    (dict(num_groups=0), -1),
+    (dict(num_groups=3), -1),                    # more groups than sequences
+    (dict(), -4),                                # needs a workspace
+])
+def test_shared_decode_argument_errors(over, code):
+    lib = _lib()
+    assert _shared(lib, **over) == code
+    assert lib.pkv_last_error().decode() != ""
 
 
 def _decode(lib, **over):

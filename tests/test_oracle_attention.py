@@ -265,3 +265,96 @@ def test_combine_is_not_a_plain_average():
     assert np.max(np.abs(OA.combine_partitions(st) - ref)) <= 1e-15
     w = 1.0 / (1.0 + math.exp(-10.0))
     assert abs(ref[0] - w) <= 1e-15
+
+
+# ---------------------------------------------------------------- shared-prefix decode
+
+def _random_shared(seed, sizes=(3, 1, 2), prefixes=(8, 0, 12), Hq=4, Hkv=2, D=16, bs=4,
+                   dtype="bf16", max_priv=9):
+    """Groups of sequences whose first `prefix` tokens are the same dense K/V in the same
+    physical blocks (one table prefix per group), followed by private tokens."""
+    rng = np.random.default_rng(seed)
+    x = 16 // torch.tensor([], dtype=DTYPES[dtype]).element_size()
+    lens, pre_of = [], []
+    for n, pre in zip(sizes, prefixes):
+        for _ in range(n):
+            lens.append(pre + int(rng.integers(0, max_priv + 1)))
+            pre_of.append(pre)
+    B = len(lens)
+    nblk = [(L + bs - 1) // bs for L in lens]
+    NB = sum(nblk) + 4
+    perm = list(rng.permutation(NB))
+    tables = np.full((B, max(nblk)), -1, dtype=np.int32)
+    Kd, Vd, b = [], [], 0
+    for n, pre in zip(sizes, prefixes):
+        assert pre % bs == 0
+        shared_ids = [perm.pop() for _ in range(pre // bs)]
+        Kp = rng.standard_normal((Hkv, pre, D)).astype(np.float32)
+        Vp = rng.standard_normal((Hkv, pre, D)).astype(np.float32)
+        for _ in range(n):
+            L = lens[b]
+            own = [perm.pop() for _ in range(nblk[b] - pre // bs)]
+            tables[b, :nblk[b]] = shared_ids + own
+            Ko = rng.standard_normal((Hkv, L - pre, D)).astype(np.float32)
+            Vo = rng.standard_normal((Hkv, L - pre, D)).astype(np.float32)
+            Kd.append(torch.from_numpy(np.concatenate([Kp, Ko], axis=1)).to(DTYPES[dtype]))
+            Vd.append(torch.from_numpy(np.concatenate([Vp, Vo], axis=1)).to(DTYPES[dtype]))
+            b += 1
+    q = torch.from_numpy(rng.standard_normal((B, Hq, D)).astype(np.float32)).to(DTYPES[dtype])
+    kc, vc = _scatter_dense(Kd, Vd, tables, lens, NB, bs, x, Hkv, dtype)
+    starts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    return dict(q=q, kc=kc, vc=vc, tables=tables, lens=np.asarray(lens, dtype=np.int32),
+                dtype=dtype, scale=1.0 / math.sqrt(D), starts=starts,
+                prefixes=np.asarray(prefixes, dtype=np.int32))
+
+
+def _shared(c, P, prefixes=None):
+    return OA.shared_prefix_decode(_bits(c["q"]), _bits(c["kc"]), _bits(c["vc"]), c["dtype"],
+                                   c["tables"], c["lens"], c["scale"], c["starts"],
+                                   c["prefixes"] if prefixes is None else prefixes, P)
+
+
+def test_shared_prefix_length_rule():
+    lens = np.array([10, 7, 30, 5], dtype=np.int32)
+    assert OA.shared_prefix_length(lens, 0, 2, 9, 4) == 4     # min(9, 10, 7) = 7 -> whole blocks: 4
+    assert OA.shared_prefix_length(lens, 0, 2, 100, 1) == 7   # capped by the shortest member
+    assert OA.shared_prefix_length(lens, 2, 3, 16, 4) == 0    # a group of one shares nothing
+    assert OA.shared_prefix_length(lens, 0, 4, -3, 4) == 0
+    assert OA.shared_prefix_length(lens, 2, 4, 8, 4) == 4     # capped by L = 5, rounded down
+
+
+@pytest.mark.parametrize("P", [4, 8, 12, 512])
+def test_shared_prefix_equals_monolithic(P):
+    """Prefix read once from the first member's table + own tokens == plain attention."""
+    c = _random_shared(21)
+    mono = _oracle(c)
+    assert np.max(np.abs(_shared(c, P) - mono)) <= 1e-12
+    # prefix lengths that end inside a block are cut back to whole blocks
+    assert np.max(np.abs(_shared(c, P, np.array([10, 3, 15], dtype=np.int32)) - mono)) <= 1e-12
+
+
+def test_shared_prefix_without_sharing_is_the_partitioned_decode():
+    c = _random_shared(22, sizes=(1, 1, 1, 1), prefixes=(8, 4, 0, 12))
+    part = OA.partitioned_decode(_bits(c["q"]), _bits(c["kc"]), _bits(c["vc"]), "bf16",
+                                 c["tables"], c["lens"], c["scale"], 8)
+    assert np.array_equal(_shared(c, 8), part)
+
+
+def test_shared_prefix_reads_the_first_members_blocks():
+    """The prefix comes from the group's first table row only: a member whose table points
+    elsewhere for the prefix still sees the first member's prefix blocks."""
+    c = _random_shared(23, sizes=(2,), prefixes=(8,), max_priv=6)
+    bs = c["kc"].shape[3]
+    alt = c["tables"].copy()
+    # move member 1's prefix to fresh copies holding different keys
+    NB = c["kc"].shape[0]
+    kc = torch.cat([c["kc"], -c["kc"][alt[1, :2]]])
+    vc = torch.cat([c["vc"], c["vc"][alt[1, :2]]])
+    alt[1, :2] = [NB, NB + 1]
+    c2 = dict(c, kc=kc, vc=vc, tables=alt)
+    got = _shared(c2, 512)
+    same = _oracle(dict(c2, tables=c["tables"]))  # member 1 reading member 0's prefix blocks
+    own = _oracle(c2)                             # member 1 reading its own (negated) keys
+    assert np.max(np.abs(got - same)) <= 1e-12
+    assert np.max(np.abs(got[1] - own[1])) > 1e-3
+    assert 2 * bs == 8

@@ -348,3 +348,81 @@ def make_beam_case(num_prompts: int = 32, beams: int = 4, prompt_len: int = 2048
 def draw_normal(shape, dtype: str, seed: int, stream: int) -> torch.Tensor:
     """N(0,1) float32 draws rounded to ``dtype`` (for ad-hoc test tensors)."""
     return _normal_to(tuple(shape), rng(seed, stream), dtype)
+
+
+# ---------------------------------------------------------------------------
+# General shared-prefix groups (for the shared-prefix decode)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PrefixCase:
+    """Groups of sequences that share their first ``prefix_lens[g]`` tokens.
+
+    Whole blocks of a group's prefix are one set of physical blocks referenced by every
+    member's table.  When the prefix ends inside a block, that block is copied into a block
+    of each member (as copy-on-write leaves it), so the tables share only the whole blocks.
+    """
+    cfg: DecodeConfig
+    query: torch.Tensor
+    key_cache: torch.Tensor
+    value_cache: torch.Tensor
+    block_tables: np.ndarray   # int32 [B, max_blocks], -1 padded
+    context_lens: np.ndarray   # int32 [B]
+    group_starts: np.ndarray   # int32 [G + 1]
+    prefix_lens: np.ndarray    # int32 [G]
+    scale: float
+
+
+def make_prefix_case(group_sizes: Sequence[int], prefix_lens: Sequence[int],
+                     private: tuple = (0, 64), *, seed: int = 1105, poison: bool = True,
+                     **overrides) -> PrefixCase:
+    """Members of group g have prefix_lens[g] shared tokens plus U[private] tokens of their own.
+    ``overrides`` replace fields of the beam configuration (heads, head size, block size,
+    dtype)."""
+    cfg = dataclasses.replace(BEAM_CFG, seed=seed, **overrides)
+    bs, Hq, Hkv, D, x = cfg.block_size, cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.x
+    g_len = rng(seed, S_LENS)
+    lens, nshared, nown = [], [], []
+    for n, pre in zip(group_sizes, prefix_lens):
+        for _ in range(n):
+            L = int(pre) + int(g_len.integers(private[0], private[1] + 1))
+            lens.append(L)
+            nshared.append(int(pre) // bs)
+            nown.append((L + bs - 1) // bs - int(pre) // bs)
+    B = len(lens)
+    n_unique = sum(int(p) // bs for p in prefix_lens) + sum(nown)
+    NB = n_unique + 8
+    perm = rng(seed, S_PERM).permutation(NB)
+    tdt = DTYPES[cfg.dtype]
+    fill = float("nan") if poison else 0.0
+    key_cache = torch.full((NB, Hkv, D // x, bs, x), fill, dtype=tdt)
+    value_cache = torch.full((NB, Hkv, D, bs), fill, dtype=tdt)
+    fill_pool(key_cache, value_cache, perm[:n_unique], cfg)
+    max_blocks = max([s + o for s, o in zip(nshared, nown)] + [1])
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    off, b = 0, 0
+    for n, pre in zip(group_sizes, prefix_lens):
+        shared = perm[off:off + int(pre) // bs]
+        off += len(shared)
+        first_copy = None
+        for _ in range(n):
+            own = perm[off:off + nown[b]]
+            off += nown[b]
+            tables[b, :len(shared)] = shared
+            tables[b, len(shared):len(shared) + len(own)] = own
+            if pre % bs and len(own):
+                # the prefix's partial block: every member holds a copy of the same tokens
+                if first_copy is None:
+                    first_copy = int(own[0])
+                else:
+                    key_cache[int(own[0]), :, :, :pre % bs] = key_cache[first_copy, :, :, :pre % bs]
+                    value_cache[int(own[0]), :, :, :pre % bs] = value_cache[first_copy, :, :, :pre % bs]
+            L = lens[b]
+            if poison and L % bs and L > 0:
+                poison_slots(key_cache, value_cache, int(tables[b, (L - 1) // bs]), L % bs)
+            b += 1
+    q = _normal_to((B, Hq, D), rng(seed, S_Q), cfg.dtype)
+    starts = np.concatenate([[0], np.cumsum(group_sizes)]).astype(np.int32)
+    return PrefixCase(cfg, q, key_cache, value_cache, tables, np.asarray(lens, dtype=np.int32),
+                      starts, np.asarray(prefix_lens, dtype=np.int32),
+                      float(np.float32(1.0 / math.sqrt(D))))
