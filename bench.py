@@ -11,6 +11,10 @@ written) divided by the step time: achieved GB/s.  `roofline` covers the dominan
 events on the stream they are launched on;
 `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample.
 
+The beam-search workload (c5) times its own step: copy-on-write of each beam's partial last
+block (copy_blocks), the new tokens (reshape_and_cache), then the shared-prefix decode, whose
+bytes count each shared prompt block once (the per-sequence count is reported beside).
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3]
 
 HBM traffic of the partition kernel (the `roofline.traffic` field) comes from rocprofv3 counter
@@ -41,6 +45,8 @@ WORKLOADS = {
     "c2": "MHA decode, 7B-like layer: batch 64, 32 heads, head 128, block 16, fp16",
     "c3": "GQA decode: batch 256, 32 q heads / 8 KV heads, head 128, block 16, bf16, lognormal lengths",
     "c4": "long-context split-K: batch 8, 64 q / 8 KV heads, head 128, block 32, bf16, 131072 tokens",
+    "c5": "shared-prefix beam search: 32 prompts x 4 beams, 40 heads, head 128, block 16, fp16, "
+          "2048-token shared prompts + U[1, 512] own tokens; copy-on-write + shared-prefix decode",
 }
 KERNEL_SOURCES = ["attention_valu.hip", "attention_gqa.hip", "work_plan.hip", "pkv_device.h",
                   "pkv_internal.h"]
@@ -159,6 +165,42 @@ def cpu_baseline(case, budget_s: float = 12.0):
                       f"all {Hq} query heads), {dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
+def beam_setup(dev):
+    """The 32 x 4 beam-search step on the GPU: each beam whose last block is partial copies it to
+    a fresh block (copy-on-write), its next token is written there, and all beams decode with
+    the shared-prefix kernel.  Returns (step inputs, context lengths, unique KV tokens)."""
+    import torch
+
+    from workloads import draw_normal, make_beam_case, S_COW
+
+    bc = make_beam_case(num_prompts=32, poison=False)
+    bs = bc.cfg.block_size
+    B, H, D = bc.query.shape
+    tables, lens = bc.block_tables.copy(), bc.context_lens.copy()
+    free = list(bc.free_blocks)
+    pairs, slots = [], np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        L = int(lens[b])
+        if L % bs:
+            j = (L - 1) // bs
+            new = free.pop(0)
+            pairs.append((int(tables[b, j]), new))
+            tables[b, j] = new
+            slots[b] = new * bs + L % bs
+            lens[b] = L + 1
+    t = dict(q=bc.query.to(dev), kc=bc.key_cache.to(dev), vc=bc.value_cache.to(dev),
+             bt=torch.from_numpy(tables).to(dev), cl=torch.from_numpy(lens).to(dev),
+             nk=draw_normal((B, H, D), "f16", bc.cfg.seed, S_COW).to(dev),
+             nv=draw_normal((B, H, D), "f16", bc.cfg.seed, S_COW + 100).to(dev),
+             slots=torch.from_numpy(slots).to(dev),
+             mapping=torch.from_numpy(np.array(pairs, dtype=np.int64).reshape(-1, 2)).to(dev),
+             gs=torch.arange(0, B + 1, bc.beams, dtype=torch.int32, device=dev),
+             pl=torch.full((bc.num_prompts,), bc.prompt_len, dtype=torch.int32, device=dev),
+             scale=bc.scale, n_pairs=len(pairs), block_bytes=H * D * bs * 2)
+    unique = bc.num_prompts * bc.prompt_len + int((lens - bc.prompt_len).sum())
+    return t, lens, unique
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,31 +231,46 @@ def main() -> int:
     from workloads import make_decode_case
 
     t_gen = time.perf_counter()
-    case = make_decode_case(args.workload)
-    print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
-    q = case.query.to(dev)
-    kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
-    bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
-    nk, nv, slots = case.new_key.to(dev), case.new_value.to(dev), case.slot_mapping.to(dev)
+    P = args.partition
+    stream = torch.cuda.current_stream()
+    beam = args.workload == "c5"
+    if beam:
+        t, lens_np, unique_tokens = beam_setup(dev)
+        q, kc, vc, bt, cl = t["q"], t["kc"], t["vc"], t["bt"], t["cl"]
+        nk, nv, slots, scale = t["nk"], t["nv"], t["slots"], t["scale"]
+        lmax = int(lens_np.max())
+        case = None
+    else:
+        case = make_decode_case(args.workload)
+        q = case.query.to(dev)
+        kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
+        bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
+        nk, nv, slots = case.new_key.to(dev), case.new_value.to(dev), case.slot_mapping.to(dev)
+        scale, lmax = case.scale, case.max_context_len
+    print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     out = torch.empty_like(q)
     B, Hq, D = q.shape
     Hkv, bs = kc.shape[1], kc.shape[3]
     eb = q.element_size()
-    lmax = case.max_context_len
-    P = args.partition
     need = pkv.paged_attention_workspace_size(B, Hq, D, lmax, P)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        if beam:
+            pkv.copy_blocks([kc], [vc], t["mapping"], stream=stream)
         pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, case.scale, lmax, P, ws, stream=stream)
+        if beam:
+            pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
+                                              P, ws, stream=stream)
+        else:
+            pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=stream)
+        if not beam:
+            pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -229,9 +286,17 @@ def main() -> int:
     k_ms = [a.elapsed_time(b) for a, b in events]
     k_avg = float(np.mean(k_ms))
 
-    lens = case.context_lens.numpy()
+    lens = lens_np if beam else case.context_lens.numpy()
     dec_bytes = pkv.decode_bytes(lens, Hq, Hkv, D, bs, eb)
-    write_bytes = 2 * 2 * int((lens > 0).sum()) * Hkv * D * eb + 8 * B
+    logical_dec_bytes = dec_bytes
+    if beam:
+        # HBM holds each shared prompt block once and the shared-prefix kernel reads it once:
+        # the algorithmic bytes count the unique KV tokens (per-sequence counts are given beside)
+        dec_bytes -= (int(lens.sum()) - unique_tokens) * Hkv * D * 2 * eb
+    n_new = int((slots >= 0).sum().item())
+    write_bytes = 2 * 2 * n_new * Hkv * D * eb + 8 * B
+    if beam:  # copy-on-write: each pair reads and writes one key block and one value block
+        write_bytes += 2 * 2 * t["n_pairs"] * t["block_bytes"] + 16 * t["n_pairs"]
     step_bytes = dec_bytes + write_bytes
     gbs = step_bytes / (ms_step / 1e3) / 1e9
     kernel_gbs = dec_bytes / (k_avg / 1e3) / 1e9
@@ -247,7 +312,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.cfg.dtype,
+        "dtype": {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[q.dtype],
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
@@ -257,12 +322,19 @@ def main() -> int:
         "kv_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "phase 1: work-list kernel + partition kernel",
+                     "traffic": traffic,
+                     "kernel": ("shared-prefix decode: plan + partition kernel + split-K reduce" if beam
+                                else "phase 1: work-list kernel + partition kernel"),
                      "kernel_ms": round(k_avg, 5), "kernel_ms_p10_p90":
                          [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
                      "algorithmic_bytes_per_launch": dec_bytes},
     }
-    if not args.no_cpu_baseline:
+    if beam:
+        # per-sequence (logical) bytes: every sequence's attention over all of its tokens
+        rec["config"]["unique_kv_tokens"] = unique_tokens
+        rec["logical_decode_bytes"] = logical_dec_bytes
+        rec["logical_decode_GBs"] = round(logical_dec_bytes / (k_avg / 1e3) / 1e9, 2)
+    if not args.no_cpu_baseline and not beam:
         rec["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(rec), flush=True)
     return 0

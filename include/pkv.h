@@ -64,10 +64,15 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  * Accumulation is fp32; out is rounded to the element type (round to nearest
  * even).  context_lens[b] == 0 gives out[b] = 0.
  *
- * Long contexts are split into partitions of `partition_size` tokens, each
- * handled by its own workgroup; sequences with more than one partition are
- * combined by a second kernel with the log-sum-exp rule (split-K decoding,
- * the "Vllm" page, "Prefill vs decoding" item 5 on FlashDecoding).
+ * Long contexts are split (split-K decoding, the "Vllm" page, "Prefill vs
+ * decoding" item 5 on FlashDecoding): each sequence into whole partitions of P
+ * = partition_size tokens, and the tokens after its last whole partition into
+ * chunks of Q = ceil(P / 4) tokens rounded up to whole blocks (short work
+ * items for the end of the call).  Each piece is handled by its own
+ * workgroup per KV head; a sequence with several pieces gets its output from
+ * a second kernel that merges them in token order with the log-sum-exp rule.
+ * The call is bit-identical to pkv_paged_attention_partitions followed by
+ * pkv_paged_attention_reduce.
  *
  * Arguments (device unless stated):
  *   out          [num_seqs, num_heads, head_size] element type, written
@@ -85,16 +90,16 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *   head_size    64 or 128;  block_size 8, 16 or 32
  *   num_heads    a multiple of num_kv_heads; group size num_heads/num_kv_heads
  *                in {1, 2, 4, 8} for PKV_F32, 1..16 for PKV_F16/PKV_BF16
- *   num_seqs     below 2^19
  *   max_context_len  host upper bound of context_lens (sizes the grid)
- *   partition_size   0 = auto (1024); otherwise a multiple of block_size in
- *                [block_size, 1024]; at most 8192 partitions per sequence
+ *   partition_size   0 = auto: 2048 for PKV_F16/PKV_BF16 with block_size >= 16,
+ *                else 1024; otherwise a multiple of block_size in
+ *                [block_size, 2048], at most 128 blocks for PKV_F16/PKV_BF16;
+ *                at most 8192 partitions per sequence
  *   workspace    device scratch of at least
  *                pkv_paged_attention_workspace_size(...) bytes, 256-byte
  *                aligned, no initial contents required (it holds the list of
- *                non-empty (sequence, partition) work items built by the
- *                call, and the split-K partials); one call at a time per
- *                workspace
+ *                work items built by the call, and the split-K partials);
+ *                one call at a time per workspace
  * Physical block ids in block_tables must be valid pool indices: they are
  * not checked on the device.
  */
@@ -106,21 +111,21 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
                                int32_t max_context_len, int32_t dtype, int32_t partition_size,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of scratch needed by the call above: a 256-byte header, an 8 KiB
- * prefetch pad, one uint32 work item per (sequence, partition) and, when
- * max_context_len spans more
- * than one partition, per (sequence, query head, partition) one fp32 running
- * max, one fp32 running sum and head_size fp32 partial outputs.  Returns 0 for
+/* Bytes of scratch needed by the decode calls (pkv_paged_attention_decode,
+ * _partitions + _reduce, _decode_shared): a 256-byte header, an 8 KiB prefetch
+ * pad, one int32 per sequence, and per sequence S work items of 16 bytes and,
+ * per (sequence, query head), S fp32 running maxima, S fp32 running sums and
+ * S * head_size fp32 partial outputs, where S = ceil(max_context_len / P') + 4
+ * with P' = partition_size, or 1024 for partition_size 0.  Returns 0 for
  * num_seqs == 0 and for invalid arguments. */
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                           int32_t max_context_len, int32_t partition_size);
 
 /* The first phase of pkv_paged_attention_decode, alone: the work-list kernel
- * and then one workgroup per (sequence, KV head, non-empty partition).
- * Sequences that fit one partition get their final output in `out`; longer
- * ones leave per-partition partial results in `workspace` for
- * pkv_paged_attention_reduce.  Same arguments and rules as
- * pkv_paged_attention_decode. */
+ * and then one workgroup per (work item, KV head).  Sequences handled by one
+ * item get their final output in `out`; the others leave per-item partial
+ * results (and their count) in `workspace` for pkv_paged_attention_reduce.
+ * Same arguments and rules as pkv_paged_attention_decode. */
 int pkv_paged_attention_partitions(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,
                                    const int32_t* context_lens, float scale, int32_t num_seqs,
@@ -130,11 +135,11 @@ int pkv_paged_attention_partitions(void* out, const void* query, const void* key
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
-/* The second kernel alone: for each sequence with more than one partition,
- * out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p.
- * Sequences with one partition are left untouched.  Must follow
- * pkv_paged_attention_partitions on the same stream with the same sizes;
- * nothing is enqueued when max_context_len fits one partition. */
+/* The second kernel alone: for each sequence with more than one work item,
+ * out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p,
+ * over its items p in token order.  Sequences with one item are left
+ * untouched.  Must follow pkv_paged_attention_partitions on the same stream
+ * with the same sizes (the workspace holds the counts it reads). */
 int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t head_size, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size, const void* workspace,
@@ -148,10 +153,11 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
  * point to the same physical blocks for their first tokens (PagedAttention's
  * memory sharing with reference counts and copy-on-write, the mlqm.cn vLLM
  * explainer, "PagedAttention" and its copy-on-write example; the AIGC
- * interview book section 23, fork / append_slots).  The prefix is split into
- * partitions that carry up to 16 / (num_heads / num_kv_heads) members' query
- * rows at once; every member's own tokens follow in partitions of their own;
- * all partial results of a sequence are merged with the log-sum-exp rule.
+ * interview book section 23, fork / append_slots).  The prefix is cut like a
+ * context (whole partitions, then chunks) into items that carry up to
+ * 16 / (num_heads / num_kv_heads) members' query rows at once; every member's
+ * own tokens follow in items of their own; all partial results of a sequence
+ * are merged in token order with the log-sum-exp rule.
  *
  * Arguments as for pkv_paged_attention_decode, plus (device):
  *   group_starts int32 [num_groups + 1]: group g holds sequences
@@ -165,15 +171,16 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
  *                context length) rounded down to a multiple of block_size;
  *                ignored for a group of one.
  *   num_groups   in [1, num_seqs] (any value when num_seqs == 0)
- *   workspace    at least pkv_paged_attention_shared_workspace_size(...)
- *                bytes, 256-byte aligned, no initial contents required
+ *   workspace    at least pkv_paged_attention_workspace_size(...) bytes,
+ *                256-byte aligned, no initial contents required
  * PKV_F16 and PKV_BF16 only; any group size num_heads/num_kv_heads in 1..16.
  * Group arrays that break the rules above cannot make the call read or write
  * outside its buffers, but the output of a sequence that is not covered
  * exactly once is then unspecified.  Results agree with
- * pkv_paged_attention_decode within rounding; they are bit-identical to it
- * when every prefix is a multiple of partition_size and the group size
- * num_heads/num_kv_heads is at least 2.
+ * pkv_paged_attention_decode within rounding; for PKV_F16/PKV_BF16 they are
+ * bit-identical to it when every prefix is a multiple of the partition size
+ * in use (both calls then cut every sequence at the same tokens and run the
+ * same kernel).
  */
 int pkv_paged_attention_decode_shared(void* out, const void* query, const void* key_cache,
                                       const void* value_cache, const int32_t* block_tables,
@@ -184,16 +191,6 @@ int pkv_paged_attention_decode_shared(void* out, const void* query, const void* 
                                       int32_t max_num_blocks_per_seq, int32_t max_context_len,
                                       int32_t dtype, int32_t partition_size, void* workspace,
                                       size_t workspace_bytes, void* stream);
-
-/* Bytes of scratch needed by pkv_paged_attention_decode_shared: a 256-byte
- * header, an 8 KiB prefetch pad, one int32 per sequence, and per sequence
- * S = ceil(max_context_len / partition_size) + 1 work items of 16 bytes and,
- * per (sequence, query head), S fp32 running maxima, S fp32 running sums and
- * S * head_size fp32 partial outputs.  0 for num_seqs == 0 or invalid
- * arguments. */
-size_t pkv_paged_attention_shared_workspace_size(int32_t num_seqs, int32_t num_heads,
-                                                 int32_t head_size, int32_t max_context_len,
-                                                 int32_t partition_size);
 
 /*
  * Scatter new tokens' keys and values into their cache slots (the KV-cache

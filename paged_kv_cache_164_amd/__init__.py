@@ -15,7 +15,6 @@ from ._binding import (  # noqa: F401
     library_path,
     paged_attention_decode,
     paged_attention_decode_shared,
-    paged_attention_shared_workspace_size,
     paged_attention_partitions,
     paged_attention_reduce,
     paged_attention_workspace_size,

@@ -36,7 +36,6 @@ _SIGNATURES = {
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_decode_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
                                           + _DECODE_ARGTYPES[6:]),
-    "pkv_paged_attention_shared_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
                                        _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
     "pkv_copy_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p]),
@@ -107,14 +106,8 @@ def paged_attention_workspace_size(num_seqs: int, num_heads: int, head_size: int
                                                             max_context_len, partition_size))
 
 
-def paged_attention_shared_workspace_size(num_seqs: int, num_heads: int, head_size: int,
-                                          max_context_len: int, partition_size: int = 0) -> int:
-    return int(library().pkv_paged_attention_shared_workspace_size(
-        num_seqs, num_heads, head_size, max_context_len, partition_size))
-
-
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, workspace, stream, shared=False):
+                 max_context_len, partition_size, workspace, stream):
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
     B, Hq, D = query.shape
     NB, Hkv, Dx, bs, x = key_cache.shape
@@ -134,8 +127,7 @@ def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
     for t in (out, query, key_cache, value_cache, block_tables, context_lens):
         if not t.is_contiguous():
             raise PKVError("all decode tensors must be contiguous")
-    size_fn = paged_attention_shared_workspace_size if shared else paged_attention_workspace_size
-    need = size_fn(B, Hq, D, max_context_len, partition_size)
+    need = paged_attention_workspace_size(B, Hq, D, max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -161,7 +153,7 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
     """Decode where the sequences [group_starts[g], group_starts[g+1]) share their first
     prefix_lens[g] tokens' blocks: each shared block is read once per group."""
     args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                            max_context_len, partition_size, workspace, stream, shared=True)
+                            max_context_len, partition_size, workspace, stream)
     _on_gpu(group_starts, prefix_lens)
     ng = prefix_lens.numel()
     if (group_starts.dtype != torch.int32 or prefix_lens.dtype != torch.int32

@@ -1,6 +1,6 @@
-// Paged decode attention, phase 1, for grouped-query heads (fp16 / bf16) on the matrix cores.
+// Paged decode attention, phase 1, for fp16 / bf16 on the matrix cores (any group size 1..16).
 //
-// One wave handles one work item = (sequence, KV head, partition of partition_size tokens),
+// One wave handles one work item = (sequence, KV head, range of at most partition_size tokens),
 // streaming it tile by tile (16 tokens) with an online softmax, so a wave needs no LDS and no
 // barrier; the next tile's loads are in flight while a tile is computed.  Per tile:
 //   S^T[t][g] = K[t][:] . Q[g][:]       v_mfma_f32_16x16x32 (bf16 / f16), G heads in N
@@ -18,8 +18,9 @@
 //
 // Scheduling: workgroup t takes ticket t of the list that the plan kernel (work_plan.hip)
 // filled: work item t / num_kv_heads, KV head t % num_kv_heads.  Every real item is therefore
-// dispatched before any empty slot of the (upper-bound) grid, and full partitions run before
-// the partial last ones.
+// dispatched before any empty slot of the (upper-bound) grid, and whole partitions run before
+// the short remainder chunks.  An item carries its token range, so no length has to be read
+// before its first tiles can be requested.
 //
 // Shared-prefix decode uses the same item code with up to 16 / G sequences per item: when
 // several sequences (beams, parallel samples) hold the same physical blocks for their first
@@ -75,13 +76,11 @@ __device__ __forceinline__ uint2 mask4(uint2 v, int base, int limit) {
   return make_uint2(v.x & m0, v.y & m1);
 }
 
-// One item: tokens [tok0, end) of the sequences b0 .. b0 + nseq - 1 (same blocks for all of
-// them: table row b0 is used), KV head kh, partial slot `slot`.  end_and_np() gives the end
-// token and, when nonzero, the number of partial slots shared by every column's sequence (zero:
-// read each column's count from np_of); it is called after the block-id loads are issued.
-template <class DT, int D, int BS, class EndFn>
+// One item: tokens [tok0, tok_end) of the sequences b0 .. b0 + nseq - 1 (same blocks for all
+// of them: table row b0 is used), KV head kh, partial slot `slot`.
+template <class DT, int D, int BS>
 __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int b0, int nseq,
-                                         int tok0, int slot, EndFn end_and_np) {
+                                         int tok0, int tok_end, int slot) {
   static_assert(DT::X == 8, "matrix-core path is for 16-bit element types");
 
   constexpr int KC = D / 32;   // 32-dim k-steps of the logit product
@@ -94,14 +93,12 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
   const int Hkv = a.num_kv_heads;
   const int lane = threadIdx.x & 63;
   const int32_t* bt = a.block_tables + (int64_t)b0 * a.max_blocks + tok0 / BS;
-  // The item's block ids (at most 128) go to two lane registers, loaded together with the
-  // length (entries past the row's end are never read; entries past the context are unused).
+  // The item's block ids (at most 128) go to two lane registers (entries past the row's end
+  // are never read; entries past the context are unused).
   const int row_left = a.max_blocks - tok0 / BS;
   const int nmax = min(P / BS, row_left);
   const int ids0 = (lane < nmax) ? bt[lane] : 0;
   const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
-  int tok_end, np_all;
-  end_and_np(tok_end, np_all);
   const int h0 = kh * G;
   if (tok0 >= tok_end) {  // the sole item of an empty context
     for (int i = lane; i < G * D; i += 64)
@@ -172,21 +169,26 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     }
   };
 
+  // Q^T as the B operand of the logit product: lane holds Q[col][32 kc + 8 quad .. +8].  Unused
+  // columns (col >= ncols) load the first column's row; their results are never stored.
+  // These loads go out before the first tiles': the wait counter retires loads in issue order,
+  // so a query load issued after the tile prologue would make the first product (and, through
+  // the loop's merged wait state, every later one) wait for the tiles behind it as well.
+  uint4 qop[KC];
+  {
+    const int64_t qrow = (col < ncols) ? crow : (int64_t)b0 * a.num_heads + h0;
+    const uint4* qv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.query) + qrow * D * 2);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qop[kc] = qv[kc * 4 + quad];
+  }
+  const int np_col = a.np_of[b0 + min(cseq, nseq - 1)];  // partial results of the column's sequence
+
   // The loads of the next three tiles are in flight while a tile is being computed (a ring of
   // four tile buffers); prefetches past the last tile read the prefetch pad.
   Tile T0, T1, T2, T3;
   load_tile(0, T0);
   load_tile(16, T1);
   load_tile(32, T2);
-  // Q^T as the B operand of the logit product: lane holds Q[col][32 kc + 8 quad .. +8].
-  uint4 qop[KC];
-  {
-    const uint4* qv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.query) + crow * D * 2);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      qop[kc] = (col < ncols) ? qv[kc * 4 + quad] : make_uint4(0, 0, 0, 0);
-  }
-  const int np_col = (np_all > 0 || col >= ncols) ? np_all : a.np_of[b0 + cseq];
 
   f32x4 oacc[NDT];
 #pragma unroll
@@ -206,7 +208,8 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // Every tile starts before ntok, so tmax is finite and alpha is never 2^(-inf + inf).
+    // The first tile holds a token, so m_run is finite from then on; a tile past the end has
+    // only -inf logits: m stays, alpha is exactly 1 and every weight is 0.
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
@@ -230,15 +233,17 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     for (int i = 0; i < NDT; ++i) oacc[i] = mma_k16(DT(), tl.v[i], pop, oacc[i]);
   };
 
+  // Computes of tiles past the end (at most three) are not skipped: a branch around them would
+  // make the compiler's wait bookkeeping conservative; they change nothing (see above).
   for (int i = 0; i < ntiles; i += 4) {
     load_tile((i + 3) * 16, T3);
     compute_tile(i * 16, T0);
     load_tile((i + 4) * 16, T0);
-    if (i + 1 < ntiles) compute_tile((i + 1) * 16, T1);
+    compute_tile((i + 1) * 16, T1);
     load_tile((i + 5) * 16, T1);
-    if (i + 2 < ntiles) compute_tile((i + 2) * 16, T2);
+    compute_tile((i + 2) * 16, T2);
     load_tile((i + 6) * 16, T2);
-    if (i + 3 < ntiles) compute_tile((i + 3) * 16, T3);
+    compute_tile((i + 3) * 16, T3);
   }
 
   // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r]
@@ -253,7 +258,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
         for (int r = 0; r < 4; ++r)
           store_elem(DT(), a.out, crow * D + i * 16 + quad * 4 + r, oacc[i][r] * inv);
     } else {
-      const int64_t sp = crow * a.max_partitions + slot;
+      const int64_t sp = crow * a.slots + slot;
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
         *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) = oacc[i];
@@ -272,96 +277,53 @@ __global__ __launch_bounds__(64) void gqa_grid_kernel(DecodeArgs a, int G) {
   const int Hkv = a.num_kv_heads;
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
-  const uint32_t pr = a.pairs[t / Hkv];
-  const int b = int(pr / kMaxPartitions), p = int(pr % kMaxPartitions);
-  const int P = a.partition_size;
-  gqa_item<DT, D, BS>(a, G, t % Hkv, b, 1, p * P, p, [&](int& end, int& np) {
-    const int L = min(max(a.context_lens[b], 0), a.len_limit);
-    end = min(p * P + P, L);
-    np = max((L + P - 1) / P, 1);
-  });
-}
-
-// Shared-prefix decode: one workgroup per ticket of the items that the shared plan listed.
-template <class DT, int D, int BS>
-__global__ __launch_bounds__(64) void shared_grid_kernel(DecodeArgs a, int G) {
-  const int Hkv = a.num_kv_heads;
-  const int t = blockIdx.x;
-  if (t >= int(a.queue[1]) * Hkv) return;
   const uint4 it = a.items[t / Hkv];
-  gqa_item<DT, D, BS>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.y >> 8),
-                      [&](int& end, int& np) {
-                        end = int(it.w);
-                        np = 0;
-                      });
+  gqa_item<DT, D, BS>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.w),
+                      int(it.y >> 8));
 }
 
 template <class DT, int D, int BS>
 hipError_t launch_t(const DecodeArgs& a, int group, hipStream_t stream) {
-  hipError_t e = launch_plan(a, stream);
+  hipError_t e = launch_plan(a, BS, 16 / group, stream);
   if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.slots;
   hipLaunchKernelGGL((gqa_grid_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream, a,
                      group);
   return hipGetLastError();
 }
 
-template <class DT, int D, int BS>
-hipError_t launch_shared_t(const DecodeArgs& a, int group, hipStream_t stream) {
-  hipError_t e = launch_plan_shared(a, BS, 16 / group, stream);
-  if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
-  hipLaunchKernelGGL((shared_grid_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream,
-                     a, group);
-  return hipGetLastError();
-}
-
 template <class DT, int D>
-hipError_t by_block(const DecodeArgs& a, int bs, int group, bool shared, hipStream_t s) {
+hipError_t by_block(const DecodeArgs& a, int bs, int group, hipStream_t s) {
   switch (bs) {
-    case 8: return shared ? launch_shared_t<DT, D, 8>(a, group, s) : launch_t<DT, D, 8>(a, group, s);
-    case 16: return shared ? launch_shared_t<DT, D, 16>(a, group, s) : launch_t<DT, D, 16>(a, group, s);
-    case 32: return shared ? launch_shared_t<DT, D, 32>(a, group, s) : launch_t<DT, D, 32>(a, group, s);
+    case 8: return launch_t<DT, D, 8>(a, group, s);
+    case 16: return launch_t<DT, D, 16>(a, group, s);
+    case 32: return launch_t<DT, D, 32>(a, group, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <class DT>
-hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, bool shared, hipStream_t s) {
+hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s) {
   switch (D) {
-    case 64: return by_block<DT, 64>(a, bs, group, shared, s);
-    case 128: return by_block<DT, 128>(a, bs, group, shared, s);
+    case 64: return by_block<DT, 64>(a, bs, group, s);
+    case 128: return by_block<DT, 128>(a, bs, group, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// Any group size fits: an item holds 16 / G sequences (one for G > 8).
 bool gqa_supported(int dtype, int head_size, int block_size, int group) {
-  return (dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
-         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 2 && group <= 16;
-}
-
-hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
-                               int group, hipStream_t stream) {
-  switch (dtype) {
-    case 1: return by_head<F16>(a, head_size, block_size, group, false, stream);
-    case 2: return by_head<BF16>(a, head_size, block_size, group, false, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-// Every group size fits: an item holds 16 / G sequences (one for G = 16).
-bool shared_supported(int dtype, int head_size, int block_size, int group) {
   return (dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
          (block_size == 8 || block_size == 16 || block_size == 32) && group >= 1 && group <= 16;
 }
 
-hipError_t launch_decode_shared(const DecodeArgs& a, int dtype, int head_size, int block_size,
-                                int group, hipStream_t stream) {
+hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                             int group, hipStream_t stream) {
   switch (dtype) {
-    case 1: return by_head<F16>(a, head_size, block_size, group, true, stream);
-    case 2: return by_head<BF16>(a, head_size, block_size, group, true, stream);
+    case 1: return by_head<F16>(a, head_size, block_size, group, stream);
+    case 2: return by_head<BF16>(a, head_size, block_size, group, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -43,17 +43,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   constexpr int SPLIT = kThreads / D;  // partition strands per head dim
   const int h = blockIdx.x % a.num_heads;
   const int b = blockIdx.x / a.num_heads;
-  const int L = min(max(a.context_lens[b], 0), a.len_limit);
-  const int P = a.partition_size;
-  // shared-prefix decode: the plan kernel counted each sequence's partial results
-  const int NP = a.np_of ? min(a.np_of[b], a.max_partitions) : (L + P - 1) / P;
+  // the plan kernel counted each sequence's partial results
+  const int NP = min(a.np_of[b], a.slots);
   if (NP <= 1) return;  // written directly by phase 1
-  const int64_t base = ((int64_t)b * a.num_heads + h) * a.max_partitions;
+  const int64_t base = ((int64_t)b * a.num_heads + h) * a.slots;
 
   extern __shared__ float smem[];
   float* s_red = smem;              // [kWaves] block-reduction scratch
   float* s_num = smem + kWaves;     // [kThreads] partial numerators
-  float* s_w = s_num + kThreads;    // [max_partitions] partition weights
+  float* s_w = s_num + kThreads;    // [slots] partition weights
 
   float m = -INFINITY;
   for (int q = threadIdx.x; q < NP; q += kThreads) m = fmaxf(m, a.part_m[base + q]);
@@ -80,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
 
 template <class DT, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (kWaves + kThreads + size_t(a.max_partitions));
+  const size_t lds = sizeof(float) * (kWaves + kThreads + size_t(a.slots));
   hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_heads)),
                      dim3(kThreads), lds, stream, a);
   return hipGetLastError();

@@ -1,8 +1,9 @@
-// Paged decode attention, phase 1, vector-ALU variant (all element types).
+// Paged decode attention, phase 1, vector-ALU variant (fp32 caches; 16-bit ones run on the
+// matrix cores).
 //
-// One workgroup (4 wave64s) per (sequence, KV head, partition of
-// partition_size tokens), taken from the plan kernel's list of non-empty
-// partitions (work_plan.hip).  The cache layout is the one of the "Vllm" page,
+// One workgroup (4 wave64s) per (work item, KV head): an item is a range of
+// at most partition_size tokens of one sequence, taken from the plan kernel's
+// list (work_plan.hip).  The cache layout is the one of the "Vllm" page,
 // section "CacheEngine": a (block, KV head) key tile is
 // [head_size/x][block_size][x] and a value tile is [head_size][block_size],
 // each one contiguous run of head_size * block_size elements.  A wave
@@ -47,26 +48,24 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   constexpr int U = 2;  // tiles in flight per wave
   const int P = a.partition_size;
   const int Hkv = a.num_kv_heads;
-  // Workgroup t takes ticket t of the plan's list: work item t / Hkv, KV head t % Hkv.
+  // Workgroup t takes ticket t of the plan's list: work item t / Hkv, KV head t % Hkv.  Items
+  // here hold one sequence each (shared prefixes run on the matrix-core kernel).
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
-  const uint32_t pr = a.pairs[t / Hkv];
+  const uint4 it = a.items[t / Hkv];
   const int kh = t % Hkv;
-  const int b = int(pr / kMaxPartitions);
-  const int p = int(pr % kMaxPartitions);
-  const int L = min(max(a.context_lens[b], 0), a.len_limit);
-  const int tok0 = p * P;
+  const int b = int(it.x);
+  const int slot = int(it.y >> 8);
+  const int tok0 = int(it.z);
   const int h0 = kh * G;
-  if (tok0 >= L) {
-    if (p == 0) {  // empty context: defined as a zero output
-      for (int i = threadIdx.x; i < G * D; i += kThreads)
-        store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h0) * D + i, 0.f);
-    }
+  if (int(it.w) <= tok0) {  // the sole item of an empty context: defined as a zero output
+    for (int i = threadIdx.x; i < G * D; i += kThreads)
+      store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h0) * D + i, 0.f);
     return;
   }
-  const int ntok = min(P, L - tok0);
+  const int ntok = int(it.w) - tok0;
   const int nblk = (ntok + BS - 1) / BS;
-  const int NP = (L + P - 1) / P;
+  const int NP = a.np_of[b];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_uniform(threadIdx.x / kWave);
 
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int64_t block_bytes = tile_bytes * Hkv;
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks + (int64_t)p * (P / BS);
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks + tok0 / BS;
 
   // ---- 1. logits
   for (int j0 = wave; j0 < nblk; j0 += kWaves * U) {
@@ -220,10 +219,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += s_red[(w * G + g) * D + d];
     const int h = h0 + g;
-    if (NP == 1) {
+    if (NP <= 1) {
       store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h) * D + d, sum / s_stat[G + g]);
     } else {
-      const int64_t sp = ((int64_t)b * a.num_heads + h) * a.max_partitions + p;
+      const int64_t sp = ((int64_t)b * a.num_heads + h) * a.slots + slot;
       a.part_acc[sp * D + d] = sum;
       if (d == 0) {
         a.part_m[sp] = s_stat[g];
@@ -236,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 template <class DT, int D, int BS, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = valu_lds_bytes(G, D, a.partition_size);
-  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
-  hipError_t e = launch_plan(a, stream);
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.slots;
+  hipError_t e = launch_plan(a, BS, 1, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_valu_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(kThreads), lds,
                      stream, a);
@@ -277,20 +276,15 @@ hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s)
 }  // namespace
 
 bool valu_supported(int dtype, int head_size, int block_size, int group) {
-  (void)dtype;
-  return (head_size == 64 || head_size == 128) &&
+  return dtype == 0 && (head_size == 64 || head_size == 128) &&
          (block_size == 8 || block_size == 16 || block_size == 32) &&
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
                               int group, hipStream_t stream) {
-  switch (dtype) {
-    case 0: return by_head<F32>(a, head_size, block_size, group, stream);
-    case 1: return by_head<F16>(a, head_size, block_size, group, stream);
-    case 2: return by_head<BF16>(a, head_size, block_size, group, stream);
-  }
-  return hipErrorInvalidValue;
+  if (dtype != 0) return hipErrorInvalidValue;
+  return by_head<F32>(a, head_size, block_size, group, stream);
 }
 
 }  // namespace pkv

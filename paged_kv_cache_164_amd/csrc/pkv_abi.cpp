@@ -35,19 +35,12 @@ int elem_bytes(int dtype) {
   return 0;
 }
 
-int effective_partition(int partition_size) {
-  return partition_size == 0 ? pkv::kDefaultPartition : partition_size;
-}
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// The reduce kernel keeps one weight per partition in LDS (32 KiB at the limit).
-constexpr int64_t kMaxPartitions = pkv::kMaxPartitions;
 
 struct Resolved {
   pkv::DecodeArgs args;
   size_t ws_needed;
   int group;
+  int block_size;
   bool use_mfma;
 };
 
@@ -57,6 +50,17 @@ struct Groups {
   const int32_t* prefix_lens;
   int32_t count;
 };
+
+// Bytes of workspace for the given sizes (0 if invalid); shared by the size query, the decode
+// entry points and the reduce entry point, which must agree on the layout.
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_size,
+                           int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
+  if (partition_size < 0 || partition_size > pkv::kMaxPartition) return 0;
+  const int64_t slots = pkv::layout_slots(max_context_len, partition_size);
+  if (slots > pkv::kMaxPartitions + 2 * pkv::kTailChunks) return 0;
+  return pkv::workspace_layout(num_seqs, num_heads, head_size, slots).total;
+}
 
 // Shared validation of the decode entry points.
 int resolve_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -76,29 +80,27 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   if (head_size != 64 && head_size != 128) return fail(PKV_ERR_UNSUPPORTED, "head_size must be 64 or 128");
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return fail(PKV_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
-  const int P = effective_partition(partition_size);
-  if (P < block_size || P > pkv::kMaxPartition || P % block_size != 0)
-    return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 1024]");
-  // Grouped heads of 16-bit types go to the matrix-core kernel; everything else to the VALU one.
-  // The shared-prefix decode always runs on the matrix cores (16-bit types only).
+  // 16-bit caches run on the matrix-core kernel (any group size up to 16), fp32 on the VALU one.
   const bool shared = groups != nullptr;
-  const bool use_mfma = shared || (dtype != PKV_F32 && group > 1 &&
-                                   pkv::gqa_supported(dtype, head_size, block_size, group));
-  if (shared && !pkv::shared_supported(dtype, head_size, block_size, group))
+  const bool use_mfma = dtype != PKV_F32 && pkv::gqa_supported(dtype, head_size, block_size, group);
+  if (shared && !use_mfma)
     return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs PKV_F16 or PKV_BF16 and a group size <= 16");
   if (!use_mfma && !pkv::valu_supported(dtype, head_size, block_size, group))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
+  if (partition_size < 0 || partition_size > pkv::kMaxPartition ||
+      (partition_size > 0 && (partition_size < block_size || partition_size % block_size != 0)))
+    return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 2048]");
+  const int P = partition_size > 0 ? partition_size : pkv::auto_partition(use_mfma, block_size);
+  if (use_mfma && P > pkv::kMaxItemBlocks * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size may span at most 128 blocks");
   const size_t lds = use_mfma ? 0 : pkv::valu_lds_bytes(group, head_size, P);
   if (lds > pkv::kMaxDynamicLds)
     return fail(PKV_ERR_UNSUPPORTED, "group size x partition_size needs more than 64 KiB of LDS");
-  const int64_t max_parts = ceil_div(max_context_len, P);
-  if (max_parts > kMaxPartitions)
+  const int64_t slots = pkv::layout_slots(max_context_len, partition_size);
+  if (slots > pkv::kMaxPartitions + 2 * pkv::kTailChunks)
     return fail(PKV_ERR_UNSUPPORTED, "max_context_len / partition_size exceeds 8192 partitions");
-  // partial slots per (sequence, head); a shared prefix may end inside a partition
-  const int64_t slots = shared ? max_parts + 1 : std::max<int64_t>(max_parts, 1);
   const int64_t grid = (int64_t)num_seqs * num_kv_heads * slots;
   if (grid >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-  if (num_seqs >= pkv::kMaxPlanSeqs) return fail(PKV_ERR_UNSUPPORTED, "more than 2^19 - 1 sequences");
   if (num_seqs > 0 && (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens))
     return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
   if (shared && num_seqs > 0) {
@@ -106,48 +108,32 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
     if (groups->count < 1 || groups->count > num_seqs)
       return fail(PKV_ERR_INVALID_ARG, "num_groups must be in [1, num_seqs]");
   }
-  const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)slots);
-  const pkv::SharedWorkspaceLayout sw =
-      pkv::shared_workspace_layout(num_seqs, num_heads, head_size, (int)slots);
-  const size_t need = num_seqs > 0 ? (shared ? sw.total : w.total) : 0;
+  const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, slots);
+  const size_t need = num_seqs > 0 ? w.total : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(need) + " bytes");
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   pkv::DecodeArgs& a = r->args;
+  a = pkv::DecodeArgs{};
   a.out = out;
   a.query = query;
   a.key_cache = key_cache;
   a.value_cache = value_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.queue = a.pairs = nullptr;
-  a.prefetch_pad = nullptr;
   a.group_starts = shared ? groups->starts : nullptr;
   a.prefix_lens = shared ? groups->prefix_lens : nullptr;
   a.num_groups = shared ? groups->count : 0;
-  a.items = nullptr;
-  a.np_of = nullptr;
-  a.part_m = a.part_l = a.part_acc = nullptr;
-  if (need > 0 && shared) {
-    char* ws = static_cast<char*>(workspace);
-    a.queue = reinterpret_cast<uint32_t*>(ws);
-    a.prefetch_pad = ws + sw.pad_off;
-    a.np_of = reinterpret_cast<int32_t*>(ws + sw.np_off);
-    a.items = reinterpret_cast<uint4*>(ws + sw.items_off);
-    a.part_m = reinterpret_cast<float*>(ws + sw.m_off);
-    a.part_l = reinterpret_cast<float*>(ws + sw.l_off);
-    a.part_acc = reinterpret_cast<float*>(ws + sw.acc_off);
-  } else if (need > 0) {
+  if (need > 0) {
     char* ws = static_cast<char*>(workspace);
     a.queue = reinterpret_cast<uint32_t*>(ws);
     a.prefetch_pad = ws + w.pad_off;
-    a.pairs = reinterpret_cast<uint32_t*>(ws + w.pairs_off);
-    if (max_parts > 1) {
-      a.part_m = reinterpret_cast<float*>(ws + w.m_off);
-      a.part_l = reinterpret_cast<float*>(ws + w.l_off);
-      a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
-    }
+    a.np_of = reinterpret_cast<int32_t*>(ws + w.np_off);
+    a.items = reinterpret_cast<uint4*>(ws + w.items_off);
+    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
   }
   a.scale_log2 = scale * pkv::kLog2e;
   a.num_seqs = num_seqs;
@@ -156,27 +142,27 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   a.max_blocks = max_num_blocks_per_seq;
   a.len_limit = (int)std::min<int64_t>(max_context_len, (int64_t)max_num_blocks_per_seq * block_size);
   a.partition_size = P;
-  // max_context_len == 0 still launches one workgroup per (sequence, KV head): it writes the
-  // zero output of an empty context.
-  a.max_partitions = (int)slots;
+  a.tail_chunk = pkv::tail_chunk(P, block_size);
+  a.slots = (int)slots;
   r->ws_needed = need;
   r->group = group;
+  r->block_size = block_size;
   r->use_mfma = use_mfma;
   return PKV_OK;
 }
 
 int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
   if (r.args.num_seqs == 0) return PKV_OK;
-  hipError_t e = r.args.np_of
-      ? pkv::launch_decode_shared(r.args, dtype, head_size, block_size, r.group, s)
-      : r.use_mfma
+  hipError_t e = r.use_mfma
       ? pkv::launch_decode_gqa(r.args, dtype, head_size, block_size, r.group, s)
       : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention kernel launch");
 }
 
+// The reduce kernel reads each sequence's partial count from the workspace and returns at once
+// for sequences with a single item, so it is launched whatever the lengths turned out to be.
 int launch_phase2(const Resolved& r, int dtype, int head_size, hipStream_t s) {
-  if (r.args.max_partitions <= 1 || r.args.num_seqs == 0) return PKV_OK;
+  if (r.args.num_seqs == 0) return PKV_OK;
   hipError_t e = pkv::launch_reduce(r.args, dtype, head_size, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "reduce kernel launch");
 }
@@ -189,23 +175,7 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                           int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
-  const int P = effective_partition(partition_size);
-  if (P <= 0) return 0;
-  const int64_t parts = std::max<int64_t>(ceil_div(max_context_len, P), 1);
-  if (parts > kMaxPartitions) return 0;
-  return pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts).total;
-}
-
-size_t pkv_paged_attention_shared_workspace_size(int32_t num_seqs, int32_t num_heads,
-                                                 int32_t head_size, int32_t max_context_len,
-                                                 int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_size <= 0 || max_context_len < 0) return 0;
-  const int P = effective_partition(partition_size);
-  if (P <= 0) return 0;
-  const int64_t parts = ceil_div(max_context_len, P);
-  if (parts > kMaxPartitions) return 0;
-  return pkv::shared_workspace_layout(num_seqs, num_heads, head_size, (int)parts + 1).total;
+  return workspace_bytes_for(num_seqs, num_heads, head_size, max_context_len, partition_size);
 }
 
 #define PKV_DECODE_PARAMS                                                                     \
@@ -249,8 +219,7 @@ int pkv_paged_attention_decode_shared(
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = launch_phase1(r, dtype, head_size, block_size, s);
     if (rc != PKV_OK) return rc;
-    hipError_t e = pkv::launch_reduce(r.args, dtype, head_size, s);
-    return e == hipSuccess ? PKV_OK : hip_fail(e, "reduce kernel launch");
+    return launch_phase2(r, dtype, head_size, s);
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }
@@ -276,13 +245,14 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
     if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0)
       return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
     if (head_size != 64 && head_size != 128) return fail(PKV_ERR_UNSUPPORTED, "head_size must be 64 or 128");
-    const int P = effective_partition(partition_size);
-    if (P <= 0 || P > pkv::kMaxPartition) return fail(PKV_ERR_INVALID_ARG, "bad partition_size");
-    const int64_t parts = ceil_div(max_context_len, P);
-    if (parts > kMaxPartitions) return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
-    if (parts <= 1 || num_seqs == 0) return PKV_OK;
+    if (partition_size < 0 || partition_size > pkv::kMaxPartition)
+      return fail(PKV_ERR_INVALID_ARG, "bad partition_size");
+    if (num_seqs == 0) return PKV_OK;
     if (!out || !context_lens) return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
-    const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, (int)parts);
+    const int64_t slots = pkv::layout_slots(max_context_len, partition_size);
+    if (slots > pkv::kMaxPartitions + 2 * pkv::kTailChunks)
+      return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
+    const pkv::WorkspaceLayout w = pkv::workspace_layout(num_seqs, num_heads, head_size, slots);
     if (!workspace || workspace_bytes < w.total || (reinterpret_cast<uintptr_t>(workspace) & 255u))
       return fail(PKV_ERR_WORKSPACE, "workspace missing, misaligned or too small");
     Resolved r{};
@@ -290,14 +260,14 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
     char* ws = const_cast<char*>(static_cast<const char*>(workspace));
     a.out = out;
     a.context_lens = context_lens;
+    a.np_of = reinterpret_cast<int32_t*>(ws + w.np_off);
     a.part_m = reinterpret_cast<float*>(ws + w.m_off);
     a.part_l = reinterpret_cast<float*>(ws + w.l_off);
     a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.len_limit = max_context_len;
-    a.partition_size = P;
-    a.max_partitions = (int)parts;
+    a.slots = (int)slots;
     return launch_phase2(r, dtype, head_size, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");

@@ -1,15 +1,31 @@
-// Work plan of the decode kernels: the list of (sequence, partition) pairs that hold tokens.
+// Work plan of the decode kernels: the list of work items, one per (token range, sequences).
 //
-// The grid of a paged decode over B sequences with up to NP_max partitions each has
-// B * NP_max slots, most of them empty when context lengths are skewed; launching the empty
-// ones costs dispatcher time that the real ones wait for.  Instead, one workgroup lists the
-// non-empty pairs and persistent workers pull them from a queue.  Order of the list: every
-// full partition first (sequence-major), then each sequence's partial last partition, so the
-// shortest items run last and the end of the kernel drains quickly.  A sequence of length 0
-// gets one (empty) partial item: its worker writes the zero output.
+// A dense grid of B * partitions slots would be mostly empty when context lengths are skewed,
+// and launching the empty slots costs dispatcher time that the real ones wait for.  Instead,
+// one workgroup lists the non-empty items and the attention grid takes them in list order
+// (workgroup t: item t / num_kv_heads).  Each range of tokens [s, e) is cut into whole
+// partitions of P tokens, and what remains after the last whole partition into chunks of at
+// most Q = P / 2 tokens (whole blocks).  The list holds every whole partition first, then the
+// chunks from the longest to the shortest (eight size classes): the last items to start are
+// the shortest, so the end of the kernel drains quickly (longest-processing-time-first order).
 //
-// Layout in the caller's workspace (see workspace_layout): header[0] = queue counter (reset
-// here), header[1] = number of pairs; pairs[i] = b * kMaxPartitions + p.
+// Shared prefixes (optional): group g holds the sequences [s0, s1) = [starts[g], starts[g+1])
+// whose first `pre` tokens sit in the same physical blocks (beams or samples of one prompt,
+// PagedAttention's block sharing).  The prefix range [0, pre) gets items that carry up to
+// `per_item` members at once (their query rows become the columns of one item), so each shared
+// block is read once per item rather than once per member; each member's own range [pre, L)
+// gets items of its own.  pre = min(prefix_lens[g], every member's length), rounded down to a
+// multiple of the block size; a one-member group has pre = 0.  Without groups every sequence is
+// a group of its own.
+//
+// A sequence's partial-result slots are numbered in token order: its prefix items, then its own.
+// np_of[b] counts them; a sequence with one item (np_of <= 1) gets its output directly, and a
+// sequence of length 0 gets one empty item, which writes the zero output.  Group bounds are
+// clamped into [0, num_seqs], and at most `capacity` items are written, so a malformed group
+// list cannot make the call address out of bounds.
+//
+// Layout in the caller's workspace (see workspace_layout): header[1] = number of items;
+// items[i] = (b0, nseq | slot << 8, begin, end).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -18,79 +34,72 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
-// Exclusive prefix sum of one value per thread over the workgroup; returns the total in *total.
-__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+constexpr int kWavesPerPlan = kPlanThreads / 64;
+constexpr int kClasses = 1 + 8;  // whole partitions, then eight chunk size classes
+
+// Exclusive prefix sums over the workgroup of N values per thread, all at once.  On return
+// v[k] holds the sum of v[k] over the lower threads, plus the totals of all classes j < k
+// (the lists of the classes follow one another), and *total the sum of everything.
+// s_wave: [waves][N] shared scratch; s_base: [N + 1].
+template <int N>
+__device__ void block_exclusive_scan_classes(int (&v)[N], int (*s_wave)[N], int* s_base,
+                                             int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  int incl[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) incl[k] = v[k];
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int n = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += n;
-  }
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    int w = (lane < kPlanThreads / 64) ? s_wave[lane] : 0;
-    int wi = w;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int n = __shfl_up(wi, d, 64);
-      if (lane >= d) wi += n;
+    for (int k = 0; k < N; ++k) {
+      const int n = __shfl_up(incl[k], d, 64);
+      if (lane >= d) incl[k] += n;
     }
-    if (lane < kPlanThreads / 64) s_wave[lane] = wi - w;  // exclusive wave offsets
-    if (lane == kPlanThreads / 64 - 1) s_wave[kPlanThreads / 64] = wi;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) s_wave[wave][k] = incl[k];
   }
   __syncthreads();
-  const int r = s_wave[wave] + incl - v;
-  *total = s_wave[kPlanThreads / 64];
+  // lane k of wave 0 turns class k's wave totals into exclusive wave offsets; lane 0 then lays
+  // the classes one after another
+  if (wave == 0 && lane < N) {
+    int run = 0;
+    for (int w = 0; w < kWavesPerPlan; ++w) {
+      const int c = s_wave[w][lane];
+      s_wave[w][lane] = run;
+      run += c;
+    }
+    s_base[lane] = run;
+  }
   __syncthreads();
-  return r;
-}
-
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ context_lens,
-                                                            int num_seqs, int len_limit, int P,
-                                                            uint32_t* __restrict__ header,
-                                                            uint32_t* __restrict__ pairs) {
-  __shared__ int s_wave[kPlanThreads / 64 + 1];
-  // each thread owns a contiguous run of sequences
-  const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
-  const int b0 = threadIdx.x * per, b1 = min(num_seqs, b0 + per);
-  int nfull = 0, npart = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int L = min(max(context_lens[b], 0), len_limit);
-    nfull += L / P;
-    npart += (L % P != 0 || L == 0) ? 1 : 0;
-  }
-  int total_full, total_part;
-  int fo = block_exclusive_scan(nfull, s_wave, &total_full);
-  int po = total_full + block_exclusive_scan(npart, s_wave, &total_part);
-  for (int b = b0; b < b1; ++b) {
-    const int L = min(max(context_lens[b], 0), len_limit);
-    const int F = L / P;
-    for (int p = 0; p < F; ++p) pairs[fo++] = uint32_t(b) * kMaxPartitions + p;
-    if (L % P != 0 || L == 0) pairs[po++] = uint32_t(b) * kMaxPartitions + F;
-  }
   if (threadIdx.x == 0) {
-    header[0] = 0;  // queue counter
-    header[1] = uint32_t(total_full + total_part);
+    int run = 0;
+    for (int k = 0; k < N; ++k) {
+      const int c = s_base[k];
+      s_base[k] = run;
+      run += c;
+    }
+    s_base[N] = run;
   }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = s_base[k] + s_wave[wave][k] + incl[k] - v[k];
+  *total = s_base[N];
 }
 
-// Shared-prefix decode.  Group g holds the sequences [s0, s1) = [starts[g], starts[g+1]) whose
-// first `pre` tokens sit in the same physical blocks (beams or samples of one prompt).  Its
-// prefix is cut into partitions [p P, min((p + 1) P, pre)), each read once for up to
-// `per_item` members at a time (their query rows become the columns of one item); each member
-// then gets its own items over [pre + j P, min(pre + (j + 1) P, L)).  A member's partial slots
-// are its prefix partitions first, then its own: np_of[b] of them in all.
-// pre = min(prefix_lens[g], every member's length), rounded down to a multiple of the block size;
-// a one-member group has pre = 0.  The group bounds are clamped into [0, num_seqs], and no more
-// than `capacity` items are written, so a malformed group list cannot address out of bounds.
 struct GroupSpan {
   int s0, s1, pre;
 };
 
 __device__ __forceinline__ GroupSpan group_span(const DecodeArgs& a, int g, int bs) {
   GroupSpan r;
+  if (a.group_starts == nullptr) {
+    r.s0 = g;
+    r.s1 = g + 1;
+    r.pre = 0;
+    return r;
+  }
   r.s0 = min(max(a.group_starts[g], 0), a.num_seqs);
   r.s1 = min(max(a.group_starts[g + 1], r.s0), a.num_seqs);
   r.pre = 0;
@@ -102,78 +111,111 @@ __device__ __forceinline__ GroupSpan group_span(const DecodeArgs& a, int g, int 
   return r;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_shared_kernel(DecodeArgs a, int bs,
-                                                                   int per_item,
-                                                                   int64_t capacity) {
-  __shared__ int s_wave[kPlanThreads / 64 + 1];
-  const int P = a.partition_size;
-  for (int b = threadIdx.x; b < a.num_seqs; b += kPlanThreads) a.np_of[b] = 0;
-  __syncthreads();
-  // each thread owns a contiguous run of groups
-  const int per = (a.num_groups + kPlanThreads - 1) / kPlanThreads;
-  const int g0 = threadIdx.x * per, g1 = min(a.num_groups, g0 + per);
-  auto len_of = [&](int b) { return min(max(a.context_lens[b], 0), a.len_limit); };
-  int nfull = 0, npart = 0;
-  for (int g = g0; g < g1; ++g) {
-    const GroupSpan sp = group_span(a, g, bs);
-    const int chunks = (sp.s1 - sp.s0 + per_item - 1) / per_item;
-    nfull += chunks * (sp.pre / P);
-    npart += chunks * (sp.pre % P != 0 ? 1 : 0);
-    for (int b = sp.s0; b < sp.s1; ++b) {
-      const int L = len_of(b), r = L - sp.pre;
-      nfull += r / P;
-      npart += (r % P != 0 || L == 0) ? 1 : 0;
-    }
+// Items of a token range of length n: whole partitions, then remainder chunks of at most Q.
+__device__ __forceinline__ int whole_parts(int n, int P) { return n / P; }
+// Size class of a chunk of n (1 <= n <= Q) tokens: 1 (longest) .. 8 (shortest).
+__device__ __forceinline__ int chunk_class(int n, int Q) { return 1 + min(7, (Q - n) * 8 / Q); }
+
+// Per-thread counters (or next positions) of the item classes.  Classes are selected with
+// unrolled compare-and-add, never by a run-time array index, so the counters stay in registers.
+struct ClassCounters {
+  int v[kClasses];
+  __device__ void clear() {
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) v[k] = 0;
   }
-  int total_full, total_part;
-  int64_t fo = block_exclusive_scan(nfull, s_wave, &total_full);
-  int64_t po = total_full + block_exclusive_scan(npart, s_wave, &total_part);
-  auto put = [&](int64_t& pos, int b0, int nseq, int slot, int begin, int end) {
-    if (pos < capacity)
-      a.items[pos] = make_uint4(uint32_t(b0), uint32_t(nseq) | (uint32_t(slot) << 8),
-                                uint32_t(begin), uint32_t(end));
-    ++pos;
+  __device__ void add(int cls, int n) {
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) v[k] += (k == cls) ? n : 0;
+  }
+  // returns the current value of class cls and advances it
+  __device__ int take(int cls) {
+    int r = 0;
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) {
+      r = (k == cls) ? v[k] : r;
+      v[k] += (k == cls) ? 1 : 0;
+    }
+    return r;
+  }
+};
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs, int per_item,
+                                                            int64_t capacity) {
+  __shared__ int s_wave[kWavesPerPlan][kClasses];
+  __shared__ int s_base[kClasses + 1];
+  const int P = a.partition_size, Q = a.tail_chunk;
+  const int ngroups = a.group_starts ? a.num_groups : a.num_seqs;
+  if (a.group_starts) {  // sequences outside every group keep a count of 0 (the reduce skips them)
+    for (int b = threadIdx.x; b < a.num_seqs; b += kPlanThreads) a.np_of[b] = 0;
+    __syncthreads();
+  }
+  // each thread owns a contiguous run of groups
+  const int per = (ngroups + kPlanThreads - 1) / kPlanThreads;
+  const int g0 = threadIdx.x * per, g1 = min(ngroups, g0 + per);
+  auto len_of = [&](int b) { return min(max(a.context_lens[b], 0), a.len_limit); };
+
+  // pass 1: items per class.  A range [s, e) has (e - s) / P whole partitions and at most two
+  // chunks; `mult` copies of it (one per member chunk of a shared prefix).
+  ClassCounters c;
+  c.clear();
+  auto count_range = [&](int s, int e, int mult) {
+    const int F = whole_parts(e - s, P);
+    c.add(0, F * mult);
+    for (int t0 = s + F * P; t0 < e; t0 += Q) c.add(chunk_class(min(Q, e - t0), Q), mult);
   };
   for (int g = g0; g < g1; ++g) {
     const GroupSpan sp = group_span(a, g, bs);
-    const int npre = (sp.pre + P - 1) / P;
-    for (int c0 = sp.s0; c0 < sp.s1; c0 += per_item) {
-      const int n = min(per_item, sp.s1 - c0);
-      for (int p = 0; p < npre; ++p) {
-        const int begin = p * P, end = min(begin + P, sp.pre);
-        put(end - begin == P ? fo : po, c0, n, p, begin, end);
-      }
-    }
+    count_range(0, sp.pre, (sp.s1 - sp.s0 + per_item - 1) / per_item);
     for (int b = sp.s0; b < sp.s1; ++b) {
       const int L = len_of(b);
-      const int npriv = (L - sp.pre + P - 1) / P;
-      for (int j = 0; j < npriv; ++j) {
-        const int begin = sp.pre + j * P, end = min(begin + P, L);
-        put(end - begin == P ? fo : po, b, 1, npre + j, begin, end);
-      }
-      if (L == 0) put(po, b, 1, 0, 0, 0);  // its item writes the zero output
-      a.np_of[b] = max(npre + npriv, 1);
+      count_range(sp.pre, L, 1);
+      if (L == 0) c.add(kClasses - 1, 1);
+    }
+  }
+  int total;
+  block_exclusive_scan_classes(c.v, s_wave, s_base, &total);
+
+  // pass 2: the same items, each at its class's next position, slots in token order
+  auto put = [&](int cls, int b0, int nseq, int slot, int begin, int end) {
+    const int64_t pos = c.take(cls);
+    if (pos < capacity)
+      a.items[pos] = make_uint4(uint32_t(b0), uint32_t(nseq) | (uint32_t(slot) << 8),
+                                uint32_t(begin), uint32_t(end));
+  };
+  auto put_range = [&](int b0, int nseq, int s, int e, int slot) {
+    const int F = whole_parts(e - s, P);
+    for (int j = 0; j < F; ++j, ++slot) put(0, b0, nseq, slot, s + j * P, s + (j + 1) * P);
+    for (int t0 = s + F * P; t0 < e; t0 += Q, ++slot) {
+      const int t1 = min(t0 + Q, e);
+      put(chunk_class(t1 - t0, Q), b0, nseq, slot, t0, t1);
+    }
+    return slot;
+  };
+  for (int g = g0; g < g1; ++g) {
+    const GroupSpan sp = group_span(a, g, bs);
+    int npre = 0;
+    for (int c0 = sp.s0; c0 < sp.s1; c0 += per_item)
+      npre = put_range(c0, min(per_item, sp.s1 - c0), 0, sp.pre, 0);
+    for (int b = sp.s0; b < sp.s1; ++b) {
+      const int L = len_of(b);
+      const int n = put_range(b, 1, sp.pre, L, npre);
+      if (L == 0) put(kClasses - 1, b, 1, 0, 0, 0);  // its item writes the zero output
+      a.np_of[b] = max(n, 1);
     }
   }
   if (threadIdx.x == 0) {
     a.queue[0] = 0;
-    a.queue[1] = uint32_t(min<int64_t>(int64_t(total_full) + total_part, capacity));
+    a.queue[1] = uint32_t(min<int64_t>(total, capacity));
   }
 }
 
 }  // namespace
 
-hipError_t launch_plan_shared(const DecodeArgs& a, int block_size, int seqs_per_item,
-                              hipStream_t stream) {
-  const int64_t capacity = (int64_t)a.num_seqs * a.max_partitions;
-  hipLaunchKernelGGL(plan_shared_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, block_size,
+hipError_t launch_plan(const DecodeArgs& a, int block_size, int seqs_per_item, hipStream_t stream) {
+  const int64_t capacity = (int64_t)a.num_seqs * a.slots;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, block_size,
                      seqs_per_item, capacity);
-  return hipGetLastError();
-}
-
-hipError_t launch_plan(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens,
-                     a.num_seqs, a.len_limit, a.partition_size, a.queue, a.pairs);
   return hipGetLastError();
 }
 

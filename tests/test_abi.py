@@ -23,7 +23,7 @@ def test_exports_every_header_symbol():
     text = open(os.path.join(ROOT, "include", "pkv.h")).read()
     declared = set(re.findall(r"\b(pkv_\w+)\s*\(", text))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 10
+    assert len(declared) == 9
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -37,32 +37,19 @@ def test_single_hip_runtime_shared_with_torch():
 def test_workspace_size():
     _lib()
     a256 = lambda v: (v + 255) // 256 * 256
-    hdr = 256 + 8192  # queue header + prefetch pad
-    # one partition: header, pad, one work item per sequence
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 512, 512) == hdr + a256(4 * 4)
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 0, 0) == hdr + a256(4 * 4)
+
+    def expect(B, H, D, L, P):
+        # header, prefetch pad, partial counts, then S items of 16 B and S partial slots
+        # per (sequence, head) with S = ceil(L / P') + 4, P' = P or 1024 for auto
+        S = -(-L // (P or 1024)) + 4
+        n = B * H * S
+        return 256 + 8192 + a256(4 * B) + a256(16 * B * S) + 2 * a256(4 * n) + a256(4 * n * D)
+
+    for L, P in [(512, 512), (0, 0), (1025, 512), (2049, 0), (131072, 2048), (1, 16)]:
+        assert pkv.paged_attention_workspace_size(4, 8, 64, L, P) == expect(4, 8, 64, L, P), (L, P)
     assert pkv.paged_attention_workspace_size(0, 8, 64, 100, 0) == 0
-    # three partitions: header, work items, then m, l (256-byte aligned each) and acc
-    n = 4 * 8 * 3
-    stats = a256(n * 4)
-    acc = a256(n * 64 * 4)
-    expect = hdr + a256(4 * 3 * 4) + 2 * stats + acc
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 1025, 512) == expect
-    # auto partition size is 1024: 2049 tokens need three partitions too
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 2049, 0) == expect
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 1024, 0) == hdr + a256(4 * 4)
-
-
-def test_shared_workspace_size():
-    _lib()
-    a256 = lambda v: (v + 255) // 256 * 256
-    # header, pad, one int32 per sequence, then S = parts + 1 items of 16 B and partial slots
-    for L, P, parts in [(2049, 0, 3), (512, 512, 1), (0, 0, 0)]:
-        S = parts + 1
-        n = 4 * 8 * S
-        expect = 256 + 8192 + a256(4 * 4) + a256(4 * S * 16) + 2 * a256(n * 4) + a256(n * 64 * 4)
-        assert pkv.paged_attention_shared_workspace_size(4, 8, 64, L, P) == expect
-    assert pkv.paged_attention_shared_workspace_size(0, 8, 64, 100, 0) == 0
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 100, 4096) == 0   # partition too large
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 100, -1) == 0
 
 
 def _shared(lib, **over):
@@ -104,7 +91,8 @@ def _decode(lib, **over):
     (dict(num_heads=12), -1),            # not a multiple of num_kv_heads
     (dict(dtype=7), -1),
     (dict(partition_size=24), -1),       # not a multiple of block_size
-    (dict(partition_size=2048), -1),     # above 1024
+    (dict(partition_size=4096), -1),     # above 2048
+    (dict(dtype=1, block_size=8, partition_size=2048), -1),   # more than 128 blocks per item
     (dict(scale=float("nan")), -1),
     (dict(query=None), -3),
     (dict(max_context_len=4096), -4),    # needs a workspace

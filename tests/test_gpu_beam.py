@@ -27,6 +27,17 @@ def _decode(q, kc, vc, tables, lens, scale):
     return out
 
 
+def _decode_shared(q, kc, vc, tables, lens, scale, beams, prompt_len):
+    """The beams of one prompt are one group sharing the prompt's blocks."""
+    out = torch.empty_like(q)
+    B = q.shape[0]
+    gs = torch.arange(0, B + 1, beams, dtype=torch.int32, device=DEV)
+    pl = torch.full((B // beams,), prompt_len, dtype=torch.int32, device=DEV)
+    pkv.paged_attention_decode_shared(out, q, kc, vc, torch.from_numpy(tables).to(DEV),
+                                      torch.from_numpy(lens).to(DEV), gs, pl, scale, int(lens.max()))
+    return out
+
+
 def _beam_run(num_prompts, n_pairs=None):
     bc = make_beam_case(num_prompts=num_prompts)
     bs = bc.cfg.block_size
@@ -56,6 +67,7 @@ def _beam_run(num_prompts, n_pairs=None):
     pkv.copy_blocks([kc], [vc], torch.from_numpy(mapping).to(DEV))
     pkv.reshape_and_cache(nk.to(DEV), nv.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV))
     out1 = _decode(q, kc, vc, tables, lens, bc.scale)
+    sh1 = _decode_shared(q, kc, vc, tables, lens, bc.scale, bc.beams, bc.prompt_len)
     torch.cuda.synchronize()
     log(f"beam: {len(pairs)} copy-on-write pairs")
 
@@ -69,13 +81,15 @@ def _beam_run(num_prompts, n_pairs=None):
         all_pairs = sorted({(int(g.integers(B)), int(g.integers(H))) for _ in range(n_pairs)})
     ref_out = OA.paged_decode(storage_bits(bc.query), kb, vb, "f16", tables, lens, bc.scale,
                               pairs=all_pairs)
-    got = out1.cpu().to(torch.float64).numpy()
-    if all_pairs is not None:
-        idx = tuple(np.array(all_pairs).T)
-        got, ref_out = got[idx], ref_out[idx]
-    ok, err, ratio = within_tolerance(got, ref_out, "f16")
-    log(f"beam decode vs oracle: max|err|={err:.3e} ratio={ratio:.3f}")
-    assert ok
+    for name, o in (("plain", out1), ("shared-prefix", sh1)):
+        got = o.cpu().to(torch.float64).numpy()
+        ref_sel = ref_out
+        if all_pairs is not None:
+            idx = tuple(np.array(all_pairs).T)
+            got, ref_sel = got[idx], ref_out[idx]
+        ok, err, ratio = within_tolerance(got, ref_sel, "f16")
+        log(f"beam {name} decode vs oracle: max|err|={err:.3e} ratio={ratio:.3f}")
+        assert ok
 
     # (ii) swap 25% of the blocks in use out to pinned host memory and back into new ids
     in_use = np.unique(tables[tables >= 0])
@@ -97,9 +111,11 @@ def _beam_run(num_prompts, n_pairs=None):
     remap = dict(zip(chosen.tolist(), new_ids.tolist()))
     tables2 = np.vectorize(lambda t: remap.get(int(t), int(t)))(tables).astype(np.int32)
     out2 = _decode(q, kc, vc, tables2, lens, bc.scale)
+    sh2 = _decode_shared(q, kc, vc, tables2, lens, bc.scale, bc.beams, bc.prompt_len)
     torch.cuda.synchronize()
     log(f"beam: swapped {n} blocks out and back")
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(sh1.view(torch.int16), sh2.view(torch.int16))
 
 
 def test_beam_small_all_outputs():

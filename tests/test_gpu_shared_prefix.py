@@ -86,14 +86,16 @@ def test_shared_prefix_edge_lengths():
         assert np.all(got[2:5] == 0.0)
 
 
-def test_shared_prefix_bitwise_equals_plain_decode():
-    """GQA with prefixes on partition boundaries: the same partitions on the same kernel, only
-    the columns of an item come from several sequences, so the results agree bit for bit."""
-    c = make_prefix_case([4, 4, 3, 1], [1024, 2048, 1024, 0], (1, 2000), num_heads=32,
-                         num_kv_heads=8, head_size=128, block_size=16, dtype="bf16")
+@pytest.mark.parametrize("dtype,Hq,Hkv", [("bf16", 32, 8), ("f16", 8, 8)])
+def test_shared_prefix_bitwise_equals_plain_decode(dtype, Hq, Hkv):
+    """Prefixes on partition boundaries (auto partition: 2048 tokens): both calls cut every
+    sequence at the same tokens and run the same kernel; only the columns of an item come from
+    several sequences, so the results agree bit for bit."""
+    c = make_prefix_case([4, 4, 3, 1], [2048, 4096, 2048, 0], (1, 2600), num_heads=Hq,
+                         num_kv_heads=Hkv, head_size=128, block_size=16, dtype=dtype)
     inputs = _gpu_inputs(c)
-    for P in (0, 512):
-        log(f"shared vs plain bitwise P={P}")
+    for P in (0, 1024, 512):
+        log(f"shared vs plain bitwise {dtype} {Hq}/{Hkv} P={P}")
         a = _shared(c, P, inputs)
         b = _plain(c, P, inputs)
         torch.cuda.synchronize()
@@ -105,7 +107,7 @@ def test_shared_prefix_repeatable_and_workspace_reuse():
     c = make_prefix_case([4, 2], [512, 160], (0, 700), num_heads=8, num_kv_heads=8,
                          head_size=128, block_size=16, dtype="f16")
     inputs = _gpu_inputs(c)
-    need = pkv.paged_attention_shared_workspace_size(len(c.context_lens), 8, 128,
+    need = pkv.paged_attention_workspace_size(len(c.context_lens), 8, 128,
                                                      int(c.context_lens.max()), 256)
     ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=DEV)
     a = _shared(c, 256, inputs, ws)
