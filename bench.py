@@ -316,7 +316,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
-                   "partition_size": P or 1024, "kv_tokens": int(lens.sum()), "max_context_len": lmax,
+                   "partition_size": P or ("auto: 2048" if eb == 2 and bs >= 16 else "auto: 1024"),
+                   "kv_tokens": int(lens.sum()), "max_context_len": lmax,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
