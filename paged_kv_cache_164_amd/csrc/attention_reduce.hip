@@ -1,86 +1,89 @@
-// Paged decode attention, phase 2: combine the partitions of long contexts.
+// Paged decode attention, phase 2: merge each sequence's partial results.
 //
-// For one (sequence, query head) with partitions p = 0..NP-1 carrying
-// (m_p, l_p, acc_p) in base-2 logit units:
+// For one (sequence, query head) with items p = 0..NP-1 carrying (m_p, l_p, acc_p) in base-2
+// logit units:
 //   M = max_p m_p,  w_p = 2^(m_p - M)
 //   out = sum_p w_p acc_p / sum_p w_p l_p
-// which equals the softmax-weighted sum over the whole context (the
-// log-sum-exp identity behind split-K / FlashDecoding decoding; the "Vllm"
-// page, "Prefill vs decoding" item 5).  The summation order is fixed, so
-// results are run-to-run deterministic.
+// which equals the softmax-weighted sum over the whole context (the log-sum-exp identity
+// behind split-K / FlashDecoding decoding; the "Vllm" page, "Prefill vs decoding" item 5).
+//
+// One workgroup per (sequence, query head).  Its threads form S strands of D/4 threads; a
+// thread holds 4 dims of one strand, and strand s takes items s, s + S, ... with its own
+// running maximum (so all of its loads go out at once, with no workgroup-wide max first).  The
+// strands are then merged in LDS, always in strand order: the result is run-to-run
+// deterministic.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
-__device__ __forceinline__ float block_max(float v, float* scratch) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float r = scratch[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, scratch[w]);
-  return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) scratch[wave] = v;
-  __syncthreads();
-  float r = scratch[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r += scratch[w];
-  return r;
-}
-
 template <class DT, int D>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
-  constexpr int SPLIT = kThreads / D;  // partition strands per head dim
-  const int h = blockIdx.x % a.num_heads;
-  const int b = blockIdx.x / a.num_heads;
-  // the plan kernel counted each sequence's partial results
+  constexpr int TPS = D / 4;           // threads per strand (4 dims each)
+  constexpr int S = kThreads / TPS;    // strands
+  const int row = blockIdx.x;          // b * num_heads + h
+  const int b = row / a.num_heads;
   const int NP = min(a.np_of[b], a.slots);
   if (NP <= 1) return;  // written directly by phase 1
-  const int64_t base = ((int64_t)b * a.num_heads + h) * a.slots;
+  const int s = threadIdx.x / TPS, d0 = (threadIdx.x % TPS) * 4;
+  const int64_t base = (int64_t)row * a.slots;
+  const float* pm = a.part_m + base;
+  const float* pl = a.part_l + base;
+  const float* pacc = a.part_acc + base * D + d0;
 
-  extern __shared__ float smem[];
-  float* s_red = smem;              // [kWaves] block-reduction scratch
-  float* s_num = smem + kWaves;     // [kThreads] partial numerators
-  float* s_w = s_num + kThreads;    // [slots] partition weights
-
-  float m = -INFINITY;
-  for (int q = threadIdx.x; q < NP; q += kThreads) m = fmaxf(m, a.part_m[base + q]);
-  const float M = block_max(m, s_red);
-  float den = 0.f;
-  for (int q = threadIdx.x; q < NP; q += kThreads) {
-    const float w = exp2f(a.part_m[base + q] - M);
-    s_w[q] = w;
-    den += w * a.part_l[base + q];
+  // strand s: online merge of its items (running max ms, sum ls, vector acc)
+  float ms = -INFINITY, ls = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int q = s; q < NP; q += S) {
+    const float mq = pm[q], lq = pl[q];
+    const float4 aq = *reinterpret_cast<const float4*>(pacc + (int64_t)q * D);
+    const float mn = fmaxf(ms, mq);
+    const float c = exp2f(ms - mn), w = exp2f(mq - mn);  // ms = -inf at first: c = 0
+    ls = fmaf(ls, c, w * lq);
+    acc.x = fmaf(acc.x, c, w * aq.x);
+    acc.y = fmaf(acc.y, c, w * aq.y);
+    acc.z = fmaf(acc.z, c, w * aq.z);
+    acc.w = fmaf(acc.w, c, w * aq.w);
+    ms = mn;
   }
-  den = block_sum(den, s_red);  // contains the barrier that publishes s_w
-
-  const int d = threadIdx.x % D, strand = threadIdx.x / D;
-  float num = 0.f;
-  for (int q = strand; q < NP; q += SPLIT) num = fmaf(s_w[q], a.part_acc[(base + q) * D + d], num);
-  s_num[threadIdx.x] = num;
+  __shared__ float s_m[S], s_l[S];
+  __shared__ float4 s_acc[S][TPS];
+  if (threadIdx.x % TPS == 0) {
+    s_m[s] = ms;
+    s_l[s] = ls;
+  }
+  s_acc[s][threadIdx.x % TPS] = acc;
   __syncthreads();
-  if (strand == 0) {
+  if (s != 0) return;
+  // strand 0's threads merge all strands, in strand order (strands without items hold m = -inf)
+  float M = s_m[0];
 #pragma unroll
-    for (int s = 1; s < SPLIT; ++s) num += s_num[s * D + d];
-    store_elem(DT(), a.out, ((int64_t)b * a.num_heads + h) * D + d, num / den);
+  for (int k = 1; k < S; ++k) M = fmaxf(M, s_m[k]);
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const float w = exp2f(s_m[k] - M);
+    const float4 v = s_acc[k][threadIdx.x];
+    den = fmaf(w, s_l[k], den);
+    num.x = fmaf(w, v.x, num.x);
+    num.y = fmaf(w, v.y, num.y);
+    num.z = fmaf(w, v.z, num.z);
+    num.w = fmaf(w, v.w, num.w);
   }
+  const float inv = 1.f / den;
+  const int64_t o = (int64_t)row * D + d0;
+  store_elem(DT(), a.out, o + 0, num.x * inv);
+  store_elem(DT(), a.out, o + 1, num.y * inv);
+  store_elem(DT(), a.out, o + 2, num.z * inv);
+  store_elem(DT(), a.out, o + 3, num.w * inv);
 }
 
 template <class DT, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const size_t lds = sizeof(float) * (kWaves + kThreads + size_t(a.slots));
   hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_heads)),
-                     dim3(kThreads), lds, stream, a);
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

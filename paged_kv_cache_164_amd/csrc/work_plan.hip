@@ -29,6 +29,8 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
+#include <algorithm>
+
 namespace pkv {
 namespace {
 
@@ -45,6 +47,7 @@ template <int N>
 __device__ void block_exclusive_scan_classes(int (&v)[N], int (*s_wave)[N], int* s_base,
                                              int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
   int incl[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) incl[k] = v[k];
@@ -61,26 +64,28 @@ __device__ void block_exclusive_scan_classes(int (&v)[N], int (*s_wave)[N], int*
     for (int k = 0; k < N; ++k) s_wave[wave][k] = incl[k];
   }
   __syncthreads();
-  // lane k of wave 0 turns class k's wave totals into exclusive wave offsets; lane 0 then lays
-  // the classes one after another
-  if (wave == 0 && lane < N) {
-    int run = 0;
-    for (int w = 0; w < kWavesPerPlan; ++w) {
-      const int c = s_wave[w][lane];
-      s_wave[w][lane] = run;
-      run += c;
+  // Wave 0: lane k (< N) turns class k's wave totals into exclusive wave offsets and finds the
+  // class total; a scan over lanes then lays the classes one after another.
+  if (wave == 0) {
+    int tot = 0;
+    if (lane < N) {
+      int c[kWavesPerPlan];
+#pragma unroll
+      for (int w = 0; w < kWavesPerPlan; ++w) c[w] = (w < nwaves) ? s_wave[w][lane] : 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerPlan; ++w) {
+        if (w < nwaves) s_wave[w][lane] = tot;
+        tot += c[w];
+      }
     }
-    s_base[lane] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int k = 0; k < N; ++k) {
-      const int c = s_base[k];
-      s_base[k] = run;
-      run += c;
+    int cls = tot;  // inclusive scan of the class totals over lanes 0..N-1
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int n = __shfl_up(cls, d, 64);
+      if (lane >= d) cls += n;
     }
-    s_base[N] = run;
+    if (lane < N) s_base[lane] = cls - tot;
+    if (lane == N - 1) s_base[N] = cls;
   }
   __syncthreads();
 #pragma unroll
@@ -147,11 +152,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
   const int P = a.partition_size, Q = a.tail_chunk;
   const int ngroups = a.group_starts ? a.num_groups : a.num_seqs;
   if (a.group_starts) {  // sequences outside every group keep a count of 0 (the reduce skips them)
-    for (int b = threadIdx.x; b < a.num_seqs; b += kPlanThreads) a.np_of[b] = 0;
+    for (int b = threadIdx.x; b < a.num_seqs; b += blockDim.x) a.np_of[b] = 0;
     __syncthreads();
   }
   // each thread owns a contiguous run of groups
-  const int per = (ngroups + kPlanThreads - 1) / kPlanThreads;
+  const int per = (ngroups + blockDim.x - 1) / blockDim.x;
   const int g0 = threadIdx.x * per, g1 = min(ngroups, g0 + per);
   auto len_of = [&](int b) { return min(max(a.context_lens[b], 0), a.len_limit); };
 
@@ -183,9 +188,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
       a.items[pos] = make_uint4(uint32_t(b0), uint32_t(nseq) | (uint32_t(slot) << 8),
                                 uint32_t(begin), uint32_t(end));
   };
+  // Whole partitions take consecutive places of class 0.  A thread writes up to kOwnWhole of
+  // them itself; longer runs are queued to its wave, which writes them with all lanes below.
+  constexpr int kOwnWhole = 8;
+  int q_b0 = 0, q_nseq = 0, q_s = 0, q_slot = 0, q_count = 0;
+  int64_t q_pos = 0;
   auto put_range = [&](int b0, int nseq, int s, int e, int slot) {
     const int F = whole_parts(e - s, P);
-    for (int j = 0; j < F; ++j, ++slot) put(0, b0, nseq, slot, s + j * P, s + (j + 1) * P);
+    const int64_t w0 = c.v[0];
+    c.v[0] += F;
+    if (F > kOwnWhole && q_count == 0) {  // one queued run per thread (see below)
+      q_b0 = b0, q_nseq = nseq, q_s = s, q_slot = slot, q_count = F, q_pos = w0;
+      slot += F;
+    } else {
+      for (int j = 0; j < F; ++j, ++slot) {
+        if (w0 + j < capacity)
+          a.items[w0 + j] = make_uint4(uint32_t(b0), uint32_t(nseq) | (uint32_t(slot) << 8),
+                                       uint32_t(s + j * P), uint32_t(s + (j + 1) * P));
+      }
+    }
     for (int t0 = s + F * P; t0 < e; t0 += Q, ++slot) {
       const int t1 = min(t0 + Q, e);
       put(chunk_class(t1 - t0, Q), b0, nseq, slot, t0, t1);
@@ -204,6 +225,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
       a.np_of[b] = max(n, 1);
     }
   }
+  // the queued runs of whole partitions, one lane's run at a time, 64 items per step
+  unsigned long long pending = __ballot(q_count > 0);
+  while (pending) {
+    const int l = __ffsll(pending) - 1;
+    pending &= pending - 1;
+    const int b0 = __shfl(q_b0, l, 64), nseq = __shfl(q_nseq, l, 64), s0 = __shfl(q_s, l, 64);
+    const int slot0 = __shfl(q_slot, l, 64), F = __shfl(q_count, l, 64);
+    const int64_t w0 = __shfl(q_pos, l, 64);
+    for (int j = threadIdx.x & 63; j < F; j += 64) {
+      if (w0 + j < capacity)
+        a.items[w0 + j] = make_uint4(uint32_t(b0), uint32_t(nseq) | (uint32_t(slot0 + j) << 8),
+                                     uint32_t(s0 + j * P), uint32_t(s0 + (j + 1) * P));
+    }
+  }
   if (threadIdx.x == 0) {
     a.queue[0] = 0;
     a.queue[1] = uint32_t(min<int64_t>(total, capacity));
@@ -214,7 +249,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
 
 hipError_t launch_plan(const DecodeArgs& a, int block_size, int seqs_per_item, hipStream_t stream) {
   const int64_t capacity = (int64_t)a.num_seqs * a.slots;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, block_size,
+  // one thread per group up to 1024 threads, in whole waves
+  const int groups = a.group_starts ? a.num_groups : a.num_seqs;
+  const int threads = (int)std::min<int64_t>(kPlanThreads, std::max<int64_t>(64, (groups + 63) / 64 * 64));
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(threads), 0, stream, a, block_size,
                      seqs_per_item, capacity);
   return hipGetLastError();
 }
