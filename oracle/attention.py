@@ -37,9 +37,10 @@ import numpy as np
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Exact float64 value of stored elements given as raw bits.
 
-    ``dtype`` is 'f32' (uint32 bits), 'f16' (uint16, IEEE binary16) or
+    ``dtype`` is 'f32' (uint32 bits), 'f16' (uint16, IEEE binary16),
     'bf16' (uint16: the upper half of an IEEE binary32, so shifting the bits
-    left by 16 gives the binary32 with the same value).
+    left by 16 gives the binary32 with the same value) or 'e4m3' (uint8, the
+    8-bit float of oracle.fp8, without its scale).
     """
     if dtype == "f32":
         return bits.view(np.float32).astype(np.float64)
@@ -47,6 +48,9 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float16).astype(np.float64)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        from oracle.fp8 import e4m3_decode
+        return e4m3_decode(bits)
     raise ValueError(dtype)
 
 
@@ -56,11 +60,13 @@ def chunk_width(bits: np.ndarray) -> int:
 
 
 def gather_kv(key_bits: np.ndarray, value_bits: np.ndarray, dtype: str, table_row: np.ndarray,
-              L: int, kv_head: int) -> Tuple[np.ndarray, np.ndarray]:
+              L: int, kv_head: int, k_scale: float = 1.0,
+              v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """Dense K[t, d], V[t, d] (float64, t < L) of one sequence and one KV head.
 
-    K[t, d] = key_cache[table[t // bs], kv_head, d // x, t % bs, d % x]
-    V[t, d] = value_cache[table[t // bs], kv_head, d, t % bs]
+    K[t, d] = key_cache[table[t // bs], kv_head, d // x, t % bs, d % x] * k_scale
+    V[t, d] = value_cache[table[t // bs], kv_head, d, t % bs] * v_scale
+    (the scales are 1 except for an 8-bit cache; they are taken as the float32 the kernel gets)
     """
     bs = key_bits.shape[3]
     x = key_bits.shape[4]
@@ -72,7 +78,7 @@ def gather_kv(key_bits: np.ndarray, value_bits: np.ndarray, dtype: str, table_ro
     off = t % bs
     K = key_bits[blk[:, None], kv_head, (d // x)[None, :], off[:, None], (d % x)[None, :]]
     V = value_bits[blk[:, None], kv_head, d[None, :], off[:, None]]
-    return widen(K, dtype), widen(V, dtype)
+    return widen(K, dtype) * as_scale(k_scale), widen(V, dtype) * as_scale(v_scale)
 
 
 def dense_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -92,11 +98,13 @@ def as_scale(scale: float) -> float:
 
 def paged_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
                  dtype: str, block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
-                 pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                 pairs: Optional[Iterable[Tuple[int, int]]] = None, kv_dtype: Optional[str] = None,
+                 k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Output [B, Hq, D] in float64 (or only the (b, h) in ``pairs``; other rows stay NaN).
 
     ``query_bits`` [B, Hq, D], ``key_bits`` [NB, Hkv, D/x, bs, x],
-    ``value_bits`` [NB, Hkv, D, bs] hold raw storage bits of ``dtype``.
+    ``value_bits`` [NB, Hkv, D, bs] hold raw storage bits of ``dtype`` (the caches of
+    ``kv_dtype`` when given, e.g. 'e4m3' with its per-cache scales).
     """
     B, Hq, D = query_bits.shape
     Hkv = key_bits.shape[1]
@@ -111,7 +119,8 @@ def paged_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.nd
         by_seq_head.setdefault((b, h // group), []).append(h)
     for (b, g), heads in sorted(by_seq_head.items()):
         L = int(context_lens[b])
-        K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, g)
+        K, V = gather_kv(key_bits, value_bits, kv_dtype or dtype, block_tables[b], L, g,
+                         k_scale, v_scale)
         for h in heads:
             q = widen(query_bits[b, h], dtype)
             out[b, h] = dense_decode(q, K, V, sc)
