@@ -193,6 +193,32 @@ int pkv_paged_attention_decode_shared(void* out, const void* query, const void* 
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention over an 8-bit KV cache: keys and values stored as OCP FP8
+ * E4M3 codes with one float scale per cache (key = code * k_scale, value =
+ * code * v_scale), the 8-bit KV-cache quantisation the AIGC interview book
+ * names for TurboMind (LMDeploy section).  The E4M3 format: sign, 4 exponent
+ * bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 is NaN, largest
+ * value 448.  Computes the attention of pkv_paged_attention_decode on the
+ * dequantised keys and values, with fp32 accumulation.
+ *   key_cache    uint8 [num_blocks, num_kv_heads, head_size/16, block_size, 16]
+ *                (x = 16 / sizeof = 16)
+ *   value_cache  uint8 [num_blocks, num_kv_heads, head_size, block_size]
+ *   query, out   PKV_F16 or PKV_BF16 (`dtype`), as for the 16-bit call
+ *   k_scale, v_scale  host floats, finite and > 0
+ * All other arguments, the partitioning, the workspace
+ * (pkv_paged_attention_workspace_size) and the error codes as for
+ * pkv_paged_attention_decode; group sizes 1..16.
+ */
+int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, float scale, float k_scale,
+                                   float v_scale, int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                   int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                   int32_t dtype, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Scatter new tokens' keys and values into their cache slots (the KV-cache
  * write of the cybasar.com nano-vLLM article, section 5.2.3, in the block
  * layout above):
@@ -213,6 +239,21 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
                           const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                           int32_t head_size, int32_t block_size, int64_t num_blocks,
                           int64_t key_stride, int64_t value_stride, int32_t dtype, void* stream);
+
+/*
+ * pkv_reshape_and_cache into an 8-bit cache (layouts of
+ * pkv_paged_attention_decode_fp8): each element x of key / value (PKV_F16 or
+ * PKV_BF16, `dtype`) is stored as the E4M3 code of clamp(x / scale, -448,
+ * 448), the division rounded to float32 and the conversion to the nearest
+ * code, ties to even; a NaN input gives a NaN code.  Slots, strides, skipping
+ * and errors as for pkv_reshape_and_cache; head_size a multiple of 16;
+ * key_cache 16-byte aligned.
+ */
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                              int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                              int32_t dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * Copy whole blocks inside the device cache, for every layer (CacheEngine

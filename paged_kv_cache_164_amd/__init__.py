@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     library_path,
     paged_attention_decode,
     paged_attention_decode_shared,
+    paged_attention_decode_fp8,
+    reshape_and_cache_fp8,
     paged_attention_partitions,
     paged_attention_reduce,
     paged_attention_workspace_size,

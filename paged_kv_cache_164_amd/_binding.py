@@ -36,6 +36,10 @@ _SIGNATURES = {
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_decode_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
                                           + _DECODE_ARGTYPES[6:]),
+    "pkv_paged_attention_decode_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                       + _DECODE_ARGTYPES[7:]),
+    "pkv_reshape_and_cache_fp8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
+                                           _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
     "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
                                        _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
     "pkv_copy_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p]),
@@ -107,14 +111,19 @@ def paged_attention_workspace_size(num_seqs: int, num_heads: int, head_size: int
 
 
 def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, workspace, stream):
+                 max_context_len, partition_size, workspace, stream, kv8=False):
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens)
     B, Hq, D = query.shape
     NB, Hkv, Dx, bs, x = key_cache.shape
     dt = _dtype_code(query)
-    if not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
+    if kv8:
+        if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+            raise PKVError("an 8-bit cache holds uint8 codes")
+        if query.dtype != out.dtype or query.element_size() != 2:
+            raise PKVError("query and out must share one 16-bit dtype")
+    elif not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
         raise PKVError("query, caches and out must share one dtype")
-    if x * query.element_size() != 16 or Dx * x != D:
+    if x * key_cache.element_size() != 16 or Dx * x != D:
         raise PKVError(f"key_cache must be [num_blocks, Hkv, D/x, bs, x] with x = 16/sizeof ({tuple(key_cache.shape)})")
     if tuple(value_cache.shape) != (NB, Hkv, D, bs):
         raise PKVError(f"value_cache must be [num_blocks, Hkv, D, bs], got {tuple(value_cache.shape)}")
@@ -162,6 +171,18 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
         raise PKVError("group_starts must be int32 [num_groups + 1], prefix_lens int32 [num_groups]")
     args = args[:6] + (group_starts.data_ptr(), prefix_lens.data_ptr(), ng) + args[6:]
     _check(library().pkv_paged_attention_decode_shared(*args), "pkv_paged_attention_decode_shared")
+    return out
+
+
+def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
+                               scale, k_scale, v_scale, max_context_len, partition_size=0,
+                               workspace=None, stream=None):
+    """Decode over an 8-bit (FP8 E4M3) cache: key_cache uint8 [NB, Hkv, D/16, bs, 16],
+    value_cache uint8 [NB, Hkv, D, bs]; key = code * k_scale, value = code * v_scale."""
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream, kv8=True)
+    args = args[:7] + (float(k_scale), float(v_scale)) + args[7:]
+    _check(library().pkv_paged_attention_decode_fp8(*args), "pkv_paged_attention_decode_fp8")
     return out
 
 
@@ -214,6 +235,33 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=N
            "pkv_reshape_and_cache")
 
 
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                         stream=None):
+    """key/value [N, Hkv, D] fp16/bf16 -> FP8 E4M3 codes in the 8-bit caches (x = 16)."""
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping)
+    N, Hkv, D = key.shape
+    NB, Hkv2, Dx, bs, x = key_cache.shape
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8 or x != 16:
+        raise PKVError("8-bit caches: uint8 [NB, Hkv, D/16, bs, 16] and [NB, Hkv, D, bs]")
+    if Hkv2 != Hkv or Dx * x != D or tuple(value.shape) != (N, Hkv, D):
+        raise PKVError("key/value [N, Hkv, D] must match the cache layout")
+    if tuple(value_cache.shape) != (NB, Hkv, D, bs) or key.dtype != value.dtype:
+        raise PKVError("value_cache must be [num_blocks, Hkv, D, bs]; key and value one dtype")
+    for t in (key, value):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise PKVError("key/value need stride(-1) == 1 and stride(1) == head_size")
+    if not (key_cache.is_contiguous() and value_cache.is_contiguous()):
+        raise PKVError("caches must be contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N or not slot_mapping.is_contiguous():
+        raise PKVError("slot_mapping must be contiguous int64 with one entry per token")
+    _check(library().pkv_reshape_and_cache_fp8(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                               value_cache.data_ptr(), slot_mapping.data_ptr(), N,
+                                               Hkv, D, bs, NB, key.stride(0), value.stride(0),
+                                               _dtype_code(key), float(k_scale), float(v_scale),
+                                               _stream(stream)),
+           "pkv_reshape_and_cache_fp8")
+
+
 def copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],
                 block_mapping: torch.Tensor, stream=None, _ptr_buffers=None):
     """Copy whole blocks (src, dst) in every layer's key and value cache (device mapping [n, 2] int64)."""
@@ -260,11 +308,12 @@ def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping, stream=None
 
 
 def decode_bytes(context_lens, num_heads: int, num_kv_heads: int, head_size: int, block_size: int,
-                 elem_bytes: int) -> int:
+                 elem_bytes: int, kv_elem_bytes: Optional[int] = None) -> int:
     """Algorithmic HBM bytes of one decode call: every context token's K and V (all KV heads),
-    q in and out, one int32 block id per block and one int32 length per sequence."""
+    q in and out, one int32 block id per block and one int32 length per sequence.  For an
+    8-bit cache pass kv_elem_bytes=1 (elem_bytes is then the query's)."""
     lens = [int(v) for v in context_lens]
-    kv = sum(lens) * num_kv_heads * head_size * 2 * elem_bytes
+    kv = sum(lens) * num_kv_heads * head_size * 2 * (kv_elem_bytes or elem_bytes)
     qo = 2 * len(lens) * num_heads * head_size * elem_bytes
     ids = 4 * sum((L + block_size - 1) // block_size for L in lens)
     return kv + qo + ids + 4 * len(lens)

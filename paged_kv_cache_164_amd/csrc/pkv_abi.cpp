@@ -42,6 +42,12 @@ struct Resolved {
   int group;
   int block_size;
   bool use_mfma;
+  bool kv8;
+};
+
+// Scales of an 8-bit (FP8 E4M3) cache; null for 16/32-bit caches.
+struct Kv8 {
+  float k_scale, v_scale;
 };
 
 // Prefix groups of the shared-prefix decode (null for the plain decode).
@@ -68,7 +74,7 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len,
                    int32_t dtype, int32_t partition_size, void* workspace, size_t workspace_bytes,
-                   Resolved* r, const Groups* groups = nullptr) {
+                   Resolved* r, const Groups* groups = nullptr, const Kv8* kv8 = nullptr) {
   if (elem_bytes(dtype) == 0) return fail(PKV_ERR_INVALID_ARG, "dtype must be PKV_F32, PKV_F16 or PKV_BF16");
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
       max_num_blocks_per_seq < 0)
@@ -80,8 +86,14 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   if (head_size != 64 && head_size != 128) return fail(PKV_ERR_UNSUPPORTED, "head_size must be 64 or 128");
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return fail(PKV_ERR_UNSUPPORTED, "block_size must be 8, 16 or 32");
-  // 16-bit caches run on the matrix-core kernel (any group size up to 16), fp32 on the VALU one.
+  // 16-bit caches run on the matrix-core kernel (any group size up to 16), fp32 on the VALU one;
+  // 8-bit caches on their matrix-core kernel, with fp16 / bf16 queries.
   const bool shared = groups != nullptr;
+  if (kv8 && dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "an 8-bit cache needs PKV_F16 or PKV_BF16 queries");
+  if (kv8 && !(std::isfinite(kv8->k_scale) && kv8->k_scale > 0.f && std::isfinite(kv8->v_scale) &&
+               kv8->v_scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
   const bool use_mfma = dtype != PKV_F32 && pkv::gqa_supported(dtype, head_size, block_size, group);
   if (shared && !use_mfma)
     return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs PKV_F16 or PKV_BF16 and a group size <= 16");
@@ -135,7 +147,8 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
     a.part_l = reinterpret_cast<float*>(ws + w.l_off);
     a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
   }
-  a.scale_log2 = scale * pkv::kLog2e;
+  a.scale_log2 = scale * pkv::kLog2e * (kv8 ? kv8->k_scale : 1.f);
+  a.v_scale = kv8 ? kv8->v_scale : 1.f;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -148,12 +161,14 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   r->group = group;
   r->block_size = block_size;
   r->use_mfma = use_mfma;
+  r->kv8 = kv8 != nullptr;
   return PKV_OK;
 }
 
 int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
   if (r.args.num_seqs == 0) return PKV_OK;
-  hipError_t e = r.use_mfma
+  hipError_t e = r.kv8 ? pkv::launch_decode_fp8(r.args, dtype, head_size, block_size, r.group, s)
+      : r.use_mfma
       ? pkv::launch_decode_gqa(r.args, dtype, head_size, block_size, r.group, s)
       : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "attention kernel launch");
@@ -216,6 +231,26 @@ int pkv_paged_attention_decode_shared(
     int rc = resolve_decode(PKV_DECODE_ARGS, &r, &groups);
     if (rc != PKV_OK) return rc;
     if (num_seqs == 0) return PKV_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = launch_phase1(r, dtype, head_size, block_size, s);
+    if (rc != PKV_OK) return rc;
+    return launch_phase2(r, dtype, head_size, s);
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_paged_attention_decode_fp8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Resolved r;
+    const Kv8 kv8{k_scale, v_scale};
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r, nullptr, &kv8);
+    if (rc != PKV_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = launch_phase1(r, dtype, head_size, block_size, s);
     if (rc != PKV_OK) return rc;
@@ -295,6 +330,36 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
                                                  num_blocks, key_stride, value_stride, eb,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : hip_fail(e, "reshape_and_cache launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                              int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                              int32_t dtype, float k_scale, float v_scale, void* stream) {
+  try {
+    if (dtype != PKV_F16 && dtype != PKV_BF16)
+      return fail(PKV_ERR_INVALID_ARG, "key and value must be PKV_F16 or PKV_BF16");
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || block_size <= 0 || num_blocks < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (head_size % 16 != 0) return fail(PKV_ERR_INVALID_ARG, "head_size must be a multiple of x = 16");
+    if (key_stride < (int64_t)num_kv_heads * head_size || value_stride < (int64_t)num_kv_heads * head_size)
+      return fail(PKV_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_size");
+    if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+      return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "key_cache must be 16-byte aligned");
+    hipError_t e = pkv::launch_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping,
+                                                     num_tokens, num_kv_heads, head_size, block_size,
+                                                     num_blocks, key_stride, value_stride, dtype,
+                                                     k_scale, v_scale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "reshape_and_cache_fp8 launch");
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }

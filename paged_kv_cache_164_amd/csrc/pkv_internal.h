@@ -54,7 +54,8 @@ struct DecodeArgs {
   float* part_m;    // [num_seqs, num_heads, slots] running max (log2 units)
   float* part_l;    // [num_seqs, num_heads, slots] sum of exp2(s - m)
   float* part_acc;  // [num_seqs, num_heads, slots, head_size] unnormalised output
-  float scale_log2;  // scale * log2(e): logits are kept in base-2 units
+  float scale_log2;  // scale * log2(e) (* key scale for an 8-bit cache): base-2 logit units
+  float v_scale;     // 8-bit cache: value scale, applied to the output (1 otherwise)
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -104,12 +105,21 @@ bool gqa_supported(int dtype, int head_size, int block_size, int group);
 hipError_t launch_decode_gqa(const DecodeArgs& a, int dtype, int head_size, int block_size,
                              int group, hipStream_t stream);
 hipError_t launch_reduce(const DecodeArgs& a, int dtype, int head_size, hipStream_t stream);
+// 8-bit (FP8 E4M3) caches, fp16 / bf16 queries (dtype 1 / 2); shapes as for launch_decode_gqa.
+hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                             int group, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                     void* value_cache, const int64_t* slot_mapping, int num_tokens,
                                     int num_kv_heads, int head_size, int block_size,
                                     int64_t num_blocks, int64_t key_stride, int64_t value_stride,
                                     int elem_bytes, hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                        void* value_cache, const int64_t* slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_size,
+                                        int block_size, int64_t num_blocks, int64_t key_stride,
+                                        int64_t value_stride, int dtype, float k_scale,
+                                        float v_scale, hipStream_t stream);
 hipError_t launch_copy_blocks(const uint64_t* key_ptrs, const uint64_t* value_ptrs, int num_layers,
                               const int64_t* mapping, int num_pairs, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream);

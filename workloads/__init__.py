@@ -137,6 +137,9 @@ class DecodeCase:
     scale: float
     used_blocks: np.ndarray     # physical ids in use, in assignment order
     free_blocks: np.ndarray     # physical ids not referenced by any table
+    kv_dtype: Optional[str] = None  # 'e4m3': caches hold uint8 FP8 codes (new K/V stay 16-bit)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -253,6 +256,28 @@ def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optio
     return DecodeCase(cfg, q, key_cache, value_cache, torch.from_numpy(tables),
                       torch.from_numpy(lens.astype(np.int32)), new_k, new_v,
                       torch.from_numpy(slot), scale, used.astype(np.int64), free.astype(np.int64))
+
+
+def to_e4m3_codes(t: torch.Tensor, scale: float) -> torch.Tensor:
+    """uint8 FP8 E4M3 codes of t / scale, rounded by torch's float8_e4m3fn cast after clamping
+    to the format's range (NaN stays NaN)."""
+    y = t.to(torch.float32) / torch.tensor(scale, dtype=torch.float32)
+    y = torch.where(torch.isnan(y), y, y.clamp(-448.0, 448.0))
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def with_fp8_cache(case: DecodeCase, k_scale: float = 0.0137, v_scale: float = 0.0211) -> DecodeCase:
+    """The same step with an 8-bit cache: every stored key / value (NaN in unused slots) as its
+    E4M3 code with the given per-cache scales.  Queries and the step's new tokens keep the
+    model's 16-bit type."""
+    NB, H, Dx, bs, x = case.key_cache.shape
+    D = Dx * x
+    # the 16-bit key layout [.., D/8, bs, 8] as [.., D/16, bs, 16] (x = 16 / sizeof(code) = 16)
+    k = case.key_cache.permute(0, 1, 3, 2, 4).reshape(NB, H, bs, D // 16, 16).permute(0, 1, 3, 2, 4)
+    return dataclasses.replace(case, key_cache=to_e4m3_codes(k.contiguous(), k_scale),
+                               value_cache=to_e4m3_codes(case.value_cache, v_scale),
+                               kv_dtype="e4m3", k_scale=float(np.float32(k_scale)),
+                               v_scale=float(np.float32(v_scale)))
 
 
 def random_free_slots(case: DecodeCase, n: int, stream_seed: int = 0) -> np.ndarray:
