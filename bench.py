@@ -208,6 +208,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
+                    help="fp8: the same workload over an 8-bit (FP8 E4M3) KV cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0)
     ap.add_argument("--derive-traffic", nargs=4, metavar="CSV")
@@ -228,13 +230,17 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_164_amd as pkv
-    from workloads import make_decode_case
+    from workloads import make_decode_case, with_fp8_cache
 
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
     P = args.partition
     stream = torch.cuda.current_stream()
     beam = args.workload == "c5"
+    kv8 = args.kv == "fp8"
+    if kv8 and (beam or args.workload == "c1"):
+        print("--kv fp8 applies to the 16-bit workloads c2, c3, c4", file=sys.stderr)
+        return 2
     if beam:
         t, lens_np, unique_tokens = beam_setup(dev)
         q, kc, vc, bt, cl = t["q"], t["kc"], t["vc"], t["bt"], t["cl"]
@@ -243,6 +249,8 @@ def main() -> int:
         case = None
     else:
         case = make_decode_case(args.workload)
+        if kv8:
+            case = with_fp8_cache(case)
         q = case.query.to(dev)
         kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
         bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
@@ -259,17 +267,24 @@ def main() -> int:
     def step(ev=None):
         if beam:
             pkv.copy_blocks([kc], [vc], t["mapping"], stream=stream)
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
+        if kv8:
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
+                                      stream=stream)
+        else:
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        if beam:
+        if kv8:
+            pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
+                                           case.v_scale, lmax, P, ws, stream=stream)
+        elif beam:
             pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
                                               P, ws, stream=stream)
         else:
             pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        if not beam:
+        if not beam and not kv8:
             pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=stream)
 
     for _ in range(args.warmup):
@@ -287,14 +302,15 @@ def main() -> int:
     k_avg = float(np.mean(k_ms))
 
     lens = lens_np if beam else case.context_lens.numpy()
-    dec_bytes = pkv.decode_bytes(lens, Hq, Hkv, D, bs, eb)
+    kvb = 1 if kv8 else eb
+    dec_bytes = pkv.decode_bytes(lens, Hq, Hkv, D, bs, eb, kvb)
     logical_dec_bytes = dec_bytes
     if beam:
         # HBM holds each shared prompt block once and the shared-prefix kernel reads it once:
         # the algorithmic bytes count the unique KV tokens (per-sequence counts are given beside)
-        dec_bytes -= (int(lens.sum()) - unique_tokens) * Hkv * D * 2 * eb
+        dec_bytes -= (int(lens.sum()) - unique_tokens) * Hkv * D * 2 * kvb
     n_new = int((slots >= 0).sum().item())
-    write_bytes = 2 * 2 * n_new * Hkv * D * eb + 8 * B
+    write_bytes = 2 * n_new * Hkv * D * (eb + kvb) + 8 * B  # new K/V read, codes written
     if beam:  # copy-on-write: each pair reads and writes one key block and one value block
         write_bytes += 2 * 2 * t["n_pairs"] * t["block_bytes"] + 16 * t["n_pairs"]
     step_bytes = dec_bytes + write_bytes
@@ -314,9 +330,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[q.dtype],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
+        "config": {"workload": f"{args.workload}{'-fp8' if kv8 else ''}: {WORKLOADS[args.workload]}"
+                               + ("; KV cache as FP8 E4M3 codes with per-cache scales" if kv8 else ""),
+                   "num_seqs": B,
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
-                   "partition_size": P or ("auto: 2048" if eb == 2 and bs >= 16 else "auto: 1024"),
+                   "partition_size": P or ("auto: 2048" if eb == 2 and (bs >= 16 or kv8) else "auto: 1024"),
                    "kv_tokens": int(lens.sum()), "max_context_len": lmax,
                    "step_bytes": step_bytes},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -325,17 +343,20 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": ("shared-prefix decode: plan + partition kernel + split-K reduce" if beam
+                                else "8-bit cache decode: plan + partition kernel + split-K reduce" if kv8
                                 else "phase 1: work-list kernel + partition kernel"),
                      "kernel_ms": round(k_avg, 5), "kernel_ms_p10_p90":
                          [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
                      "algorithmic_bytes_per_launch": dec_bytes},
     }
+    if kv8:
+        rec["config"]["kv_dtype"] = "fp8_e4m3"
     if beam:
         # per-sequence (logical) bytes: every sequence's attention over all of its tokens
         rec["config"]["unique_kv_tokens"] = unique_tokens
         rec["logical_decode_bytes"] = logical_dec_bytes
         rec["logical_decode_GBs"] = round(logical_dec_bytes / (k_avg / 1e3) / 1e9, 2)
-    if not args.no_cpu_baseline and not beam:
+    if not args.no_cpu_baseline and not beam and not kv8:
         rec["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(rec), flush=True)
     return 0

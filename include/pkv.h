@@ -93,7 +93,7 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *   max_context_len  host upper bound of context_lens (sizes the grid)
  *   partition_size   0 = auto: 2048 for PKV_F16/PKV_BF16 with block_size >= 16,
  *                else 1024; otherwise a multiple of block_size in
- *                [block_size, 2048], at most 128 blocks for PKV_F16/PKV_BF16;
+ *                [block_size, 4096], at most 128 blocks for PKV_F16/PKV_BF16;
  *                at most 8192 partitions per sequence
  *   workspace    device scratch of at least
  *                pkv_paged_attention_workspace_size(...) bytes, 256-byte
@@ -207,7 +207,9 @@ int pkv_paged_attention_decode_shared(void* out, const void* query, const void* 
  *   k_scale, v_scale  host floats, finite and > 0
  * All other arguments, the partitioning, the workspace
  * (pkv_paged_attention_workspace_size) and the error codes as for
- * pkv_paged_attention_decode; group sizes 1..16.
+ * pkv_paged_attention_decode, except the partition size: auto is 2048 for
+ * every block size, and a partition may span up to 256 blocks.  Group sizes
+ * 1..16.
  */
 int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,

@@ -82,11 +82,14 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   const int P = a.partition_size;
   const int Hkv = a.num_kv_heads;
   const int lane = threadIdx.x & 63;
+  // The item's block ids (at most 256) go to four lane registers.
   const int32_t* bt = a.block_tables + (int64_t)b0 * a.max_blocks + tok0 / BS;
   const int row_left = a.max_blocks - tok0 / BS;
   const int nmax = min(P / BS, row_left);
   const int ids0 = (lane < nmax) ? bt[lane] : 0;
   const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
+  const int ids2 = (128 + lane < nmax) ? bt[128 + lane] : 0;
+  const int ids3 = (192 + lane < nmax) ? bt[192 + lane] : 0;
   const int h0 = kh * G;
   if (tok0 >= tok_end) {  // the sole item of an empty context
     for (int i = lane; i < G * D; i += 64)
@@ -119,8 +122,10 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
   auto block_of = [&](int j) -> int64_t {
-    j = min(j, 127);  // a lookahead past the last block is never used for a load
-    return (j < 64) ? __builtin_amdgcn_readlane(ids0, j) : __builtin_amdgcn_readlane(ids1, j - 64);
+    j = min(j, 255);  // a lookahead past the last block is never used for a load
+    const int r = j & 63;
+    return (j < 128) ? ((j < 64) ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r))
+                     : ((j < 192) ? __builtin_amdgcn_readlane(ids2, r) : __builtin_amdgcn_readlane(ids3, r));
   };
   // this lane's tokens within a tile: key rows of the two row groups, and 8 value tokens
   const int ktok0 = 8 * (col / 4) + (col % 4), ktok1 = ktok0 + 4;

@@ -101,9 +101,12 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
     return fail(PKV_ERR_UNSUPPORTED, "unsupported group size num_heads/num_kv_heads");
   if (partition_size < 0 || partition_size > pkv::kMaxPartition ||
       (partition_size > 0 && (partition_size < block_size || partition_size % block_size != 0)))
-    return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 2048]");
-  const int P = partition_size > 0 ? partition_size : pkv::auto_partition(use_mfma, block_size);
-  if (use_mfma && P > pkv::kMaxItemBlocks * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 4096]");
+  const int P = partition_size > 0 ? partition_size
+                                   : pkv::auto_partition(use_mfma, kv8 != nullptr, block_size);
+  if (kv8 && P > pkv::kMaxItemBlocks8 * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size may span at most 256 blocks (8-bit cache)");
+  if (use_mfma && !kv8 && P > pkv::kMaxItemBlocks * block_size)
     return fail(PKV_ERR_INVALID_ARG, "partition_size may span at most 128 blocks");
   const size_t lds = use_mfma ? 0 : pkv::valu_lds_bytes(group, head_size, P);
   if (lds > pkv::kMaxDynamicLds)

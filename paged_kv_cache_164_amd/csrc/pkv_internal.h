@@ -7,18 +7,22 @@
 
 namespace pkv {
 
-constexpr int kMaxPartition = 2048;       // partition_size limit (and 128 blocks per item)
-constexpr int kMaxItemBlocks = 128;       // block ids one item holds in lane registers
+constexpr int kMaxPartition = 4096;       // partition_size limit
+constexpr int kMaxItemBlocks = 128;       // block ids an item holds in lane registers (16-bit)
+constexpr int kMaxItemBlocks8 = 256;      // ... in the 8-bit cache kernel
 constexpr int kMaxPartitions = 8192;      // per sequence (bounds the workspace and the grid)
 constexpr int kTailChunks = 2;            // a remainder is cut into at most this many chunks
 constexpr int kThreads = 256;  // VALU workgroup: 4 wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;  // logits are kept in base-2 units
 
-// partition_size 0 ("auto"): 2048 tokens when an item's block ids fit the lane registers
-// (block_size >= 16) and the matrix-core kernel runs, else 1024.
-inline int auto_partition(bool mfma, int block_size) {
-  return (mfma && block_size * kMaxItemBlocks >= 2048) ? 2048 : 1024;
+// partition_size 0 ("auto"): 2048 tokens on the matrix cores when an item's block ids fit its
+// lane registers (block_size >= 16 for a 16-bit cache, >= 8 for an 8-bit one), else 1024.
+// (4096-token items of an 8-bit cache carry the same bytes as 2048 of a 16-bit one; they are
+// faster for a few very long contexts but slower for many mixed ones, so auto stays at 2048.)
+inline int auto_partition(bool mfma, bool kv8, int block_size) {
+  const int max_blocks = kv8 ? kMaxItemBlocks8 : kMaxItemBlocks;
+  return (mfma && block_size * max_blocks >= 2048) ? 2048 : 1024;
 }
 // Remainders (the tokens after a range's last whole partition) are cut into chunks of at most
 // ceil(P / 2) rounded up to whole blocks, so the last items of a call are short.

@@ -48,7 +48,7 @@ def test_workspace_size():
     for L, P in [(512, 512), (0, 0), (1025, 512), (2049, 0), (131072, 2048), (1, 16)]:
         assert pkv.paged_attention_workspace_size(4, 8, 64, L, P) == expect(4, 8, 64, L, P), (L, P)
     assert pkv.paged_attention_workspace_size(0, 8, 64, 100, 0) == 0
-    assert pkv.paged_attention_workspace_size(4, 8, 64, 100, 4096) == 0   # partition too large
+    assert pkv.paged_attention_workspace_size(4, 8, 64, 100, 8192) == 0   # partition too large
     assert pkv.paged_attention_workspace_size(4, 8, 64, 100, -1) == 0
 
 
@@ -91,8 +91,9 @@ def _decode(lib, **over):
     (dict(num_heads=12), -1),            # not a multiple of num_kv_heads
     (dict(dtype=7), -1),
     (dict(partition_size=24), -1),       # not a multiple of block_size
-    (dict(partition_size=4096), -1),     # above 2048
+    (dict(partition_size=8192), -1),     # above 4096
     (dict(dtype=1, block_size=8, partition_size=2048), -1),   # more than 128 blocks per item
+    (dict(dtype=1, block_size=16, partition_size=4096), -1),  # more than 128 blocks per item
     (dict(scale=float("nan")), -1),
     (dict(query=None), -3),
     (dict(max_context_len=4096), -4),    # needs a workspace

@@ -82,10 +82,11 @@ def test_fp8_step_c3_small():
 @pytest.mark.parametrize("dtype,D,bs,heads,P", [
     ("bf16", 128, 16, (32, 8), 0), ("f16", 128, 16, (8, 8), 0), ("bf16", 64, 8, (8, 4), 64),
     ("f16", 128, 32, (16, 2), 256), ("bf16", 128, 16, (16, 1), 16), ("f16", 64, 32, (12, 4), 2048),
-    ("bf16", 128, 8, (40, 8), 1024),
+    ("bf16", 128, 8, (40, 8), 1024), ("bf16", 128, 16, (32, 8), 4096), ("f16", 128, 32, (8, 2), 0),
 ])
 def test_fp8_decode_shapes(dtype, D, bs, heads, P):
-    lens = [0, 1, 31, 32, 33, 63, 64, 65, 300, 511, 512, 513, 1500, 2047, 2048, 2049, 2600]
+    lens = [0, 1, 31, 32, 33, 63, 64, 65, 300, 511, 512, 513, 1500, 2047, 2048, 2049, 2600,
+            4095, 4096, 4097, 6200]
     case = with_fp8_cache(make_decode_case("c3", lens=lens, dtype=dtype, head_size=D,
                                            block_size=bs, num_heads=heads[0],
                                            num_kv_heads=heads[1]))
