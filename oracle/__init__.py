@@ -22,6 +22,10 @@ What it computes, and from where:
   of nano-vLLM's KV-cache write (cybasar.com nano-vLLM article, section
   5.2.3) in the block layout of the "Vllm" page's "CacheEngine" section, and
   CacheEngine's copy_blocks / swap_blocks.
+* ``block_manager.OracleBlockManager`` -- the host bookkeeping that feeds
+  those operations (the BlockSpaceManager of the AIGC interview book, section
+  23, and the "Vllm" page's scheduler): admission with a watermark, fork,
+  append with copy-on-write, free, swap planning.
 
 Parity pins (tests/test_oracle_*.py) tie every function to something other
 than itself: a library SDPA on dense inputs, closed forms, invariants, and the

@@ -1,6 +1,7 @@
 """pkv: paged KV-cache decode attention and cache maintenance on MI355X (gfx950).
 
-A thin ctypes binding over ``libpkv.so`` (C ABI declared in ``include/pkv.h``).
+A thin ctypes binding over ``libpkv.so`` (C ABI declared in ``include/pkv.h``
+and, for the host block manager, ``include/pkv_block_manager.h``).
 Every operation runs in the library's HIP kernels; this module only checks
 tensor shapes, dtypes and devices and marshals pointers, sizes and the
 current HIP stream.  There is no fallback: if the library is missing or the
@@ -25,3 +26,4 @@ from ._binding import (  # noqa: F401
     swap_blocks,
     decode_bytes,
 )
+from .block_manager import BlockManager  # noqa: F401

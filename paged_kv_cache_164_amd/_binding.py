@@ -19,7 +19,8 @@ PKV_SWAP_IN, PKV_SWAP_OUT = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # PKV_LIBRARY may name another build of the same library (e.g. one compiled with other tuning knobs).
 _LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpkv.so")
-_HEADER = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
+_INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
+_HEADERS = [os.path.join(_INCLUDE, h) for h in ("pkv.h", "pkv_block_manager.h")]
 _lib: Optional[ctypes.CDLL] = None
 
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
@@ -45,15 +46,35 @@ _SIGNATURES = {
     "pkv_copy_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p]),
     "pkv_swap_blocks": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
     "pkv_last_error": (ctypes.c_char_p, []),
+    # host block manager (include/pkv_block_manager.h); the manager is an opaque pointer
+    "pkv_bm_create": (_c_p, [_c_int, _c_int, _c_int, _c_f]),
+    "pkv_bm_destroy": (None, [_c_p]),
+    "pkv_bm_can_allocate": (_c_int, [_c_p, _c_int]),
+    "pkv_bm_allocate": (_c_int, [_c_p, _c_i64, _c_int]),
+    "pkv_bm_fork": (_c_int, [_c_p, _c_i64, _c_i64]),
+    "pkv_bm_can_append": (_c_int, [_c_p, _c_int]),
+    "pkv_bm_append": (_c_int, [_c_p, _c_i64, _c_p, _c_p, _c_p]),
+    "pkv_bm_free": (_c_int, [_c_p, _c_i64]),
+    "pkv_bm_swap_out": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_p]),
+    "pkv_bm_swap_in": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_p]),
+    "pkv_bm_block_table": (_c_int, [_c_p, _c_i64, _c_p, _c_int, _c_p]),
+    "pkv_bm_seq_len": (_c_i64, [_c_p, _c_i64]),
+    "pkv_bm_seq_device": (_c_int, [_c_p, _c_i64]),
+    "pkv_bm_num_free": (_c_int, [_c_p, _c_int]),
+    "pkv_bm_ref_count": (_c_int, [_c_p, _c_int, _c_int]),
 }
 
 
 def _header_symbols() -> List[str]:
-    text = open(_HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pkv_\w+)\s*\(", text, re.M)))
+    """Every function the public headers declare."""
+    names = set()
+    for h in _HEADERS:
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pkv_\w+)\s*\(", open(h).read(), re.M))
+    return sorted(names)
 
 
-EXPORTED_SYMBOLS = _header_symbols() if os.path.exists(_HEADER) else sorted(_SIGNATURES)
+EXPORTED_SYMBOLS = (_header_symbols() if all(os.path.exists(h) for h in _HEADERS)
+                    else sorted(_SIGNATURES))
 
 
 class PKVError(RuntimeError):

@@ -187,6 +187,10 @@ int launch_phase2(const Resolved& r, int dtype, int head_size, hipStream_t s) {
 
 }  // namespace
 
+namespace pkv {
+int record_error(int code, const char* msg) { return fail(code, msg); }
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }

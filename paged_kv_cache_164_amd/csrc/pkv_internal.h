@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace pkv {
 
 constexpr int kMaxPartition = 4096;       // partition_size limit
@@ -124,6 +126,10 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int block_size, int64_t num_blocks, int64_t key_stride,
                                         int64_t value_stride, int dtype, float k_scale,
                                         float v_scale, hipStream_t stream);
+// Records msg as the calling thread's pkv_last_error() and returns code (host code).
+int record_error(int code, const char* msg);
+inline int record_error(int code, const std::string& msg) { return record_error(code, msg.c_str()); }
+
 hipError_t launch_copy_blocks(const uint64_t* key_ptrs, const uint64_t* value_ptrs, int num_layers,
                               const int64_t* mapping, int num_pairs, int64_t block_bytes,
                               int64_t num_blocks, hipStream_t stream);

@@ -1,6 +1,7 @@
 """The C-ABI library loads, exports every entry point of include/pkv.h, and rejects bad
 arguments on the host before touching the GPU (CPU only: no kernel is launched)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -20,10 +21,11 @@ def _lib():
 
 def test_exports_every_header_symbol():
     lib = _lib()
-    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
-    declared = set(re.findall(r"\b(pkv_\w+)\s*\(", text))
+    declared = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        declared |= set(re.findall(r"\b(pkv_\w+)\s*\(", open(h).read()))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 11
+    assert len(declared) == 26
     for name in declared:
         assert hasattr(lib, name), name
 

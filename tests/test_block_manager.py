@@ -1,0 +1,325 @@
+"""Host block manager: the oracle model pinned to the pages, the C++ manager (through the
+C ABI) against the oracle op by op, and the manager's error behaviour.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.block_manager import CPU, GPU, LATER, NEVER, OK, BlockError, OracleBlockManager
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cow_worked_example.json")
+
+
+def _lib_manager(*args, **kw):
+    from paged_kv_cache_164_amd import BlockManager
+    return BlockManager(*args, **kw)
+
+
+def _both(*args, **kw):
+    return [OracleBlockManager(*args, **kw), _lib_manager(*args, **kw)]
+
+
+# ---------------------------------------------------------------------------
+# pins of the oracle model
+# ---------------------------------------------------------------------------
+
+def _run_worked_example(bm):
+    g = json.load(open(GOLDEN))
+    A, B, C = 1, 2, 3
+    bm.allocate(A, g["prompt_tokens"])
+    bm.fork(A, B)
+    bm.fork(A, C)
+    names = {"A": A, "B": B, "C": C}
+    for n, t in g["initial_tables"].items():
+        assert bm.block_table(names[n]) == t
+    for blk, r in g["initial_ref_count"].items():
+        assert bm.ref_count(int(blk)) == r
+    assert bm.num_free(GPU) == len(g["free_list"])
+    copies = []
+    for step, n in enumerate("ABC"):
+        slot, cow = bm.append(names[n])
+        assert slot == g["expected"]["new_token_slots"][n]
+        if cow is not None:
+            copies.append(list(cow))
+        for blk, r in g["expected"]["ref_count_after_each_write"][step].items():
+            assert bm.ref_count(int(blk)) == r
+    assert copies == g["expected"]["copies"]
+    for n, t in g["expected"]["tables"].items():
+        assert bm.block_table(names[n]) == t
+
+
+def test_oracle_worked_example():
+    """The copy-on-write example of the mlqm.cn explainer, 'PagedAttention' (tests/golden)."""
+    _run_worked_example(OracleBlockManager(16, 4))
+
+
+def test_oracle_watermark_closed_form():
+    # 100 blocks of 16, watermark 0.05 -> 5 blocks kept free
+    bm = OracleBlockManager(16, 100, 0, 0.05)
+    assert bm.can_allocate(95 * 16) == OK        # 100 - 95 = 5 >= 5
+    assert bm.can_allocate(95 * 16 + 1) == NEVER  # needs 96 blocks: 4 < 5 even when empty
+    bm.allocate(0, 50 * 16)
+    assert bm.can_allocate(45 * 16) == OK         # 50 - 45 = 5
+    assert bm.can_allocate(45 * 16 + 1) == LATER  # 46 blocks: 4 left now, fits when empty
+    assert bm.can_allocate(0) == OK
+
+
+class _Memory:
+    """Token-level content of both pools: physical slots hold token values.  Replays the
+    cache operations the manager plans (writes at slots, copy-on-write block copies, swap
+    pairs) and checks that every live sequence reads back its own logical tokens."""
+
+    def __init__(self, bs, ngpu, ncpu):
+        self.bs = bs
+        self.mem = {GPU: np.full(ngpu * bs, -1, np.int64), CPU: np.full(ncpu * bs, -1, np.int64)}
+        self.logical = {}
+        self.next_token = 0
+
+    def fresh(self, n):
+        t = list(range(self.next_token, self.next_token + n))
+        self.next_token += n
+        return t
+
+    def write(self, dev, slot, tok):
+        self.mem[dev][slot] = tok
+
+    def copy_block(self, src_dev, src, dst_dev, dst):
+        bs = self.bs
+        self.mem[dst_dev][dst * bs:(dst + 1) * bs] = self.mem[src_dev][src * bs:(src + 1) * bs]
+
+    def check(self, bm):
+        for sid, toks in self.logical.items():
+            table, dev = bm.block_table(sid), bm.seq_device(sid)
+            assert bm.seq_len(sid) == len(toks)
+            got = [int(self.mem[dev][table[p // self.bs] * self.bs + p % self.bs])
+                   for p in range(len(toks))]
+            assert got == toks, f"sequence {sid} reads back wrong tokens"
+
+
+def _refcount_invariant(bm, ngpu, ncpu):
+    """Each block's count is the number of live tables (on its pool) that hold it; the free
+    count is the number of blocks at 0; a block a sequence writes into is never shared."""
+    counts = {GPU: np.zeros(ngpu, np.int64), CPU: np.zeros(ncpu, np.int64)}
+    for sid in list(bm.seqs):
+        for b in bm.block_table(sid):
+            counts[bm.seq_device(sid)][b] += 1
+    for dev, n in ((GPU, ngpu), (CPU, ncpu)):
+        assert [bm.ref_count(b, dev) for b in range(n)] == counts[dev].tolist()
+        assert bm.num_free(dev) == int((counts[dev] == 0).sum())
+
+
+def _random_session(bm, mem, g, ngpu, ncpu, n_ops, shadow=None):
+    """Random allocate / fork / append / free / swap traffic.  With `shadow` (the C++
+    manager) every call is made on both and results compared exactly."""
+    next_id = 0
+    log = []
+    for _ in range(n_ops):
+        live = sorted(bm.seqs)
+        on_gpu = [s for s in live if bm.seq_device(s) == GPU]
+        on_cpu = [s for s in live if bm.seq_device(s) == CPU]
+        op = g.choice(["alloc", "fork", "append", "append", "append", "free", "out", "in"])
+        args = ()
+        if op == "alloc":
+            args = (next_id, int(g.integers(0, 3 * mem.bs + 1)))
+            next_id += 1
+        elif op == "fork" and live:
+            args = (int(g.choice(live)), next_id)
+            next_id += 1
+        elif op in ("append", "free") and (on_gpu if op == "append" else live):
+            args = (int(g.choice(on_gpu if op == "append" else live)),)
+        elif op in ("out", "in") and (on_gpu if op == "out" else on_cpu):
+            pool = on_gpu if op == "out" else on_cpu
+            k = int(g.integers(1, len(pool) + 1))
+            args = ([int(s) for s in g.choice(pool, size=k, replace=False)],)
+        else:
+            continue
+        name = {"alloc": "allocate", "out": "swap_out", "in": "swap_in"}.get(op, op)
+        try:
+            res, err = getattr(bm, name)(*args), None
+        except BlockError as e:
+            res, err = None, e
+        if shadow is not None:
+            from paged_kv_cache_164_amd import PKVError
+            try:
+                res2, err2 = getattr(shadow, name)(*args), None
+            except PKVError as e:
+                res2, err2 = None, e
+            assert (err is None) == (err2 is None), (name, args, err, err2)
+            assert res == res2, (name, args, res, res2)
+        log.append((name, args, err is None))
+        if err is not None:
+            continue
+        if name == "allocate":
+            sid, n = args
+            mem.logical[sid] = mem.fresh(n)
+            t = bm.block_table(sid)
+            for p, tok in enumerate(mem.logical[sid]):
+                mem.write(GPU, t[p // mem.bs] * mem.bs + p % mem.bs, tok)
+        elif name == "fork":
+            mem.logical[args[1]] = list(mem.logical[args[0]])
+        elif name == "append":
+            slot, cow = res
+            if cow is not None:
+                mem.copy_block(GPU, cow[0], GPU, cow[1])
+            tok = mem.fresh(1)[0]
+            mem.write(GPU, slot, tok)
+            mem.logical[args[0]].append(tok)
+        elif name == "free":
+            del mem.logical[args[0]]
+        else:
+            src, dst = (GPU, CPU) if name == "swap_out" else (CPU, GPU)
+            for a, b in res:
+                mem.copy_block(src, a, dst, b)
+        mem.check(bm)
+        _refcount_invariant(bm, ngpu, ncpu)
+        if shadow is not None:
+            for sid in bm.seqs:
+                assert shadow.block_table(sid) == bm.block_table(sid)
+                assert shadow.seq_len(sid) == bm.seq_len(sid)
+                assert shadow.seq_device(sid) == bm.seq_device(sid)
+            for dev, n in ((GPU, ngpu), (CPU, ncpu)):
+                assert shadow.num_free(dev) == bm.num_free(dev)
+    return log
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_oracle_random_sessions_read_back(seed):
+    """Brute force on small pools: after every planned write, copy and swap, each live
+    sequence reads back exactly its own tokens, and the reference counts stay consistent."""
+    g = np.random.default_rng(seed)
+    bs, ngpu, ncpu = int(g.choice([1, 2, 4, 16])), int(g.integers(4, 24)), int(g.integers(0, 24))
+    log = _random_session(OracleBlockManager(bs, ngpu, ncpu), _Memory(bs, ngpu, ncpu), g, ngpu,
+                          ncpu, 400)
+    done = {n for n, _, ok in log if ok}
+    assert {"allocate", "fork", "append"} <= done
+
+
+def test_oracle_planted_mistake_is_caught():
+    """A manager that forgets copy-on-write (writes into the shared block) fails the
+    read-back check: the check can see the mistake it exists for."""
+
+    class NoCow(OracleBlockManager):
+        def append(self, sid):
+            s = self.seqs[sid]
+            t = s["len"]
+            if t // self.bs == len(s["table"]):
+                s["table"].append(self._take(GPU))
+            s["len"] = t + 1
+            return s["table"][t // self.bs] * self.bs + t % self.bs, None
+
+    bm, mem = NoCow(4, 8), _Memory(4, 8, 0)
+    bm.allocate(0, 3)
+    mem.logical[0] = mem.fresh(3)
+    for p, tok in enumerate(mem.logical[0]):
+        mem.write(GPU, bm.block_table(0)[0] * 4 + p, tok)
+    bm.fork(0, 1)
+    mem.logical[1] = list(mem.logical[0])
+    for sid in (0, 1):
+        slot, _ = bm.append(sid)
+        tok = mem.fresh(1)[0]
+        mem.write(GPU, slot, tok)
+        mem.logical[sid].append(tok)
+    with pytest.raises(AssertionError):
+        mem.check(bm)
+
+
+# ---------------------------------------------------------------------------
+# the C++ manager through the C ABI
+# ---------------------------------------------------------------------------
+
+def test_library_worked_example():
+    _run_worked_example(_lib_manager(16, 4))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_library_matches_oracle(seed):
+    """Every call on the C++ manager returns what the oracle returns (slots, copy-on-write
+    pairs, swap pairs, refusals), and tables, lengths, devices and free counts agree."""
+    g = np.random.default_rng(100 + seed)
+    bs, ngpu, ncpu = int(g.choice([1, 3, 8, 16])), int(g.integers(2, 40)), int(g.integers(0, 40))
+    _random_session(OracleBlockManager(bs, ngpu, ncpu), _Memory(bs, ngpu, ncpu), g, ngpu, ncpu,
+                    600, shadow=_lib_manager(bs, ngpu, ncpu))
+
+
+@pytest.mark.parametrize("wm", [0.0, 0.01, 0.1, 0.5])
+def test_library_admission_matches_oracle(wm):
+    o, m = _both(16, 64, 0, wm)
+    for sid, n in enumerate([100, 300, 0, 17, 500, 16, 1]):
+        for t in (0, 1, 15, 16, 17, 200, 1000, 1024, 1025):
+            assert m.can_allocate(t) == o.can_allocate(t), (wm, t)
+        if o.can_allocate(n) == OK:
+            o.allocate(sid, n)
+            m.allocate(sid, n)
+    for s in range(70):
+        assert m.can_append(s) == o.can_append(s)
+
+
+def _snapshot(m, ids, ngpu, ncpu):
+    return ([(m.block_table(s), m.seq_len(s), m.seq_device(s)) for s in ids],
+            [m.ref_count(b, GPU) for b in range(ngpu)], [m.ref_count(b, CPU) for b in range(ncpu)])
+
+
+def test_library_errors_change_nothing():
+    from paged_kv_cache_164_amd import PKVError
+    m = _lib_manager(4, 6, 3)
+    m.allocate(1, 8)   # blocks 0, 1
+    m.fork(1, 2)
+    m.allocate(3, 9)   # blocks 2, 3, 4
+    ids = [1, 2, 3]
+    before = _snapshot(m, ids, 6, 3)
+    bad = [
+        lambda: m.allocate(1, 4),        # id in use
+        lambda: m.allocate(9, 8),        # 2 blocks, 1 free
+        lambda: m.fork(7, 8),            # unknown parent
+        lambda: m.fork(1, 3),            # child exists
+        lambda: m.append(42),            # unknown
+        lambda: m.free(42),
+        lambda: m.swap_out([1]),         # blocks shared with sequence 2
+    ]
+    for f in bad:
+        with pytest.raises(PKVError):
+            f()
+        assert _snapshot(m, ids, 6, 3) == before
+    with pytest.raises(PKVError):
+        m.swap_in([1])                   # not on the CPU
+    with pytest.raises(PKVError):
+        m.swap_out([1, 2, 3])            # 5 distinct blocks, 3 CPU blocks
+    with pytest.raises(PKVError):
+        m.swap_out([3, 3])               # listed twice
+    assert _snapshot(m, ids, 6, 3) == before
+    # appends: 1 free block; sequence 1's block 1 is full, so the token opens a new block
+    slot, cow = m.append(1)
+    assert (slot, cow) == (5 * 4 + 0, None)
+    with pytest.raises(PKVError):
+        m.append(2)                      # needs a block, none free
+    # sequence 3 (9 tokens) writes in place into its own last block 4: no block needed
+    assert m.append(3) == (4 * 4 + 1, None)
+    assert m.num_free(GPU) == 0
+
+
+def test_library_append_in_place_and_swapped_out():
+    from paged_kv_cache_164_amd import PKVError
+    m = _lib_manager(4, 4, 4)
+    m.allocate(0, 5)                     # blocks 0, 1; token 5 goes in place into block 1
+    assert m.append(0) == (1 * 4 + 1, None)
+    pairs = m.swap_out([0])
+    assert pairs == [(0, 0), (1, 1)] and m.seq_device(0) == CPU
+    with pytest.raises(PKVError):
+        m.append(0)
+    m.allocate(1, 12)                    # GPU blocks 0, 1, 2: one left, sequence 0 needs 2
+    with pytest.raises(PKVError):
+        m.swap_in([0])
+    assert m.seq_device(0) == CPU and m.block_table(0) == [0, 1]
+    m.free(1)
+    assert m.swap_in([0]) == [(0, 0), (1, 1)]
+    assert m.seq_device(0) == GPU and m.num_free(CPU) == 4 and m.seq_len(0) == 6
+    assert m.append(0) == (1 * 4 + 2, None)
+
+
+def test_library_create_errors():
+    from paged_kv_cache_164_amd import PKVError
+    for args in [(0, 4, 0, 0.0), (16, -1, 0, 0.0), (16, 4, -2, 0.0), (16, 4, 0, 1.0),
+                 (16, 4, 0, -0.1), (16, 4, 0, float("nan"))]:
+        with pytest.raises(PKVError):
+            _lib_manager(*args)
