@@ -22,6 +22,13 @@ What it computes, and from where:
   of nano-vLLM's KV-cache write (cybasar.com nano-vLLM article, section
   5.2.3) in the block layout of the "Vllm" page's "CacheEngine" section, and
   CacheEngine's copy_blocks / swap_blocks.
+* ``prefill.chunked_prefill`` -- multi-query paged attention: the flattened
+  query rows of several requests (``query_start_loc``), each request's chunk
+  at the end of its context, causal attention per row (the tiemojia.cn
+  run-flow article, section 3.5, attention metadata; the AIGC interview
+  book's note on chunked prefill).
+* ``fp8`` -- the OCP FP8 E4M3 codec of the 8-bit KV cache, from the format's
+  definition.
 * ``block_manager.OracleBlockManager`` -- the host bookkeeping that feeds
   those operations (the BlockSpaceManager of the AIGC interview book, section
   23, and the "Vllm" page's scheduler): admission with a watermark, fork,

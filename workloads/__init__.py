@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -451,3 +451,104 @@ def make_prefix_case(group_sizes: Sequence[int], prefix_lens: Sequence[int],
     return PrefixCase(cfg, q, key_cache, value_cache, tables, np.asarray(lens, dtype=np.int32),
                       starts, np.asarray(prefix_lens, dtype=np.int32),
                       float(np.float32(1.0 / math.sqrt(D))))
+
+
+# ---------------------------------------------------------------------------
+# Multi-query steps: chunked prefill and mixed batches (query_start_loc)
+# ---------------------------------------------------------------------------
+
+S_PF_LENS, S_PF_Q, S_PF_NEWKV = 20, 21, 22
+
+PREFILL_CFG = DecodeConfig("c6", "chunked prefill bf16", 16, 32, 8, 128, 16, "bf16",
+                           ("uniform", 0, 7168), ("plus", 64), seed=1006)
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    """One multi-query step: request b has ``query_lens[b]`` new tokens (its chunk) at the end
+    of a context of ``context_lens[b]`` tokens.  The caches hold every earlier token; the
+    chunk's own slots are still unwritten (NaN when poisoned): the step scatters ``new_key`` /
+    ``new_value`` [T, Hkv, D] into ``slot_mapping`` [T] and then attends."""
+    cfg: DecodeConfig
+    query: torch.Tensor            # [T, Hq, D], the requests' rows one after another
+    key_cache: torch.Tensor        # [NB, Hkv, D/x, bs, x]
+    value_cache: torch.Tensor      # [NB, Hkv, D, bs]
+    block_tables: np.ndarray       # int32 [B, max_blocks]
+    context_lens: np.ndarray       # int32 [B]
+    query_start_loc: np.ndarray    # int32 [B + 1]
+    new_key: torch.Tensor          # [T, Hkv, D]
+    new_value: torch.Tensor        # [T, Hkv, D]
+    slot_mapping: np.ndarray       # int64 [T]
+    scale: float
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start_loc)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if len(self.context_lens) else 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if len(self.context_lens) else 0
+
+
+def draw_prefill_requests(cfg: DecodeConfig = PREFILL_CFG, chunk: int = 1024):
+    """The chunked-prefill workload: cfg.num_seqs requests, each a ``chunk``-token piece of a
+    prompt whose earlier pieces (U[lo, hi] tokens) are already cached."""
+    _, lo, hi = cfg.lens
+    prefix = rng(cfg.seed, S_PF_LENS).integers(lo, hi + 1, size=cfg.num_seqs)
+    return [(int(p), chunk) for p in prefix]
+
+
+def make_prefill_case(requests: Sequence[Tuple[int, int]], *, cfg: DecodeConfig = PREFILL_CFG,
+                      poison: bool = True, **overrides) -> PrefillCase:
+    """``requests`` = [(cached tokens, new query tokens)] per request; a decode token is
+    (L - 1, 1).  ``overrides`` replace configuration fields (heads, head size, block size,
+    dtype, seed)."""
+    if overrides:
+        cfg = dataclasses.replace(cfg, **overrides)
+    bs, Hq, Hkv, D, x = cfg.block_size, cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.x
+    pre = np.array([p for p, _ in requests], dtype=np.int64)
+    nq = np.array([n for _, n in requests], dtype=np.int64)
+    lens = pre + nq
+    B = len(requests)
+    nblk = (lens + bs - 1) // bs
+    n_used = int(nblk.sum())
+    NB = _pool_size(cfg, n_used)
+    perm = rng(cfg.seed, S_PERM).permutation(NB)
+    used = perm[:n_used]
+    max_blocks = max(int(nblk.max()) if B else 1, 1)
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        tables[b, :nblk[b]] = used[off:off + nblk[b]]
+        off += nblk[b]
+    tdt = DTYPES[cfg.dtype]
+    fill = float("nan") if poison else 0.0
+    key_cache = torch.full((NB, Hkv, D // x, bs, x), fill, dtype=tdt)
+    value_cache = torch.full((NB, Hkv, D, bs), fill, dtype=tdt)
+    fill_pool(key_cache, value_cache, used, cfg)
+    qsl = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    T = int(qsl[-1])
+    slots = np.empty(T, dtype=np.int64)
+    for b in range(B):
+        for i, p in enumerate(range(int(pre[b]), int(lens[b]))):
+            slots[qsl[b] + i] = int(tables[b, p // bs]) * bs + p % bs
+        if poison and nq[b] > 0:
+            # the chunk's slots (and the tail of its last block) are not yet written
+            first = int(pre[b])
+            for j in range(first // bs, int(nblk[b])):
+                poison_slots(key_cache, value_cache, int(tables[b, j]),
+                             first % bs if j == first // bs else 0)
+    q = _normal_to((T, Hq, D), rng(cfg.seed, S_PF_Q), cfg.dtype)
+    gn = rng(cfg.seed, S_PF_NEWKV)
+    new_k = _normal_to((T, Hkv, D), gn, cfg.dtype)
+    new_v = _normal_to((T, Hkv, D), gn, cfg.dtype)
+    return PrefillCase(cfg, q, key_cache, value_cache, tables, lens.astype(np.int32), qsl,
+                       new_k, new_v, slots, float(np.float32(1.0 / math.sqrt(D))))
