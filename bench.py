@@ -47,7 +47,10 @@ WORKLOADS = {
     "c4": "long-context split-K: batch 8, 64 q / 8 KV heads, head 128, block 32, bf16, 131072 tokens",
     "c5": "shared-prefix beam search: 32 prompts x 4 beams, 40 heads, head 128, block 16, fp16, "
           "2048-token shared prompts + U[1, 512] own tokens; copy-on-write + shared-prefix decode",
+    "c6": "chunked prefill (multi-query paged attention): 16 requests x 1024 new tokens after "
+          "U[0, 7168] cached ones, 32 q / 8 KV heads, head 128, block 16, bf16",
 }
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 KERNEL_SOURCES = ["attention_valu.hip", "attention_gqa.hip", "work_plan.hip", "pkv_device.h",
                   "pkv_internal.h"]
 
@@ -201,6 +204,125 @@ def beam_setup(dev):
     return t, lens, unique
 
 
+def prefill_cpu_baseline(case, budget_s: float = 12.0):
+    """The fp64 oracle (unchanged) on the first rows of the chunked-prefill workload, row by
+    row until the time budget is spent; throughput in TFLOP/s of useful attention flops."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import cache_ops as OC
+    from oracle import prefill as OP
+    from workloads import storage_bits
+
+    kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+    OC.reshape_and_cache(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
+                         case.slot_mapping)
+    qb = storage_bits(case.query)
+    Hq, D = case.query.shape[1], case.query.shape[2]
+    qsl, lens = case.query_start_loc, case.context_lens
+    n0, L0 = int(qsl[1] - qsl[0]), int(lens[0])
+    done, t0 = 0, time.perf_counter()
+    while done < n0 and (time.perf_counter() - t0) < budget_s:
+        rows = list(range(done, min(done + 8, n0)))
+        OP.chunked_prefill(qb, kb, vb, case.cfg.dtype, case.block_tables, lens, qsl, case.scale,
+                           [(r, h) for r in rows for h in range(Hq)])
+        done = rows[-1] + 1
+    dt = time.perf_counter() - t0
+    # rows 0..done-1 of request 0 sit at positions L0 - n0 .. and see L0 - n0 + 1 .. keys
+    pairs = sum(L0 - n0 + 1 + i for i in range(done))
+    flops = 4 * D * Hq * pairs
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done} of {case.num_tokens} query rows (request 0, all {Hq} heads), "
+                      f"{dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def run_prefill(args) -> int:
+    """Chunked-prefill step: reshape_and_cache of every new token, then multi-query attention."""
+    import torch
+
+    import paged_kv_cache_164_amd as pkv
+    from oracle.prefill import attention_flops
+    from workloads import draw_prefill_requests, make_prefill_case
+
+    t_gen = time.perf_counter()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    P = args.partition
+    case = make_prefill_case(draw_prefill_requests(), poison=False)
+    q = case.query.to(dev)
+    kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    qsl = torch.from_numpy(case.query_start_loc).to(dev)
+    nk, nv = case.new_key.to(dev), case.new_value.to(dev)
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    print(f"# generated {args.workload} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    out = torch.empty_like(q)
+    T, Hq, D = q.shape
+    Hkv, bs = kc.shape[1], kc.shape[3]
+    B, lmax = len(case.context_lens), case.max_context_len
+    need = pkv.paged_attention_prefill_workspace_size(B, T, Hq, Hkv, D, lmax, P)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
+                                    stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    k_ms = [a.elapsed_time(b) for a, b in events]
+    k_avg = float(np.mean(k_ms))
+    flops = attention_flops(case.context_lens, case.query_start_loc, Hq, D)
+    dt = {torch.float16: "f16", torch.bfloat16: "bf16"}[q.dtype]
+    peak = MFMA_PEAK_TFLOPS[dt]
+    tflops = flops / (ms_step / 1e3) / 1e12
+    k_tflops = flops / (k_avg / 1e3) / 1e12
+    rec = {
+        "metric": "multi-query paged attention achieved TFLOP/s (useful causal flops), 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
+                   "num_tokens": T, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
+                   "block_size": bs, "partition_size": P or "auto: 8192",
+                   "kv_tokens": int(case.context_lens.sum()), "max_context_len": lmax,
+                   "attention_flops": flops},
+        "query_tokens_per_s": round(T / (ms_step / 1e3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(k_tflops / peak, 4), "traffic": None,
+                     "kernel": "multi-query attention: plan + attention kernel",
+                     "kernel_ms": round(k_avg, 5), "kernel_ms_p10_p90":
+                         [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
+                     "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefill_cpu_baseline(case)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +348,12 @@ def main() -> int:
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
         return 0
+
+    if args.workload == "c6":
+        if args.kv != "native":
+            print("--kv fp8 applies to the decode workloads c2, c3, c4", file=sys.stderr)
+            return 2
+        return run_prefill(args)
 
     import torch
 

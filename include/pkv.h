@@ -221,6 +221,50 @@ int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-query paged attention: chunked prefill and mixed prefill / decode
+ * batches.  The query rows of num_seqs requests are flattened; request b owns
+ * rows [query_start_loc[b], query_start_loc[b + 1]) (the attention metadata of
+ * the tiemojia.cn vLLM run-flow article, section 3.5).  Its n rows are the
+ * last n positions of its context of L = context_lens[b] tokens (the chunk
+ * chunked prefill adds, the AIGC interview book's scheduler note; a decode
+ * token is n = 1), so row i (0-based) sits at position p = L - n + i and
+ *   out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t
+ * over the request's own keys and values (block table row b, GQA head map
+ * h / (num_heads / num_kv_heads), layouts as for the decode).  The chunk's
+ * own keys and values must already be in the cache (pkv_reshape_and_cache).
+ *   query, out        device [num_tokens, num_heads, head_size], PKV_F16 or
+ *                     PKV_BF16 (`dtype`); fp32 accumulation, weights rounded
+ *                     once to dtype, output rounded to nearest even
+ *   query_start_loc   device int32 [num_seqs + 1], 0 = first, last = num_tokens
+ *   context_lens      device int32 [num_seqs], each <= max_context_len
+ *   block_tables      device int32 [num_seqs, max_num_blocks_per_seq],
+ *                     max_num_blocks_per_seq * block_size >= max_context_len
+ *   scale             finite and > 0
+ *   partition_size    0 (auto: 8192) or a multiple of 32 in [32, 8192]: the
+ *                     keys of a query tile are cut at multiples of it and the
+ *                     pieces merged by a split-K reduce
+ *   workspace         device, 256-byte aligned, at least
+ *                     pkv_paged_attention_prefill_workspace_size(...) bytes
+ * head_size 64 or 128, block_size 8, 16 or 32, group size 1..16.  A request
+ * whose metadata is inconsistent on the device (decreasing offsets, rows past
+ * num_tokens, n > L, L > max_context_len) is skipped: its rows are left as
+ * they were.  Rows of an n = 0 request do not exist.  Errors as for the
+ * decode; PKV_ERR_UNSUPPORTED for PKV_F32.
+ */
+size_t pkv_paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                                  int32_t num_heads, int32_t num_kv_heads,
+                                                  int32_t head_size, int32_t max_context_len,
+                                                  int32_t partition_size);
+int pkv_paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                float scale, int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                int32_t block_size, int32_t max_num_blocks_per_seq,
+                                int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Scatter new tokens' keys and values into their cache slots (the KV-cache
  * write of the cybasar.com nano-vLLM article, section 5.2.3, in the block
  * layout above):

@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_shared,
     paged_attention_decode_fp8,
+    paged_attention_prefill,
+    paged_attention_prefill_workspace_size,
     reshape_and_cache_fp8,
     paged_attention_partitions,
     paged_attention_reduce,

@@ -39,6 +39,9 @@ _SIGNATURES = {
                                           + _DECODE_ARGTYPES[6:]),
     "pkv_paged_attention_decode_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                        + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
+    "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
+                                    + [_c_p, _c_sz, _c_p]),
     "pkv_reshape_and_cache_fp8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
                                            _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
     "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
@@ -192,6 +195,55 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
         raise PKVError("group_starts must be int32 [num_groups + 1], prefix_lens int32 [num_groups]")
     args = args[:6] + (group_starts.data_ptr(), prefix_lens.data_ptr(), ng) + args[6:]
     _check(library().pkv_paged_attention_decode_shared(*args), "pkv_paged_attention_decode_shared")
+    return out
+
+
+def paged_attention_prefill_workspace_size(num_seqs: int, num_tokens: int, num_heads: int,
+                                           num_kv_heads: int, head_size: int, max_context_len: int,
+                                           partition_size: int = 0) -> int:
+    return int(library().pkv_paged_attention_prefill_workspace_size(
+        num_seqs, num_tokens, num_heads, num_kv_heads, head_size, max_context_len, partition_size))
+
+
+def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
+                            query_start_loc, scale, max_context_len, partition_size=0,
+                            workspace=None, stream=None):
+    """Multi-query (chunked prefill / mixed batch) attention: query rows
+    [query_start_loc[b], query_start_loc[b+1]) of request b are the last positions of its
+    context_lens[b]-token context and attend causally over its paged keys and values."""
+    _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc)
+    T, Hq, D = query.shape
+    NB, Hkv, Dx, bs, x = key_cache.shape
+    B = context_lens.numel()
+    if not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
+        raise PKVError("query, caches and out must share one dtype")
+    dt = _dtype_code(query)
+    if x * key_cache.element_size() != 16 or Dx * x != D:
+        raise PKVError(f"key_cache must be [num_blocks, Hkv, D/x, bs, x] with x = 16/sizeof ({tuple(key_cache.shape)})")
+    if tuple(value_cache.shape) != (NB, Hkv, D, bs):
+        raise PKVError(f"value_cache must be [num_blocks, Hkv, D, bs], got {tuple(value_cache.shape)}")
+    if tuple(out.shape) != (T, Hq, D):
+        raise PKVError("out must have the query's shape")
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start_loc.dtype != torch.int32):
+        raise PKVError("block_tables, context_lens and query_start_loc must be int32")
+    if (block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.dim() != 1
+            or tuple(query_start_loc.shape) != (B + 1,)):
+        raise PKVError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs], "
+                       "query_start_loc [num_seqs + 1]")
+    for t in (out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc):
+        if not t.is_contiguous():
+            raise PKVError("all tensors must be contiguous")
+    need = paged_attention_prefill_workspace_size(B, T, Hq, Hkv, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().pkv_paged_attention_prefill(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(), float(scale),
+        B, T, Hq, Hkv, D, bs, block_tables.shape[1], int(max_context_len), dt, int(partition_size),
+        ws_ptr, ws_bytes, _stream(stream)), "pkv_paged_attention_prefill")
     return out
 
 

@@ -1,0 +1,414 @@
+// Multi-query paged attention: chunked prefill and mixed prefill / decode batches.
+//
+// The query rows of all requests are flattened; request b owns rows
+// [query_start_loc[b], query_start_loc[b + 1]) (the attention metadata of the tiemojia.cn
+// vLLM run-flow article, section 3.5).  Its n rows are the last n positions of its context of
+// L tokens (the chunk that chunked prefill adds to a partly prefilled prompt, the AIGC
+// interview book's scheduler note; a decode token is n = 1), and the row at position p attends
+// causally to cache positions 0..p.
+//
+// Work decomposition.  A workgroup takes one work item = (request, query tile, key range) and
+// one KV head.  Its 256 matrix columns are (query token, query head) pairs: q_tile = 256 / G
+// consecutive query tokens times the G query heads that share the KV head.  The key range of a
+// tile is cut at multiples of the partition size P, so every piece starts at or before the
+// tile's first query position and each column sees at least one key of every piece.  Pieces
+// of one tile are merged by the split-K reduce of the decode path (each query row plays the
+// part of a sequence there).
+//
+// Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
+// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS, double-buffered, and
+// every wave reads them from there: the stage is fetched once for all 256 columns.
+//   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
+//           rows, 16 columns per product);
+//   values: LDS rows of 32 tokens (80-byte stride, conflict-free), stored in the order
+//           (4q..4q+3, 16+4q..16+4q+3) for q = 0..3, so that a lane's 16-byte read is the A
+//           operand of O^T += V^T P^T with 32 keys per product and the lane's own softmax
+//           weights (two 16x16 logit tiles) are its B operand without any data movement.
+// Online softmax per column in base 2 with a lazy maximum: the running maximum is only moved
+// (and the accumulators rescaled) when a stage's maximum exceeds it by more than 2^8, so most
+// stages skip the rescale; weights are rounded once to the element type, and the row sums
+// come out of the matrix cores (a product with a ones row) from the same rounded weights.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLazyRescale = 8.f;  // log2 units: weights stay below 2^8 between rescales
+
+__device__ __forceinline__ f32x4 mma(BF16, const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(F16, const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// Two floats to two packed elements, round to nearest even (one v_cvt_pk_* on gfx950).
+__device__ __forceinline__ uint32_t pack2(BF16, float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), bf16x2));
+}
+__device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), f16x2));
+}
+__device__ __forceinline__ uint32_t one_bits(BF16) { return 0x3f803f80u; }
+__device__ __forceinline__ uint32_t one_bits(F16) { return 0x3c003c00u; }
+
+// Zero the 16-bit elements of an 8-token value piece whose token base + e is >= limit.
+__device__ __forceinline__ uint4 mask8(uint4 v, int base, int limit) {
+  auto m = [&](int e) -> uint32_t {
+    return ((base + e < limit) ? 0x0000ffffu : 0u) | ((base + e + 1 < limit) ? 0xffff0000u : 0u);
+  };
+  return make_uint4(v.x & m(0), v.y & m(2), v.z & m(4), v.w & m(6));
+}
+
+// ---------------------------------------------------------------------------------------
+// Plan: one workgroup lists the work items.  Requests whose metadata is inconsistent
+// (negative or decreasing offsets, rows past num_tokens, a chunk longer than its context, a
+// context longer than max_context_len) get no items: their rows are left unwritten.
+// Within a request, tiles go last-first (the last tile sees the most keys).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ bool request_ok(const PrefillArgs& a, int b, int& qs, int& n, int& L) {
+  qs = a.query_start_loc[b];
+  const int qe = a.query_start_loc[b + 1];
+  n = qe - qs;
+  L = a.context_lens[b];
+  return qs >= 0 && n >= 0 && qe <= a.num_tokens && n <= L && L <= a.max_context_len;
+}
+
+__global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int QT = a.q_tile, P = a.partition_size;
+  // rows of the split-K reduce: 0 (nothing to merge) unless an item of the row's tile says
+  // otherwise; rows of skipped requests stay 0
+  if (a.slots > 1)
+    for (int r = tid; r < a.num_tokens; r += 1024) a.np_of[r] = 0;
+  int running = 0;
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
+    const int b = c0 + tid;
+    int qs = 0, n = 0, L = 0, count = 0;
+    const bool ok = b < a.num_seqs && request_ok(a, b, qs, n, L) && n > 0;
+    const int ntile = ok ? (n + QT - 1) / QT : 0;
+    for (int j = 0; j < ntile; ++j) count += (L - n + j * QT) / P + 1;
+    // exclusive scan of count over the workgroup
+    int incl = count;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wave[w] = incl;
+    __syncthreads();
+    int wave_base = 0, total = 0;
+    for (int k = 0; k < 16; ++k) {
+      const int v = s_wave[k];
+      wave_base += (k < w) ? v : 0;
+      total += v;
+    }
+    int idx = running + wave_base + incl - count;
+    for (int j = ntile - 1; j >= 0; --j) {
+      const int qpos0 = L - n + j * QT;
+      const int end = qpos0 + min(QT, n - j * QT);
+      const int np = qpos0 / P + 1;
+      for (int p = 0; p < np; ++p, ++idx)
+        if (idx < a.capacity)
+          a.items[idx] = make_uint4(uint32_t(b), uint32_t(j), uint32_t(p * P),
+                                    uint32_t(p + 1 == np ? end : (p + 1) * P));
+    }
+    running += total;
+    __syncthreads();  // s_wave is rewritten by the next chunk
+  }
+  if (tid == 0) a.queue[1] = uint32_t(min<int64_t>(running, a.capacity));
+}
+
+// ---------------------------------------------------------------------------------------
+// Attention: NW waves x CB blocks of 16 columns = 256 columns per workgroup.
+// ---------------------------------------------------------------------------------------
+template <class DT, int D, int BS, int NW, int CB>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+  static_assert(NW * CB * 16 == kPrefillColumns, "columns per workgroup");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "a 32-key stage holds whole blocks");
+  constexpr int NT = NW * 64;
+  constexpr int KC = D / 32;        // 32-dim steps of the logit product
+  constexpr int NDT = D / 16;       // 16-dim output tiles
+  constexpr int KSTAGE = D * 64;    // bytes: [D/8][32 keys][16 B]
+  constexpr int VRS = 80;           // value row stride: 64 B of data + 16 B of padding
+  constexpr int VSTAGE = D * VRS;
+  constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
+  constexpr int PPT = (KPIECES + NT - 1) / NT;
+  __shared__ __align__(16) char s_k[2][KSTAGE];
+  __shared__ __align__(16) char s_v[2][VSTAGE];
+  __shared__ int s_ids[kPrefillMaxIds];
+
+  const int Hkv = a.num_kv_heads, Hq = a.num_heads;
+  const int t = blockIdx.x;
+  if (t >= int(a.queue[1]) * Hkv) return;
+  const uint4 it = a.items[t / Hkv];
+  const int kh = t % Hkv;
+  const int b = int(it.x), j = int(it.y), k0 = int(it.z), k1 = int(it.w);
+  const int G = a.group, QT = a.q_tile, P = a.partition_size;
+  const int qs = a.query_start_loc[b];
+  const int n = a.query_start_loc[b + 1] - qs;
+  const int L = a.context_lens[b];
+  const int qpos0 = L - n + j * QT;  // position of the tile's first query
+  const int nqt = min(QT, n - j * QT);
+  const int row0 = qs + j * QT;
+  const int npieces = qpos0 / P + 1;
+  const int slot = k0 / P;
+  const int nst = (k1 - k0 + 31) / 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+
+  if (a.slots > 1 && slot == 0 && kh == 0)  // read by the reduce, which runs after this kernel
+    for (int i = tid; i < nqt; i += NT) a.np_of[row0 + i] = npieces;
+
+  // block ids of the item's keys (ids past the context's last block: 0, a valid block whose
+  // data only ever meets zero weights or zeroed values)
+  const int blk0 = k0 / BS;
+  const int n_ids = (k0 + nst * 32 + BS - 1) / BS - blk0;
+  const int nblk = (L + BS - 1) / BS;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  for (int i = tid; i < n_ids; i += NT) s_ids[i] = (blk0 + i < nblk) ? bt[blk0 + i] : 0;
+
+  // columns of this wave: c = (w CB + cb) 16 + col -> query token qi = c / G, head c % G
+  int qi_c[CB], end_c[CB];
+  uint4 qop[CB][KC];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int c = (w * CB + cb) * 16 + col;
+    const int qi = c / G;
+    const int qic = min(qi, nqt - 1);  // unused columns compute a valid row; never stored
+    qi_c[cb] = qi;
+    end_c[cb] = min(k1, qpos0 + qic + 1);
+    const int64_t qrow = (int64_t)(row0 + qic) * Hq + kh * G + (c - qi * G);
+    const uint4* qv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.query) + qrow * D * 2);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qop[cb][kc] = qv[kc * 4 + quad];
+  }
+  const int qi_first = (w * CB * 16) / G;
+  const int qi_last = min((w * CB * 16 + CB * 16 - 1) / G, nqt - 1);
+  const bool active = qi_first < nqt;                       // the wave has a real column
+  const int wave_end = min(k1, qpos0 + qi_last + 1);        // keys past it: hidden from all
+  const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
+
+  const int64_t tile_bytes = (int64_t)D * BS * 2;
+  const int64_t block_bytes = tile_bytes * Hkv;
+  const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
+  const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
+
+  uint4 kst[PPT], vst[PPT];
+  auto load_stage = [&](int s) {
+    const int t0 = k0 + 32 * s;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + i * NT;
+      if (KPIECES % NT == 0 || p < KPIECES) {
+        {  // key piece: dims 8 c8 .. +8 of token tt
+          const int c8 = p >> 5, tt = p & 31, tok = t0 + tt;
+          const int64_t id = s_ids[tok / BS - blk0];
+          kst[i] = *reinterpret_cast<const uint4*>(kbase + id * block_bytes +
+                                                   (int64_t)(c8 * BS + tok % BS) * 16);
+        }
+        {  // value piece: dim d, tokens t8 .. t8 + 7 (inside one block); zero past the range
+          const int d = p >> 2, t8 = (p & 3) * 8, tok = t0 + t8;
+          const int64_t id = s_ids[tok / BS - blk0];
+          const uint4 v = *reinterpret_cast<const uint4*>(vbase + id * block_bytes +
+                                                          (int64_t)(d * BS + tok % BS) * 2);
+          vst[i] = (tok + 8 <= k1) ? v : mask8(v, tok, k1);
+        }
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int p = tid + i * NT;
+      if (KPIECES % NT == 0 || p < KPIECES) {
+        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + (p & 31)) * 16]) = kst[i];
+        const int d = p >> 2, t8 = (p & 3) * 8;
+        const int q = (t8 & 15) >> 2, half = t8 >> 4;
+        char* row = &s_v[buf][d * VRS + half * 8];
+        *reinterpret_cast<uint2*>(row + q * 16) = make_uint2(vst[i].x, vst[i].y);
+        *reinterpret_cast<uint2*>(row + (q + 1) * 16) = make_uint2(vst[i].z, vst[i].w);
+      }
+    }
+  };
+
+  f32x4 oacc[NDT][CB], lacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    lacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) m_run[cb] = -INFINITY;
+  // A operand of the row-sum product: row 0 all ones (lanes with col == 0), other rows zero
+  const uint32_t ob = (col == 0) ? one_bits(DT()) : 0u;
+  const uint4 ones = make_uint4(ob, ob, ob, ob);
+  const float sl2 = a.scale_log2;
+
+  auto compute = [&](int s, int buf) {
+    const int t0 = k0 + 32 * s;
+    const char* sk = s_k[buf];
+    const char* sv = s_v[buf];
+    f32x4 sacc[2][CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) sacc[0][cb] = sacc[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(sk + ((kc * 4 + quad) * 32 + tt * 16 + col) * 16);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) sacc[tt][cb] = mma(DT(), ka, qop[cb][kc], sacc[tt][cb]);
+      }
+    // causal / range mask, only on stages that reach past a key some column must not see
+    const bool diag = t0 + 32 > wave_full;
+    bool need[CB];
+    float mc[CB];
+    bool any = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (diag && t0 + tt * 16 + quad * 4 + r >= end_c[cb]) sacc[tt][cb][r] = -INFINITY;
+          mx = fmaxf(mx, sacc[tt][cb][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mc[cb] = mx * sl2;  // the scale is positive: the maximum commutes with it
+      need[cb] = mc[cb] > m_run[cb] + kLazyRescale;
+      any |= need[cb];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const float m_new = need[cb] ? mc[cb] : m_run[cb];
+        const float alpha = exp2f(m_run[cb] - m_new);  // 0 at the first stage (m = -inf)
+        m_run[cb] = m_new;
+        lacc[cb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) oacc[i][cb] *= alpha;
+      }
+    }
+    uint4 pop[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      float p[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[tt][r] = exp2f(fmaf(sacc[tt][cb][r], sl2, -m_run[cb]));
+      pop[cb] = make_uint4(pack2(DT(), p[0][0], p[0][1]), pack2(DT(), p[0][2], p[0][3]),
+                           pack2(DT(), p[1][0], p[1][1]), pack2(DT(), p[1][2], p[1][3]));
+      lacc[cb] = mma(DT(), ones, pop[cb], lacc[cb]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+      const uint4 va = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), va, pop[cb], oacc[i][cb]);
+    }
+  };
+
+  __syncthreads();  // s_ids
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) load_stage(s + 1);
+    if (active && k0 + 32 * s < wave_end) compute(s, s & 1);
+    if (s + 1 < nst) store_stage((s + 1) & 1);
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column
+  // sits in row 0 of its sum product (lane col, element 0)
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const float l_tot = __shfl(lacc[cb][0], col, 64);
+    const int c = (w * CB + cb) * 16 + col;
+    if (qi_c[cb] >= nqt) continue;
+    const int64_t orow = (int64_t)(row0 + qi_c[cb]) * Hq + kh * G + (c - qi_c[cb] * G);
+    if (npieces == 1) {
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) {
+        const f32x4 o = oacc[i][cb] * inv;
+        *reinterpret_cast<uint2*>(static_cast<char*>(a.out) + (orow * D + i * 16 + quad * 4) * 2) =
+            make_uint2(pack2(DT(), o[0], o[1]), pack2(DT(), o[2], o[3]));
+      }
+    } else {
+      const int64_t sp = orow * a.slots + slot;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+        *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) = oacc[i][cb];
+      if (quad == 0) {
+        a.part_m[sp] = m_run[cb];
+        a.part_l[sp] = l_tot;
+      }
+    }
+  }
+}
+
+template <class DT, int D, int BS>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int NW = 8, CB = 2;
+  const int64_t grid = a.capacity * a.num_kv_heads;
+  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, NW, CB>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <class DT, int D>
+hipError_t by_block(const PrefillArgs& a, int bs, hipStream_t s) {
+  switch (bs) {
+    case 8: return launch_t<DT, D, 8>(a, s);
+    case 16: return launch_t<DT, D, 16>(a, s);
+    case 32: return launch_t<DT, D, 32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class DT>
+hipError_t by_head(const PrefillArgs& a, int D, int bs, hipStream_t s) {
+  switch (D) {
+    case 64: return by_block<DT, 64>(a, bs, s);
+    case 128: return by_block<DT, 128>(a, bs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prefill_supported(int dtype, int head_size, int block_size, int group) {
+  return (dtype == 1 || dtype == 2) && (head_size == 64 || head_size == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 1 && group <= 16;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, const DecodeArgs& red, int dtype, int head_size,
+                          int block_size, hipStream_t stream) {
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = (dtype == 1) ? by_head<F16>(a, head_size, block_size, stream)
+                   : by_head<BF16>(a, head_size, block_size, stream);
+  if (e != hipSuccess || a.slots <= 1) return e;
+  return launch_reduce(red, dtype, head_size, stream);
+}
+
+}  // namespace pkv

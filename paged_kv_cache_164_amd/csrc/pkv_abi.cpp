@@ -185,6 +185,28 @@ int launch_phase2(const Resolved& r, int dtype, int head_size, hipStream_t s) {
   return e == hipSuccess ? PKV_OK : hip_fail(e, "reduce kernel launch");
 }
 
+// Partition size of the multi-query path (0: auto), or -1 if invalid.
+int prefill_partition(int32_t partition_size) {
+  if (partition_size == 0) return pkv::kPrefillAutoPartition;
+  if (partition_size < 32 || partition_size > pkv::kPrefillMaxPartition || partition_size % 32 != 0)
+    return -1;
+  return partition_size;
+}
+
+// Shapes of the multi-query path that the layout depends on (0 bytes if invalid).
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t max_context_len,
+                               int32_t partition_size) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_context_len < 0 || num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16)
+    return 0;
+  const int P = prefill_partition(partition_size);
+  if (P < 0) return 0;
+  if (num_seqs == 0 || num_tokens == 0) return 0;
+  return pkv::prefill_layout(num_seqs, num_tokens, num_heads, num_kv_heads, head_size,
+                             max_context_len, P).total;
+}
+
 }  // namespace
 
 namespace pkv {
@@ -311,6 +333,100 @@ int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t n
     a.len_limit = max_context_len;
     a.slots = (int)slots;
     return launch_phase2(r, dtype, head_size, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+size_t pkv_paged_attention_prefill_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                                  int32_t num_heads, int32_t num_kv_heads,
+                                                  int32_t head_size, int32_t max_context_len,
+                                                  int32_t partition_size) {
+  return prefill_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads, head_size,
+                                 max_context_len, partition_size);
+}
+
+int pkv_paged_attention_prefill(void* out, const void* query, const void* key_cache,
+                                const void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                float scale, int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                int32_t block_size, int32_t max_num_blocks_per_seq,
+                                int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (dtype != PKV_F16 && dtype != PKV_BF16)
+      return fail(dtype == PKV_F32 ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARG,
+                  "multi-query attention runs on the matrix cores: dtype must be PKV_F16 or PKV_BF16");
+    if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        max_context_len < 0 || max_num_blocks_per_seq < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (num_heads % num_kv_heads != 0)
+      return fail(PKV_ERR_INVALID_ARG, "num_heads must be a multiple of num_kv_heads");
+    if (!(std::isfinite(scale) && scale > 0.f))
+      return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+    const int group = num_heads / num_kv_heads;
+    if (!pkv::prefill_supported(dtype, head_size, block_size, group))
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "head_size must be 64 or 128, block_size 8, 16 or 32, num_heads/num_kv_heads <= 16");
+    const int P = prefill_partition(partition_size);
+    if (P < 0)
+      return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of 32 in [32, 8192]");
+    if ((int64_t)max_num_blocks_per_seq * block_size < max_context_len)
+      return fail(PKV_ERR_INVALID_ARG, "block table rows are shorter than max_context_len");
+    if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        !query_start_loc)
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    const pkv::PrefillLayout w = pkv::prefill_layout(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                                     head_size, max_context_len, P);
+    if (w.capacity * num_kv_heads >= (int64_t(1) << 31))
+      return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    if (workspace == nullptr || workspace_bytes < w.total)
+      return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(w.total) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    pkv::PrefillArgs a{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.queue = reinterpret_cast<uint32_t*>(ws);
+    a.items = reinterpret_cast<uint4*>(ws + w.items_off);
+    a.np_of = reinterpret_cast<int32_t*>(ws + w.np_off);
+    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+    a.scale_log2 = scale * pkv::kLog2e;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_num_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.group = group;
+    a.q_tile = pkv::kPrefillColumns / group;
+    a.partition_size = P;
+    a.slots = (int)w.slots;
+    a.capacity = w.capacity;
+    // the split-K reduce of the decode path, with one "sequence" per query row
+    pkv::DecodeArgs red{};
+    red.out = out;
+    red.np_of = a.np_of;
+    red.part_m = a.part_m;
+    red.part_l = a.part_l;
+    red.part_acc = a.part_acc;
+    red.num_seqs = num_tokens;
+    red.num_heads = num_heads;
+    red.num_kv_heads = num_kv_heads;
+    red.slots = a.slots;
+    const hipError_t e = pkv::launch_prefill(a, red, dtype, head_size, block_size,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "multi-query attention launch");
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }

@@ -25,7 +25,7 @@ def test_exports_every_header_symbol():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         declared |= set(re.findall(r"\b(pkv_\w+)\s*\(", open(h).read()))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 26
+    assert len(declared) == 28
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -134,3 +134,65 @@ def test_decode_bytes_formula():
     # two sequences of 17 and 16 tokens, MHA 2 heads, D 8, bs 16, 2-byte elements
     b = pkv.decode_bytes([17, 16], 2, 2, 8, 16, 2)
     assert b == 33 * 2 * 8 * 2 * 2 + 2 * 2 * 2 * 8 * 2 + 4 * 3 + 4 * 2
+
+
+def test_prefill_workspace_size():
+    _lib()
+    a256 = lambda v: (v + 255) // 256 * 256
+
+    def expect(B, T, Hq, Hkv, D, L, P):
+        # header, work items (tiles x pieces), per-row piece counts, then partials when split
+        P = P or 8192
+        qt = 256 // (Hq // Hkv)
+        S = -(-L // P) if L > 0 else 1
+        cap = (T // qt + B) * S
+        base = 256 + a256(16 * cap) + a256(4 * T)
+        if S <= 1:
+            return base
+        n = T * Hq * S
+        return base + 2 * a256(4 * n) + a256(4 * n * D)
+
+    for args in [(4, 100, 8, 2, 64, 300, 0), (16, 16384, 32, 8, 128, 8192, 0),
+                 (3, 40, 16, 1, 128, 5000, 64), (1, 1, 4, 4, 64, 131072, 4096)]:
+        assert pkv.paged_attention_prefill_workspace_size(*args) == expect(*args), args
+    assert pkv.paged_attention_prefill_workspace_size(0, 10, 8, 8, 64, 100, 0) == 0
+    assert pkv.paged_attention_prefill_workspace_size(2, 10, 8, 8, 64, 100, 48) == 0   # not x32
+    assert pkv.paged_attention_prefill_workspace_size(2, 10, 8, 8, 64, 100, 16384) == 0
+    assert pkv.paged_attention_prefill_workspace_size(2, 10, 68, 4, 64, 100, 0) == 0   # G 17
+
+
+def _prefill(lib, **over):
+    args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
+                query_start_loc=1, scale=0.125, num_seqs=2, num_tokens=10, num_heads=8,
+                num_kv_heads=2, head_size=128, block_size=16, max_blocks=4, max_context_len=64,
+                dtype=2, partition_size=0, workspace=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.pkv_paged_attention_prefill(*args.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=0), -2),                          # fp32: matrix cores only
+    (dict(dtype=7), -1),
+    (dict(num_heads=7), -1),                      # not a multiple of num_kv_heads
+    (dict(num_heads=34), -2),                     # group size 17
+    (dict(head_size=96), -2),
+    (dict(block_size=64), -2),
+    (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(partition_size=48), -1),
+    (dict(partition_size=16384), -1),
+    (dict(max_blocks=3), -1),                     # 3 x 16 < max_context_len 64
+    (dict(query_start_loc=None), -3),
+    (dict(), -4),                                 # needs a workspace
+    (dict(num_tokens=-1), -1),
+])
+def test_prefill_argument_errors(over, code):
+    lib = _lib()
+    assert _prefill(lib, **over) == code
+    assert lib.pkv_last_error().decode() != ""
+
+
+def test_prefill_nothing_to_do():
+    lib = _lib()
+    assert _prefill(lib, num_tokens=0) == 0
+    assert _prefill(lib, num_seqs=0, num_tokens=0) == 0
