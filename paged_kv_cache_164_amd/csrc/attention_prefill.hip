@@ -70,11 +70,14 @@ __device__ __forceinline__ uint4 mask8(uint4 v, int base, int limit) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Plan: one workgroup lists the work items.  Requests whose metadata is inconsistent
-// (negative or decreasing offsets, rows past num_tokens, a chunk longer than its context, a
-// context longer than max_context_len) get no items: their rows are left unwritten.
-// Within a request, tiles go last-first (the last tile sees the most keys).
+// Plan: one workgroup lists the work items, longest first (32 length classes, the longest
+// class first; the order inside a class is arbitrary, which changes no result: every item
+// writes its own outputs or partial slot).  Requests whose metadata is inconsistent (negative
+// or decreasing offsets, rows past num_tokens, a chunk longer than its context, a context
+// longer than max_context_len) get no items: their rows are left unwritten.
 // ---------------------------------------------------------------------------------------
+constexpr int kPlanClasses = 32;
+
 __device__ __forceinline__ bool request_ok(const PrefillArgs& a, int b, int& qs, int& n, int& L) {
   qs = a.query_start_loc[b];
   const int qe = a.query_start_loc[b + 1];
@@ -83,50 +86,53 @@ __device__ __forceinline__ bool request_ok(const PrefillArgs& a, int b, int& qs,
   return qs >= 0 && n >= 0 && qe <= a.num_tokens && n <= L && L <= a.max_context_len;
 }
 
-__global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
-  __shared__ int s_wave[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// Calls f(tile j, first key, end key, piece count) for every item of request b.
+template <class F>
+__device__ __forceinline__ void for_each_item(const PrefillArgs& a, int b, F&& f) {
+  int qs, n, L;
+  if (!request_ok(a, b, qs, n, L) || n == 0) return;
   const int QT = a.q_tile, P = a.partition_size;
+  for (int j = (n + QT - 1) / QT - 1; j >= 0; --j) {
+    const int qpos0 = L - n + j * QT;
+    const int end = qpos0 + min(QT, n - j * QT);
+    const int np = qpos0 / P + 1;
+    for (int p = 0; p < np; ++p) f(j, p * P, p + 1 == np ? end : (p + 1) * P);
+  }
+}
+
+__global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
+  __shared__ int s_count[kPlanClasses];
+  const int tid = threadIdx.x;
   // rows of the split-K reduce: 0 (nothing to merge) unless an item of the row's tile says
   // otherwise; rows of skipped requests stay 0
   if (a.slots > 1)
     for (int r = tid; r < a.num_tokens; r += 1024) a.np_of[r] = 0;
-  int running = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 1024) {
-    const int b = c0 + tid;
-    int qs = 0, n = 0, L = 0, count = 0;
-    const bool ok = b < a.num_seqs && request_ok(a, b, qs, n, L) && n > 0;
-    const int ntile = ok ? (n + QT - 1) / QT : 0;
-    for (int j = 0; j < ntile; ++j) count += (L - n + j * QT) / P + 1;
-    // exclusive scan of count over the workgroup
-    int incl = count;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
+  if (tid < kPlanClasses) s_count[tid] = 0;
+  __syncthreads();
+  // an item spans at most min(P, max_context_len) + q_tile keys
+  const int span = min(a.partition_size, a.max_context_len) + a.q_tile + 1;
+  auto cls = [&](int len) {
+    return kPlanClasses - 1 - min(kPlanClasses - 1, int((int64_t)len * kPlanClasses / span));
+  };
+  for (int b = tid; b < a.num_seqs; b += 1024)
+    for_each_item(a, b, [&](int, int k0, int k1) { atomicAdd(&s_count[cls(k1 - k0)], 1); });
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int c = 0; c < kPlanClasses; ++c) {
+      const int v = s_count[c];
+      s_count[c] = run;
+      run += v;
     }
-    if (lane == 63) s_wave[w] = incl;
-    __syncthreads();
-    int wave_base = 0, total = 0;
-    for (int k = 0; k < 16; ++k) {
-      const int v = s_wave[k];
-      wave_base += (k < w) ? v : 0;
-      total += v;
-    }
-    int idx = running + wave_base + incl - count;
-    for (int j = ntile - 1; j >= 0; --j) {
-      const int qpos0 = L - n + j * QT;
-      const int end = qpos0 + min(QT, n - j * QT);
-      const int np = qpos0 / P + 1;
-      for (int p = 0; p < np; ++p, ++idx)
-        if (idx < a.capacity)
-          a.items[idx] = make_uint4(uint32_t(b), uint32_t(j), uint32_t(p * P),
-                                    uint32_t(p + 1 == np ? end : (p + 1) * P));
-    }
-    running += total;
-    __syncthreads();  // s_wave is rewritten by the next chunk
+    a.queue[1] = uint32_t(min<int64_t>(run, a.capacity));
   }
-  if (tid == 0) a.queue[1] = uint32_t(min<int64_t>(running, a.capacity));
+  __syncthreads();
+  for (int b = tid; b < a.num_seqs; b += 1024)
+    for_each_item(a, b, [&](int j, int k0, int k1) {
+      const int idx = atomicAdd(&s_count[cls(k1 - k0)], 1);
+      if (idx < a.capacity)
+        a.items[idx] = make_uint4(uint32_t(b), uint32_t(j), uint32_t(k0), uint32_t(k1));
+    });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -204,40 +210,52 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
 
-  uint4 kst[PPT], vst[PPT];
-  auto load_stage = [&](int s) {
-    const int t0 = k0 + 32 * s;
+  // Stage s's keys and values go from HBM to registers two stages ahead of their use and from
+  // registers to LDS one stage ahead.  Loads are never skipped (a stage past the end reloads
+  // the last one, from L2): a load under a branch would make every wait conservative.
+  // Per-thread constants of the copies (a stage starts at a multiple of 32 >= k0, which is
+  // itself a multiple of 32, so a thread's pieces sit at fixed offsets inside their blocks):
+  //   key piece p: dims 8 (p / 32) .. +8 of stage token p % 32
+  //   value piece p: dim p / 4, stage tokens 8 (p % 4) .. +8 (inside one block)
+  constexpr int IDS_PER_STAGE = 32 / BS;
+  int kid[PPT], vid[PPT];
+  uint32_t koff[PPT], voff[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = min(tid + i * NT, KPIECES - 1);
+    const int c8 = p >> 5, tt = p & 31, d = p >> 2, t8 = (p & 3) * 8;
+    kid[i] = tt / BS;
+    koff[i] = uint32_t(c8 * BS + tt % BS) * 16u;
+    vid[i] = t8 / BS;
+    voff[i] = uint32_t(d * BS + t8 % BS) * 2u;
+  }
+  uint4 kA[PPT], vA[PPT], kB[PPT], vB[PPT];
+  auto load_stage = [&](int s, uint4* kst, uint4* vst) {
+    const int sid = min(s, nst - 1) * IDS_PER_STAGE;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * NT;
-      if (KPIECES % NT == 0 || p < KPIECES) {
-        {  // key piece: dims 8 c8 .. +8 of token tt
-          const int c8 = p >> 5, tt = p & 31, tok = t0 + tt;
-          const int64_t id = s_ids[tok / BS - blk0];
-          kst[i] = *reinterpret_cast<const uint4*>(kbase + id * block_bytes +
-                                                   (int64_t)(c8 * BS + tok % BS) * 16);
-        }
-        {  // value piece: dim d, tokens t8 .. t8 + 7 (inside one block); zero past the range
-          const int d = p >> 2, t8 = (p & 3) * 8, tok = t0 + t8;
-          const int64_t id = s_ids[tok / BS - blk0];
-          const uint4 v = *reinterpret_cast<const uint4*>(vbase + id * block_bytes +
-                                                          (int64_t)(d * BS + tok % BS) * 2);
-          vst[i] = (tok + 8 <= k1) ? v : mask8(v, tok, k1);
-        }
+      if (KPIECES % NT == 0 || tid + i * NT < KPIECES) {
+        const uint32_t ik = uint32_t(s_ids[sid + kid[i]]), iv = uint32_t(s_ids[sid + vid[i]]);
+        kst[i] = *reinterpret_cast<const uint4*>(kbase + (uint64_t)ik * block_bytes + koff[i]);
+        vst[i] = *reinterpret_cast<const uint4*>(vbase + (uint64_t)iv * block_bytes + voff[i]);
       }
     }
   };
-  auto store_stage = [&](int buf) {
+  // Values of tokens past the item's range are zeroed here (selects, no branch): the cache
+  // past a context's end may hold anything, and a zero weight times NaN is NaN.
+  auto store_stage = [&](int buf, int s, const uint4* kst, const uint4* vst) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
       if (KPIECES % NT == 0 || p < KPIECES) {
         *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + (p & 31)) * 16]) = kst[i];
         const int d = p >> 2, t8 = (p & 3) * 8;
+        uint4 v = vst[i];
+        if (k0 + 32 * (s + 1) > k1) v = mask8(v, k0 + 32 * s + t8, k1);  // the last stage only
         const int q = (t8 & 15) >> 2, half = t8 >> 4;
         char* row = &s_v[buf][d * VRS + half * 8];
-        *reinterpret_cast<uint2*>(row + q * 16) = make_uint2(vst[i].x, vst[i].y);
-        *reinterpret_cast<uint2*>(row + (q + 1) * 16) = make_uint2(vst[i].z, vst[i].w);
+        *reinterpret_cast<uint2*>(row + q * 16) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(row + (q + 1) * 16) = make_uint2(v.z, v.w);
       }
     }
   };
@@ -279,14 +297,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     bool any = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
+      if (diag) {
+        const int lim = end_c[cb] - (t0 + quad * 4);  // keys at or past it are hidden
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tt * 16 + r >= lim) sacc[tt][cb][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (diag && t0 + tt * 16 + quad * 4 + r >= end_c[cb]) sacc[tt][cb][r] = -INFINITY;
-          mx = fmaxf(mx, sacc[tt][cb][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tt][cb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       mc[cb] = mx * sl2;  // the scale is positive: the maximum commutes with it
@@ -297,7 +320,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float m_new = need[cb] ? mc[cb] : m_run[cb];
-        const float alpha = exp2f(m_run[cb] - m_new);  // 0 at the first stage (m = -inf)
+        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 at first (m = -inf)
         m_run[cb] = m_new;
         lacc[cb] *= alpha;
 #pragma unroll
@@ -311,7 +334,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[tt][r] = exp2f(fmaf(sacc[tt][cb][r], sl2, -m_run[cb]));
+        for (int r = 0; r < 4; ++r)  // v_exp_f32: weights below 2^-126 flush to 0
+          p[tt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][cb][r], sl2, -m_run[cb]));
       pop[cb] = make_uint4(pack2(DT(), p[0][0], p[0][1]), pack2(DT(), p[0][2], p[0][3]),
                            pack2(DT(), p[1][0], p[1][1]), pack2(DT(), p[1][2], p[1][3]));
       lacc[cb] = mma(DT(), ones, pop[cb], lacc[cb]);
@@ -325,15 +349,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   };
 
   __syncthreads();  // s_ids
-  load_stage(0);
-  store_stage(0);
+  load_stage(0, kA, vA);
+  load_stage(1, kB, vB);
+  store_stage(0, 0, kA, vA);
   __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) load_stage(s + 1);
-    if (active && k0 + 32 * s < wave_end) compute(s, s & 1);
-    if (s + 1 < nst) store_stage((s + 1) & 1);
+  // Pairs of stages: the only way back to the loop head is the end of a pair, so the wait
+  // counters there know exactly which loads are still in flight.  The stores are not skipped
+  // past the end either (the buffer they fill is free, and unread after the loop).
+  int s = 0;
+  for (; s + 1 < nst; s += 2) {
+    // even stage s: LDS buffer 0; registers B hold stage s + 1, A are free
+    load_stage(s + 2, kA, vA);
+    if (active && k0 + 32 * s < wave_end) compute(s, 0);
+    store_stage(1, s + 1, kB, vB);
+    __syncthreads();
+    // odd stage s + 1: LDS buffer 1; registers A hold stage s + 2, B are free
+    load_stage(s + 3, kB, vB);
+    if (active && k0 + 32 * (s + 1) < wave_end) compute(s + 1, 1);
+    store_stage(0, s + 2, kA, vA);
     __syncthreads();
   }
+  if (s < nst && active && k0 + 32 * s < wave_end) compute(s, 0);  // an odd count: the last
   if (!active) return;
 
   // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column
