@@ -16,11 +16,12 @@
 // part of a sequence there).
 //
 // Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
-// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS, double-buffered, and
-// every wave reads them from there: the stage is fetched once for all 256 columns.
+// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (three stage buffers;
+// the loads run two stages ahead), and every wave reads them from there: the stage is fetched
+// once for all 256 columns.
 //   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
 //           rows, 16 columns per product);
-//   values: LDS rows of 32 tokens (80-byte stride, conflict-free), stored in the order
+//   values: LDS rows of 32 tokens (96-byte stride), stored in the order
 //           (4q..4q+3, 16+4q..16+4q+3) for q = 0..3, so that a lane's 16-byte read is the A
 //           operand of O^T += V^T P^T with 32 keys per product and the lane's own softmax
 //           weights (two 16x16 logit tiles) are its B operand without any data movement.
@@ -60,6 +61,15 @@ __device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
 }
 __device__ __forceinline__ uint32_t one_bits(BF16) { return 0x3f803f80u; }
 __device__ __forceinline__ uint32_t one_bits(F16) { return 0x3c003c00u; }
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA column): gfx950's lane-swap
+// instructions (VALU), not an LDS permute.
+__device__ __forceinline__ float column_max(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
 
 // Zero the 16-bit elements of an 8-token value piece whose token base + e is >= limit.
 __device__ __forceinline__ uint4 mask8(uint4 v, int base, int limit) {
@@ -146,12 +156,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int KC = D / 32;        // 32-dim steps of the logit product
   constexpr int NDT = D / 16;       // 16-dim output tiles
   constexpr int KSTAGE = D * 64;    // bytes: [D/8][32 keys][16 B]
-  constexpr int VRS = 80;           // value row stride: 64 B of data + 16 B of padding
+  constexpr int VRS = 96;           // value row stride: 64 B of data + 32 B of padding (fewest
+                                    // bank conflicts of the strides measured: 64, 80, 96)
   constexpr int VSTAGE = D * VRS;
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
-  __shared__ __align__(16) char s_k[2][KSTAGE];
-  __shared__ __align__(16) char s_v[2][VSTAGE];
+  constexpr int NBUF = 3;           // stage s (read), s + 1 (ready), s + 2 (being written)
+  __shared__ __align__(16) char s_k[NBUF][KSTAGE];
+  __shared__ __align__(16) char s_v[NBUF][VSTAGE];
   __shared__ int s_ids[kPrefillMaxIds];
 
   const int Hkv = a.num_kv_heads, Hq = a.num_heads;
@@ -202,7 +214,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int qi_first = (w * CB * 16) / G;
   const int qi_last = min((w * CB * 16 + CB * 16 - 1) / G, nqt - 1);
   const bool active = qi_first < nqt;                       // the wave has a real column
-  const int wave_end = min(k1, qpos0 + qi_last + 1);        // keys past it: hidden from all
   const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
 
   const int64_t tile_bytes = (int64_t)D * BS * 2;
@@ -275,44 +286,49 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const uint4 ones = make_uint4(ob, ob, ob, ob);
   const float sl2 = a.scale_log2;
 
-  auto compute = [&](int s, int buf) {
-    const int t0 = k0 + 32 * s;
+  // ---- the pieces of a stage's work (LDS buffer buf holds the stage)
+  // S^T = K Q^T: 2 key tiles x CB column blocks, KC products each
+  auto qk = [&](int buf, f32x4 (&S)[2][CB]) {
     const char* sk = s_k[buf];
-    const char* sv = s_v[buf];
-    f32x4 sacc[2][CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) sacc[0][cb] = sacc[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) S[0][cb] = S[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const uint4 ka = *reinterpret_cast<const uint4*>(sk + ((kc * 4 + quad) * 32 + tt * 16 + col) * 16);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) sacc[tt][cb] = mma(DT(), ka, qop[cb][kc], sacc[tt][cb]);
+        for (int cb = 0; cb < CB; ++cb) S[tt][cb] = mma(DT(), ka, qop[cb][kc], S[tt][cb]);
       }
-    // causal / range mask, only on stages that reach past a key some column must not see
-    const bool diag = t0 + 32 > wave_full;
-    bool need[CB];
-    float mc[CB];
-    bool any = false;
+  };
+  // per column: the stage's largest logit, in base-2 units (the scale is positive, so the
+  // maximum commutes with it)
+  auto stage_max = [&](const f32x4 (&S)[2][CB], float (&mc)[CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      if (diag) {
-        const int lim = end_c[cb] - (t0 + quad * 4);  // keys at or past it are hidden
+      float mx = fmaxf(fmaxf(fmaxf(S[0][cb][0], S[0][cb][1]), fmaxf(S[0][cb][2], S[0][cb][3])),
+                       fmaxf(fmaxf(S[1][cb][0], S[1][cb][1]), fmaxf(S[1][cb][2], S[1][cb][3])));
+      mc[cb] = column_max(mx) * sl2;
+    }
+  };
+  // keys a column must not see (causal, or past the item): logit -inf
+  auto mask_stage = [&](int t0, f32x4 (&S)[2][CB]) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (tt * 16 + r >= lim) sacc[tt][cb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int lim = end_c[cb] - (t0 + quad * 4);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tt][cb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mc[cb] = mx * sl2;  // the scale is positive: the maximum commutes with it
+        for (int r = 0; r < 4; ++r)
+          if (tt * 16 + r >= lim) S[tt][cb][r] = -INFINITY;
+    }
+  };
+  // lazy maximum: move it (and rescale) only when a column's stage maximum exceeds it by more
+  // than the margin; the wave takes the branch if any of its columns needs it
+  auto rescale = [&](const float (&mc)[CB]) {
+    bool need[CB], any = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
       need[cb] = mc[cb] > m_run[cb] + kLazyRescale;
       any |= need[cb];
     }
@@ -327,7 +343,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < NDT; ++i) oacc[i][cb] *= alpha;
       }
     }
-    uint4 pop[CB];
+  };
+  // weights rounded to the element type (the B operand of P.V) and their sums
+  auto weights = [&](const f32x4 (&S)[2][CB], uint4 (&pop)[CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       float p[2][4];
@@ -335,41 +353,64 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)  // v_exp_f32: weights below 2^-126 flush to 0
-          p[tt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][cb][r], sl2, -m_run[cb]));
+          p[tt][r] = __builtin_amdgcn_exp2f(fmaf(S[tt][cb][r], sl2, -m_run[cb]));
       pop[cb] = make_uint4(pack2(DT(), p[0][0], p[0][1]), pack2(DT(), p[0][2], p[0][3]),
                            pack2(DT(), p[1][0], p[1][1]), pack2(DT(), p[1][2], p[1][3]));
       lacc[cb] = mma(DT(), ones, pop[cb], lacc[cb]);
     }
+  };
+  // a stage with a key some column of the wave must not see
+  auto needs_mask = [&](int s) { return k0 + 32 * s + 32 > wave_full; };
+
+  // One stage per step.  The value operands are read first (they do not depend on the logits,
+  // so their LDS latency hides behind the logit products and the softmax).  Stages past a
+  // wave's last column are computed too: their keys are all masked (zero weights), and no
+  // branch splits the step.  The block being written in step s is the one stage s - 1 used.
+  f32x4 S[2][CB];
+  float mc[CB];
+  auto step = [&](int s) {
+    uint4 vop[NDT];
+    const char* sv = s_v[s % NBUF];
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) {
-      const uint4 va = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
+    for (int i = 0; i < NDT; ++i)
+      vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
+    qk(s % NBUF, S);
+    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
+    stage_max(S, mc);
+    rescale(mc);
+    uint4 pop[CB];
+    weights(S, pop);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), va, pop[cb], oacc[i][cb]);
-    }
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
   };
 
   __syncthreads();  // s_ids
   load_stage(0, kA, vA);
   load_stage(1, kB, vB);
   store_stage(0, 0, kA, vA);
+  store_stage(1, 1, kB, vB);
+  load_stage(2, kA, vA);
+  load_stage(3, kB, vB);
   __syncthreads();
-  // Pairs of stages: the only way back to the loop head is the end of a pair, so the wait
-  // counters there know exactly which loads are still in flight.  The stores are not skipped
-  // past the end either (the buffer they fill is free, and unread after the loop).
+
+  // Steps in pairs: the only way back to the loop head is the end of a pair, so the wait
+  // counters there know exactly which loads are in flight.  Registers A carry the even
+  // stages, B the odd ones, each loaded two steps before it is stored; stores and loads are
+  // not skipped past the end (the blocks they fill are free, and unread after the loop).
   int s = 0;
   for (; s + 1 < nst; s += 2) {
-    // even stage s: LDS buffer 0; registers B hold stage s + 1, A are free
-    load_stage(s + 2, kA, vA);
-    if (active && k0 + 32 * s < wave_end) compute(s, 0);
-    store_stage(1, s + 1, kB, vB);
+    store_stage((s + 2) % NBUF, s + 2, kA, vA);
+    load_stage(s + 4, kA, vA);
+    if (active) step(s);
     __syncthreads();
-    // odd stage s + 1: LDS buffer 1; registers A hold stage s + 2, B are free
-    load_stage(s + 3, kB, vB);
-    if (active && k0 + 32 * (s + 1) < wave_end) compute(s + 1, 1);
-    store_stage(0, s + 2, kA, vA);
+    store_stage((s + 3) % NBUF, s + 3, kB, vB);
+    load_stage(s + 5, kB, vB);
+    if (active) step(s + 1);
     __syncthreads();
   }
-  if (s < nst && active && k0 + 32 * s < wave_end) compute(s, 0);  // an odd count: the last
+  if (s < nst && active) step(s);  // an odd count: the last stage
   if (!active) return;
 
   // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column
