@@ -24,10 +24,17 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-mcode-object
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-file flags.  The multi-query kernel's maxima see no NaN (masked keys are -inf; values past
+# a range are zeroed before any product), so fmaxf need not quiet its inputs first: without
+# -fno-honor-nans every operand of a max costs an extra canonicalising v_max.
+FILE_FLAGS = {"attention_prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, out_dir: str = OUT_DIR, extra=()) -> str:
     obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + [f"-I{INCLUDE}"] + list(extra) + lang + ["-c", src, "-o", obj]
+    cmd = ([HIPCC] + COMMON + FILE_FLAGS.get(os.path.basename(src), []) + [f"-I{INCLUDE}"]
+           + list(extra) + lang + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

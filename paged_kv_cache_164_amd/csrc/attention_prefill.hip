@@ -161,7 +161,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int VSTAGE = D * VRS;
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
-  constexpr int NBUF = 3;           // stage s (read), s + 1 (ready), s + 2 (being written)
+  // stage s - 1 (values, late waves), s (read), s + 1 (ready), s + 2 (being written)
+  constexpr int NBUF = 4;
   __shared__ __align__(16) char s_k[NBUF][KSTAGE];
   __shared__ __align__(16) char s_v[NBUF][VSTAGE];
   __shared__ int s_ids[kPrefillMaxIds];
@@ -362,28 +363,53 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // a stage with a key some column of the wave must not see
   auto needs_mask = [&](int s) { return k0 + 32 * s + 32 > wave_full; };
 
-  // One stage per step.  The value operands are read first (they do not depend on the logits,
-  // so their LDS latency hides behind the logit products and the softmax).  Stages past a
-  // wave's last column are computed too: their keys are all masked (zero weights), and no
-  // branch splits the step.  The block being written in step s is the one stage s - 1 used.
+  // One stage per step.  Stages past a wave's last column are computed too: their keys are
+  // all masked (zero weights).  The block written in step s is the one stage s - 2 used.
   f32x4 S[2][CB];
   float mc[CB];
-  auto step = [&](int s) {
+  // Two schedules, so that the two waves sharing a SIMD (w and w + 4) are out of phase: early
+  // waves (w < 4) do stage s's logits, softmax and P.V in step s; late waves do stage s - 1's
+  // P.V first, then stage s's logits and softmax, keeping its weights for the next step.  A
+  // late wave's products then overlap its partner's softmax, and the reverse, though the
+  // barrier of each stage keeps the two in step.
+  const bool late = w >= NW / 2;
+  uint4 pop_prev[CB];
+  auto pv = [&](int s, const uint4 (&pop)[CB]) {
     uint4 vop[NDT];
     const char* sv = s_v[s % NBUF];
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
       vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
-    qk(s % NBUF, S);
-    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
-    stage_max(S, mc);
-    rescale(mc);
-    uint4 pop[CB];
-    weights(S, pop);
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
+  };
+  auto softmax = [&](int s, uint4 (&pop)[CB]) {
+    qk(s % NBUF, S);
+    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
+    stage_max(S, mc);
+    rescale(mc);  // before the stage's weights: o holds stages < s (late waves: P.V of s - 1 done)
+    weights(S, pop);
+  };
+  auto step = [&](int s) {
+    if (!late) {
+      // value operands first: their LDS latency hides behind the logits and the softmax
+      uint4 vop[NDT];
+      const char* sv = s_v[s % NBUF];
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+        vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
+      uint4 pop[CB];
+      softmax(s, pop);
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
+    } else {
+      if (s > 0) pv(s - 1, pop_prev);
+      softmax(s, pop_prev);
+    }
   };
 
   __syncthreads();  // s_ids
@@ -411,6 +437,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
   if (s < nst && active) step(s);  // an odd count: the last stage
+  if (active && late) pv(nst - 1, pop_prev);  // the block is intact: no store since the last step
   if (!active) return;
 
   // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column

@@ -51,6 +51,87 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// The same scatter for many tokens (a prefill chunk), 16-bit elements: one workgroup per run
+// of 16 consecutive tokens.  A thread holds one (head, dim) value element of 8 tokens
+// (loads coalesced across the threads), and 8 tokens whose slots are consecutive, 8-aligned
+// and inside one block -- the usual case for a chunk, whose tokens fill blocks in order -- land
+// as one 16-byte store of the value row instead of eight 2-byte ones.  Other runs fall back to
+// element stores; keys are 16-byte chunks either way (token index fastest across threads, so a
+// block's consecutive tokens are written as one contiguous run).
+constexpr int kRunTokens = 16;
+constexpr int kRunMinTokens = 512;  // below it, one workgroup per token spreads the work wider
+
+template <bool VEC_KEY>
+__global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int head_size,
+    int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride) {
+  constexpr int X = 8;  // elements per 16-byte key chunk
+  __shared__ int64_t s_slot[kRunTokens];
+  __shared__ int s_vec[2];
+  const int64_t i0 = (int64_t)blockIdx.x * kRunTokens;
+  const int ntok = (int)min<int64_t>(kRunTokens, num_tokens - i0);
+  const int tid = threadIdx.x;
+  if (tid < kRunTokens) {
+    int64_t sl = (tid < ntok) ? slot_mapping[i0 + tid] : -1;
+    s_slot[tid] = (sl < 0 || sl >= num_blocks * block_size) ? -1 : sl;  // skipped: -1
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const int64_t a = s_slot[8 * tid];
+    bool ok = a >= 0 && a % 8 == 0 && a % block_size + 8 <= block_size;
+    for (int k = 1; k < 8; ++k) ok = ok && s_slot[8 * tid + k] == a + k;
+    s_vec[tid] = ok;
+  }
+  __syncthreads();
+  const int D = head_size;
+  const int n = num_kv_heads * D;
+  const int64_t tile = (int64_t)D * block_size;
+  for (int t = tid; t < kRunTokens * (n / X); t += blockDim.x) {
+    const int j = t % kRunTokens, c = t / kRunTokens;
+    const int64_t sl = s_slot[j];
+    if (sl < 0) continue;
+    const int h = c / (D / X), cc = c % (D / X);
+    uint16_t* dst = key_cache + ((sl / block_size) * num_kv_heads + h) * tile +
+                    ((int64_t)cc * block_size + sl % block_size) * X;
+    const uint16_t* src = key + (i0 + j) * key_stride + (int64_t)c * X;
+    if constexpr (VEC_KEY) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    } else {
+      for (int k = 0; k < X; ++k) dst[k] = src[k];
+    }
+  }
+  // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2), so consecutive
+  // threads write consecutive 16-byte pieces: a wave's stores cover whole value rows
+  for (int t = tid; t < 2 * n; t += blockDim.x) {
+    const int e = t >> 1, half = t & 1;
+    const int h = e / D, d = e % D;
+    const int kb = 8 * half;
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const uint32_t lo = (kb + k < ntok) ? value[(i0 + kb + k) * value_stride + e] : 0u;
+      const uint32_t hi = (kb + k + 1 < ntok) ? value[(i0 + kb + k + 1) * value_stride + e] : 0u;
+      v[k / 2] = lo | (hi << 16);
+    }
+    if (s_vec[half]) {
+      const int64_t sl = s_slot[kb];
+      uint16_t* dst = value_cache + ((sl / block_size) * num_kv_heads + h) * tile +
+                      (int64_t)d * block_size + sl % block_size;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t sl = s_slot[kb + k];
+        if (sl < 0) continue;
+        value_cache[((sl / block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
+                    sl % block_size] = uint16_t(v[k / 2] >> (16 * (k & 1)));
+      }
+    }
+  }
+}
+
 // The same scatter into an 8-bit cache (FP8 E4M3, x = 16): each new element of the model's
 // 16-bit type is quantised as code = E4M3(clamp(x / scale, -448, 448)), the division rounded
 // to float32 and the conversion to nearest, ties to even (a NaN stays NaN).
@@ -148,6 +229,20 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
   const bool vec = (reinterpret_cast<uintptr_t>(key) % 16 == 0) &&
                    ((key_stride * elem_bytes) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(key_cache) % 16 == 0);
+  // many 16-bit tokens: the run kernel (its 16-byte value stores need an aligned cache)
+  if (elem_bytes == 2 && num_tokens >= kRunMinTokens &&
+      reinterpret_cast<uintptr_t>(value_cache) % 16 == 0) {
+    const dim3 rgrid((unsigned)((num_tokens + kRunTokens - 1) / kRunTokens));
+#define PKV_RUNS(V)                                                                             \
+  hipLaunchKernelGGL((reshape_and_cache_runs_kernel<V>), rgrid, dim3(256), 0, stream,           \
+                     static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),    \
+                     static_cast<uint16_t*>(key_cache), static_cast<uint16_t*>(value_cache),    \
+                     slot_mapping, num_tokens, num_kv_heads, head_size, block_size, num_blocks, \
+                     key_stride, value_stride)
+    if (vec) PKV_RUNS(true); else PKV_RUNS(false);
+#undef PKV_RUNS
+    return hipGetLastError();
+  }
   const dim3 grid(num_tokens), block(256);
 #define PKV_RC(E, V)                                                                          \
   hipLaunchKernelGGL((reshape_and_cache_kernel<E, V>), grid, block, 0, stream,                \

@@ -47,6 +47,50 @@ def test_reshape_and_cache_random_free_slots(key, dtype, bs, stride_pad):
     assert _bits_equal(kc, kb) and _bits_equal(vc, vb)
 
 
+@pytest.mark.parametrize("dtype,bs,stride_pad", [("bf16", 16, 0), ("f16", 8, 0), ("bf16", 32, 3)])
+def test_reshape_and_cache_many_tokens(dtype, bs, stride_pad):
+    """A prefill-sized batch (the many-token path): runs of consecutive slots filling blocks,
+    runs that start mid-block or cross a block boundary, a run with a hole, skipped (-1) and
+    out-of-range slots, random singles, and a ragged tail (N not a multiple of 16)."""
+    case = make_decode_case("c3", num_seqs=8, len_cap=1500, dtype=dtype, block_size=bs,
+                            pool=("plus", 160))
+    Hkv, D = case.key_cache.shape[1], case.query.shape[2]
+    NB = case.key_cache.shape[0]
+    free = [int(b) for b in case.free_blocks]
+    whole = 768 // bs                          # blocks filled in order
+    free, blocks = free[whole:], free[:whole]
+    assert len(free) >= 40
+    slots = []
+    for b in blocks:
+        slots += [b * bs + o for o in range(bs)]
+    b0, b1 = free[0], free[1]
+    slots += [b0 * bs + o for o in range(3, bs)] + [b1 * bs + o for o in range(bs)]  # mid-block start
+    run = [free[2] * bs + o for o in range(bs)]
+    run[5] = -1                                # a hole
+    slots += run
+    slots += [NB * bs + 9, -3]                 # out of range, skipped
+    g = np.random.default_rng(3)
+    singles = g.choice(np.array([b * bs + o for b in free[3:40] for o in range(bs)]), size=37, replace=False)
+    slots += [int(x) for x in singles]
+    slots = np.array(slots, dtype=np.int64)
+    N = len(slots)
+    assert N >= 512 and N % 16 != 0
+    row = Hkv * D + stride_pad
+    kbuf = draw_normal((N, row), dtype, 78, 0)
+    vbuf = draw_normal((N, row), dtype, 78, 1)
+    log(f"reshape many tokens {dtype} bs{bs} N={N} stride={row}")
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    kd = kbuf.to(DEV)[:, :Hkv * D].view(N, Hkv, D)
+    vd = vbuf.to(DEV)[:, :Hkv * D].view(N, Hkv, D)
+    pkv.reshape_and_cache(kd, vd, kc, vc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+    ref_slots = np.where(slots < NB * bs, slots, -1)
+    OC.reshape_and_cache(kb, vb, storage_bits(kbuf[:, :Hkv * D].contiguous().view(N, Hkv, D)),
+                         storage_bits(vbuf[:, :Hkv * D].contiguous().view(N, Hkv, D)), ref_slots)
+    assert _bits_equal(kc, kb) and _bits_equal(vc, vb)
+
+
 def test_reshape_then_decode_step_slots():
     """The decode step's own slots (each sequence's newest token) land where the oracle puts them."""
     case = make_decode_case("c3", num_seqs=40, len_cap=4000)
