@@ -165,7 +165,8 @@ def cpu_baseline(case, budget_s: float = 12.0):
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {done} of {len(lens)} sequences ({int(lens[:done].sum())} KV tokens, "
-                      f"all {Hq} query heads), {dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus"}
+                      f"all {Hq} query heads), {dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus, "
+                      f"{cpu_model()}"}
 
 
 def beam_setup(dev):
@@ -204,6 +205,76 @@ def beam_setup(dev):
     return t, lens, unique
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def ceilings(steps: int = 20) -> None:
+    """Reference rates on the running machine: the HBM read ceiling of the decode kernels' load
+    type (a plain streaming read of 4 GiB), copy_blocks (device copy of whole blocks) and
+    swap_blocks over the host link, both directions (pinned host memory)."""
+    import torch
+
+    import paged_kv_cache_164_amd as pkv
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))  # ms
+
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    buf.random_(0, 255)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms = timed(lambda: pkv.stream_read(buf, sink, stream=stream), steps)
+    read_gbs = buf.numel() / (ms / 1e3) / 1e9
+
+    def ten():
+        for _ in range(10):
+            pkv.stream_read(buf, sink, stream=stream)
+    read10_gbs = 10 * buf.numel() / (timed(ten, 5) / 1e3) / 1e9  # back to back: no launch gaps
+    del buf
+    # blocks of the c5 shape: 40 heads x 128 dims x 16 tokens x 2 B = 160 KiB (keys; values alike)
+    nb, pairs = 4096, 1024
+    kc = torch.empty((nb, 40, 16, 16, 8), dtype=torch.float16, device=dev).normal_()
+    vc = torch.empty((nb, 40, 128, 16), dtype=torch.float16, device=dev).normal_()
+    g = np.random.default_rng(7)
+    perm = g.permutation(nb)
+    mapping = torch.from_numpy(np.stack([perm[:pairs], perm[pairs:2 * pairs]], 1).astype(np.int64)).to(dev)
+    ptrs = pkv.copy_blocks([kc], [vc], mapping, stream=stream)
+    block_bytes = kc[0].numel() * kc.element_size()
+    ms = timed(lambda: pkv.copy_blocks([kc], [vc], mapping, stream=stream, _ptr_buffers=ptrs), steps)
+    copy_gbs = 2 * 2 * pairs * block_bytes / (ms / 1e3) / 1e9  # read + write, keys and values
+    host = torch.empty((pairs,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    m_out = np.stack([perm[:pairs], np.arange(pairs)], 1).astype(np.int64)
+    m_in = np.stack([np.arange(pairs), perm[pairs:2 * pairs]], 1).astype(np.int64)
+    ms_out = timed(lambda: pkv.swap_blocks(kc, host, m_out, stream=stream), max(steps // 4, 3))
+    ms_in = timed(lambda: pkv.swap_blocks(host, kc, m_in, stream=stream), max(steps // 4, 3))
+    print(json.dumps({
+        "ceilings": "reference rates on this GPU",
+        "stream_read_GBs": round(read_gbs, 1), "stream_read_frac_of_8TBs": round(read_gbs / HBM_PEAK_GBS, 4),
+        "stream_read_back_to_back_GBs": round(read10_gbs, 1), "stream_read_bytes": 4 << 30,
+        "copy_blocks_GBs": round(copy_gbs, 1), "copy_blocks_pairs": pairs, "block_bytes": block_bytes,
+        "swap_out_GBs": round(pairs * block_bytes / (ms_out / 1e3) / 1e9, 2),
+        "swap_in_GBs": round(pairs * block_bytes / (ms_in / 1e3) / 1e9, 2),
+        "swap_bytes": pairs * block_bytes,
+    }), flush=True)
+
+
 def prefill_cpu_baseline(case, budget_s: float = 12.0):
     """The fp64 oracle (unchanged) on the first rows of the chunked-prefill workload, row by
     row until the time budget is spent; throughput in TFLOP/s of useful attention flops."""
@@ -234,7 +305,7 @@ def prefill_cpu_baseline(case, budget_s: float = 12.0):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {done} of {case.num_tokens} query rows (request 0, all {Hq} heads), "
-                      f"{dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus"}
+                      f"{dt:.1f} s, affinity {len(os.sched_getaffinity(0))} cpus, {cpu_model()}"}
 
 
 def run_prefill(args) -> int:
@@ -336,6 +407,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mib", type=int, default=0)
     ap.add_argument("--derive-traffic", nargs=4, metavar="CSV")
     ap.add_argument("--calibration-mib", type=int, default=512)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="print reference rates (streaming read, block copy, host-link swap) instead")
     args = ap.parse_args()
     if args.derive_traffic:
         derive_traffic(args.workload, *args.derive_traffic, args.calibration_mib)
@@ -345,6 +418,9 @@ def main() -> int:
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         return 2
 
+    if args.ceilings:
+        ceilings()
+        return 0
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
         return 0

@@ -265,6 +265,15 @@ int pkv_paged_attention_prefill(void* out, const void* query, const void* key_ca
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement aid (not part of the attention path): read `bytes` of device memory at `src`
+ * with the non-temporal 16-byte loads the decode kernels use for the KV cache, as fast as the
+ * memory system allows, to measure the achievable HBM read ceiling on the running GPU.
+ * `sink` is a device word the kernel may write (practically never).  src and bytes must be
+ * multiples of 16.  Asynchronous on `stream`; errors as elsewhere.
+ */
+int pkv_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/*
  * Scatter new tokens' keys and values into their cache slots (the KV-cache
  * write of the cybasar.com nano-vLLM article, section 5.2.3, in the block
  * layout above):

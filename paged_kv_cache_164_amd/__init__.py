@@ -27,5 +27,6 @@ from ._binding import (  # noqa: F401
     copy_blocks,
     swap_blocks,
     decode_bytes,
+    stream_read,
 )
 from .block_manager import BlockManager  # noqa: F401

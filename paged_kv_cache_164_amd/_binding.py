@@ -42,6 +42,7 @@ _SIGNATURES = {
     "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
     "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
                                     + [_c_p, _c_sz, _c_p]),
+    "pkv_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_p]),
     "pkv_reshape_and_cache_fp8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
                                            _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
     "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
@@ -378,6 +379,14 @@ def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping, stream=None
                                      block_bytes, src.shape[0], dst.shape[0], direction,
                                      _stream(stream)),
            "pkv_swap_blocks")
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement aid: read all of `src` (device, 16-byte multiple) with the decode kernels'
+    streaming loads (see include/pkv.h)."""
+    _on_gpu(src, sink)
+    _check(library().pkv_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                     sink.data_ptr(), _stream(stream)), "pkv_stream_read")
 
 
 def decode_bytes(context_lens, num_heads: int, num_kv_heads: int, head_size: int, block_size: int,

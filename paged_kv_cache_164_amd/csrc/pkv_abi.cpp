@@ -432,6 +432,19 @@ int pkv_paged_attention_prefill(void* out, const void* query, const void* key_ca
   }
 }
 
+int pkv_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  try {
+    if (bytes == 0) return PKV_OK;
+    if (!src || !sink) return fail(PKV_ERR_NULL_POINTER, "null pointer");
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) || (bytes & 15u))
+      return fail(PKV_ERR_INVALID_ARG, "src and bytes must be multiples of 16");
+    const hipError_t e = pkv::launch_stream_read(src, (int64_t)bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "stream read launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
                           const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                           int32_t head_size, int32_t block_size, int64_t num_blocks,
