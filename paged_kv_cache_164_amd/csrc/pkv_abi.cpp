@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "pkv_internal.h"
+#include "pkv_probe.h"
 
 namespace {
 

@@ -5,7 +5,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <algorithm>
 #include <string>
 
 namespace pkv {
@@ -192,9 +191,6 @@ bool prefill_supported(int dtype, int head_size, int block_size, int group);
 // plan + attention kernel (+ the split-K reduce, given as `red`, when a.slots > 1)
 hipError_t launch_prefill(const PrefillArgs& a, const DecodeArgs& red, int dtype, int head_size,
                           int block_size, hipStream_t stream);
-
-// measurement aid (probe_stream.hip): non-temporal 16-byte streaming read of `bytes`
-hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
 
 // Records msg as the calling thread's pkv_last_error() and returns code (host code).
 int record_error(int code, const char* msg);

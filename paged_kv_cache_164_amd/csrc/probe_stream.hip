@@ -3,8 +3,10 @@
 // kernels use for the KV cache, sixteen loads in flight per thread; the data is
 // folded into a per-thread XOR that is stored only if it matches a value the input cannot be
 // known to avoid, so the loads cannot be dropped.
+#include <algorithm>
+
 #include "pkv_device.h"
-#include "pkv_internal.h"
+#include "pkv_probe.h"
 
 namespace pkv {
 namespace {
