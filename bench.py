@@ -205,6 +205,44 @@ def beam_setup(dev):
     return t, lens, unique
 
 
+def time_steps(step, steps: int, warmup: int, graph: bool):
+    """W warm-up steps; then the K steps of the dominant kernel's HIP events (an eager pass,
+    events recorded on the launch stream by step(ev)); then the K timed steps of the whole step,
+    between synchronisations: graph replays of one captured step when `graph`, else eager
+    steps.  Returns (ms per step, per-step event times in ms)."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    k_ms = [a.elapsed_time(b) for a, b in events]
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    return ms_step, k_ms
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -318,7 +356,6 @@ def run_prefill(args) -> int:
 
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
     P = args.partition
     case = make_prefill_case(draw_prefill_requests(), poison=False)
     q = case.query.to(dev)
@@ -337,25 +374,14 @@ def run_prefill(args) -> int:
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots)
         if ev is not None:
-            ev[0].record(stream)
-        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
-                                    stream=stream)
+            ev[0].record()
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record()
 
-    for _ in range(args.warmup):
-        step()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    k_ms = [a.elapsed_time(b) for a, b in events]
+    ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
     flops = attention_flops(case.context_lens, case.query_start_loc, Hq, D)
     dt = {torch.float16: "f16", torch.bfloat16: "bf16"}[q.dtype]
@@ -379,7 +405,7 @@ def run_prefill(args) -> int:
                    "num_tokens": T, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
                    "block_size": bs, "partition_size": P or "auto: 8192",
                    "kv_tokens": int(case.context_lens.sum()), "max_context_len": lmax,
-                   "attention_flops": flops},
+                   "attention_flops": flops, "timing": "graph replay" if args.graph else "eager"},
         "query_tokens_per_s": round(T / (ms_step / 1e3), 1),
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(k_tflops / peak, 4), "traffic": None,
@@ -404,6 +430,8 @@ def main() -> int:
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="fp8: the same workload over an 8-bit (FP8 E4M3) KV cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph instead of eager steps")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0)
     ap.add_argument("--derive-traffic", nargs=4, metavar="CSV")
     ap.add_argument("--calibration-mib", type=int, default=512)
@@ -439,7 +467,6 @@ def main() -> int:
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
     P = args.partition
-    stream = torch.cuda.current_stream()
     beam = args.workload == "c5"
     kv8 = args.kv == "fp8"
     if kv8 and (beam or args.workload == "c1"):
@@ -468,41 +495,31 @@ def main() -> int:
     need = pkv.paged_attention_workspace_size(B, Hq, D, lmax, P)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
+    ptrs = pkv.copy_blocks([kc], [vc], t["mapping"]) if beam else None
+
     def step(ev=None):
-        if beam:
-            pkv.copy_blocks([kc], [vc], t["mapping"], stream=stream)
+        if beam:  # device pointer table made once, outside any graph capture
+            pkv.copy_blocks([kc], [vc], t["mapping"], _ptr_buffers=ptrs)
         if kv8:
-            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
-                                      stream=stream)
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale)
         else:
-            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=stream)
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots)
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record()
         if kv8:
             pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
-                                           case.v_scale, lmax, P, ws, stream=stream)
+                                           case.v_scale, lmax, P, ws)
         elif beam:
             pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
-                                              P, ws, stream=stream)
+                                              P, ws)
         else:
-            pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=stream)
+            pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record()
         if not beam and not kv8:
-            pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=stream)
+            pkv.paged_attention_reduce(out, cl, lmax, ws, P)
 
-    for _ in range(args.warmup):
-        step()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = [a.elapsed_time(b) for a, b in events]
+    ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
 
     lens = lens_np if beam else case.context_lens.numpy()
@@ -540,7 +557,7 @@ def main() -> int:
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
                    "partition_size": P or ("auto: 2048" if eb == 2 and (bs >= 16 or kv8) else "auto: 1024"),
                    "kv_tokens": int(lens.sum()), "max_context_len": lmax,
-                   "step_bytes": step_bytes},
+                   "step_bytes": step_bytes, "timing": "graph replay" if args.graph else "eager"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(float(lens.sum()) / (ms_step / 1e3), 1),
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,

@@ -1,0 +1,77 @@
+"""Decode steps and multi-query calls captured in a HIP graph (torch.cuda.graph): every replay,
+with eager work and synchronisations between replays, must give the eager result bit for bit.
+The entry points record kernels only (no memset or copy nodes)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_164_amd as pkv
+from gpu_cases import DEV, log
+from workloads import make_decode_case, make_prefill_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_replays(step, out, n=3):
+    """step() launches the work into `out`; returns after comparing n graph replays to eager."""
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream before capture, as torch advises
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(n):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r} differs from the eager result"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
+def test_decode_step_graph_replays():
+    case = make_decode_case("c3", num_seqs=48, len_cap=5000)
+    log(f"graph decode: {case.num_seqs} sequences, max {case.max_context_len}")
+    q, kc, vc = case.query.to(DEV), case.key_cache.to(DEV), case.value_cache.to(DEV)
+    bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+    nk, nv, slots = case.new_key.to(DEV), case.new_value.to(DEV), case.slot_mapping.to(DEV)
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.paged_attention_workspace_size(case.num_seqs, 32, 128, case.max_context_len),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots)  # same slots, same values: idempotent
+        pkv.paged_attention_decode(out, q, kc, vc, bt, cl, case.scale, case.max_context_len, 0, ws)
+
+    _check_replays(step, out)
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_multi_query_graph_replays(P):
+    case = make_prefill_case([(300, 130), (0, 77), (1000, 1), (40, 200)], poison=False,
+                             num_heads=16, num_kv_heads=4, head_size=128, block_size=16)
+    log(f"graph multi-query: {case.num_tokens} rows, P={P}")
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    pkv.reshape_and_cache(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
+                          torch.from_numpy(case.slot_mapping).to(DEV))
+    q = case.query.to(DEV)
+    bt = torch.from_numpy(case.block_tables).to(DEV)
+    cl = torch.from_numpy(case.context_lens).to(DEV)
+    qsl = torch.from_numpy(case.query_start_loc).to(DEV)
+    out = torch.empty_like(q)
+    B = len(case.context_lens)
+    ws = torch.empty(max(pkv.paged_attention_prefill_workspace_size(
+        B, case.num_tokens, 16, 4, 128, case.max_context_len, P), 256), dtype=torch.uint8, device=DEV)
+
+    def step():
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, case.max_context_len,
+                                    P, ws)
+
+    _check_replays(step, out)
