@@ -209,7 +209,8 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
     """W warm-up steps; then the K steps of the dominant kernel's HIP events (an eager pass,
     events recorded on the launch stream by step(ev)); then the K timed steps of the whole step,
     between synchronisations: graph replays of one captured step when `graph`, else eager
-    steps.  Returns (ms per step, per-step event times in ms)."""
+    steps.  step(ev=None, st=None) launches on `st` when given (the capture stream), else on
+    the stream it was set up with.  Returns (ms per step, per-step event times in ms)."""
     import torch
 
     for _ in range(warmup):
@@ -227,12 +228,12 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            step(st=side)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            step(st=torch.cuda.current_stream())
         g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -372,14 +373,17 @@ def run_prefill(args) -> int:
     B, lmax = len(case.context_lens), case.max_context_len
     need = pkv.paged_attention_prefill_workspace_size(B, T, Hq, Hkv, D, lmax, P)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+    def step(ev=None, st=None):
+        st = stream if st is None else st
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
         if ev is not None:
-            ev[0].record()
-        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws)
+            ev[0].record(st)
+        pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
+                                    stream=st)
         if ev is not None:
-            ev[1].record()
+            ev[1].record(st)
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
@@ -495,29 +499,32 @@ def main() -> int:
     need = pkv.paged_attention_workspace_size(B, Hq, D, lmax, P)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
+    stream = torch.cuda.current_stream()
     ptrs = pkv.copy_blocks([kc], [vc], t["mapping"]) if beam else None
 
-    def step(ev=None):
+    def step(ev=None, st=None):
+        st = stream if st is None else st
         if beam:  # device pointer table made once, outside any graph capture
-            pkv.copy_blocks([kc], [vc], t["mapping"], _ptr_buffers=ptrs)
+            pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
         if kv8:
-            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale)
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
+                                      stream=st)
         else:
-            pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
         if ev is not None:
-            ev[0].record()
+            ev[0].record(st)
         if kv8:
             pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
-                                           case.v_scale, lmax, P, ws)
+                                           case.v_scale, lmax, P, ws, stream=st)
         elif beam:
             pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
-                                              P, ws)
+                                              P, ws, stream=st)
         else:
-            pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws)
+            pkv.paged_attention_partitions(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=st)
         if ev is not None:
-            ev[1].record()
+            ev[1].record(st)
         if not beam and not kv8:
-            pkv.paged_attention_reduce(out, cl, lmax, ws, P)
+            pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=st)
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
