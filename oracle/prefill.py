@@ -42,9 +42,12 @@ def request_of_rows(query_start_loc: np.ndarray, rows: np.ndarray) -> np.ndarray
 def chunked_prefill(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
                     dtype: str, block_tables: np.ndarray, context_lens: np.ndarray,
                     query_start_loc: np.ndarray, scale: float,
-                    pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+                    pairs: Optional[Iterable[Tuple[int, int]]] = None,
+                    kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                    v_scale: float = 1.0) -> np.ndarray:
     """Output [T, Hq, D] in float64 (only the (row, head) in ``pairs`` when given; other
-    entries stay NaN).  ``query_bits`` [T, Hq, D] holds the flattened query rows."""
+    entries stay NaN).  ``query_bits`` [T, Hq, D] holds the flattened query rows; the caches
+    hold ``kv_dtype`` when given (e.g. 'e4m3' codes with their per-cache scales)."""
     T, Hq, D = query_bits.shape
     Hkv = key_bits.shape[1]
     assert Hq % Hkv == 0
@@ -63,7 +66,8 @@ def chunked_prefill(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np
     for (b, kvh), items in sorted(wanted.items()):
         n, L = int(qsl[b + 1] - qsl[b]), int(context_lens[b])
         assert 0 <= n <= L, "a request's chunk cannot exceed its context"
-        K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, kvh)
+        K, V = gather_kv(key_bits, value_bits, kv_dtype or dtype, block_tables[b], L, kvh,
+                         k_scale, v_scale)
         pos = query_positions(L, n)
         for r, h in items:
             p = int(pos[r - qsl[b]])

@@ -148,3 +148,59 @@ def test_flop_count_closed_form():
     qsl, lens = np.array([0, 4, 5]), np.array([10, 3])
     pairs = (4 * 6 + 10) + (1 * 2 + 1)
     assert OP.attention_flops(lens, qsl, 2, 8) == 4 * 8 * 2 * pairs
+
+
+def _fp8_step(case):
+    """The caches after the step's scatter into an 8-bit cache (the chunk quantised)."""
+    kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+    OC.reshape_and_cache_fp8(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
+                             case.cfg.dtype, case.slot_mapping, case.k_scale, case.v_scale)
+    return kb, vb
+
+
+def test_fp8_whole_prompt_equals_sdpa_on_dequantised_kv():
+    """Over an 8-bit cache: whole prompts equal causal SDPA on K, V dequantised by torch's
+    float8_e4m3fn cast (independent of the oracle's codec), times the scales."""
+    from workloads import with_fp8_cache
+    case = with_fp8_cache(make_prefill_case([(0, 29), (0, 8)], **SMALL, seed=20))
+    kb, vb = _fp8_step(case)
+    out = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
+                             case.context_lens, case.query_start_loc, case.scale,
+                             kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+    G = case.cfg.num_heads // case.cfg.num_kv_heads
+    x = kb.shape[-1]
+    for b in range(2):
+        s0, s1 = case.query_start_loc[b], case.query_start_loc[b + 1]
+        L = int(case.context_lens[b])
+        t = np.arange(L)
+        blk = case.block_tables[b][t // case.cfg.block_size]
+        off = t % case.cfg.block_size
+        Ks, Vs = [], []
+        for h in range(case.cfg.num_kv_heads):
+            d = np.arange(case.cfg.head_size)
+            kcode = kb[blk[:, None], h, (d // x)[None, :], off[:, None], (d % x)[None, :]]
+            vcode = vb[blk[:, None], h, d[None, :], off[:, None]]
+            deq = lambda c, sc: (torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn)
+                                 .to(torch.float64) * float(np.float32(sc)))
+            Ks.append(deq(kcode, case.k_scale))
+            Vs.append(deq(vcode, case.v_scale))
+        K = torch.stack(Ks).repeat_interleave(G, 0)
+        V = torch.stack(Vs).repeat_interleave(G, 0)
+        q = torch.from_numpy(OA.widen(storage_bits(case.query)[s0:s1], "bf16")).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, K, V, is_causal=True, scale=OA.as_scale(case.scale)).permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[s0:s1], ref, rtol=0, atol=1e-12)
+
+
+def test_fp8_decode_rows_equal_fp8_paged_decode():
+    from workloads import with_fp8_cache
+    case = with_fp8_cache(make_prefill_case([(40, 1), (0, 9), (100, 1)], **SMALL, seed=21))
+    kb, vb = _fp8_step(case)
+    out = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
+                             case.context_lens, case.query_start_loc, case.scale,
+                             kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+    rows = [int(case.query_start_loc[b]) for b in (0, 2)]
+    dec = OA.paged_decode(storage_bits(case.query)[rows], kb, vb, "bf16", case.block_tables[[0, 2]],
+                          case.context_lens[[0, 2]], case.scale, kv_dtype="e4m3",
+                          k_scale=case.k_scale, v_scale=case.v_scale)
+    assert np.array_equal(out[rows], dec)

@@ -104,8 +104,11 @@ def _normal_to(shape, g: np.random.Generator, dtype: str) -> torch.Tensor:
 
 
 def storage_bits(t: torch.Tensor) -> np.ndarray:
-    """Raw storage of a CPU tensor as unsigned integers (uint16 for 2-byte dtypes, uint32 for fp32)."""
+    """Raw storage of a CPU tensor as unsigned integers (uint8 for 8-bit codes, uint16 for 2-byte
+    dtypes, uint32 for fp32)."""
     t = t.contiguous()
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy()
     if t.element_size() == 2:
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.element_size() == 4:
@@ -266,7 +269,7 @@ def to_e4m3_codes(t: torch.Tensor, scale: float) -> torch.Tensor:
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def with_fp8_cache(case: DecodeCase, k_scale: float = 0.0137, v_scale: float = 0.0211) -> DecodeCase:
+def with_fp8_cache(case, k_scale: float = 0.0137, v_scale: float = 0.0211):
     """The same step with an 8-bit cache: every stored key / value (NaN in unused slots) as its
     E4M3 code with the given per-cache scales.  Queries and the step's new tokens keep the
     model's 16-bit type."""
@@ -480,6 +483,9 @@ class PrefillCase:
     new_value: torch.Tensor        # [T, Hkv, D]
     slot_mapping: np.ndarray       # int64 [T]
     scale: float
+    kv_dtype: Optional[str] = None  # 'e4m3': caches hold uint8 FP8 codes (new K/V stay 16-bit)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_tokens(self) -> int:
