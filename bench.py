@@ -353,12 +353,15 @@ def run_prefill(args) -> int:
 
     import paged_kv_cache_164_amd as pkv
     from oracle.prefill import attention_flops
-    from workloads import draw_prefill_requests, make_prefill_case
+    from workloads import draw_prefill_requests, make_prefill_case, with_fp8_cache
 
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
     P = args.partition
     case = make_prefill_case(draw_prefill_requests(), poison=False)
+    kv8 = args.kv == "fp8"
+    if kv8:
+        case = with_fp8_cache(case)
     q = case.query.to(dev)
     kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
@@ -377,11 +380,15 @@ def run_prefill(args) -> int:
 
     def step(ev=None, st=None):
         st = stream if st is None else st
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+        if kv8:
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale, stream=st)
+        else:
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
         if ev is not None:
             ev[0].record(st)
         pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
-                                    stream=st)
+                                    stream=st, k_scale=case.k_scale if kv8 else None,
+                                    v_scale=case.v_scale if kv8 else None)
         if ev is not None:
             ev[1].record(st)
 
@@ -405,7 +412,9 @@ def run_prefill(args) -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "num_seqs": B,
+        "config": {"workload": f"{args.workload}{'-fp8' if kv8 else ''}: {WORKLOADS[args.workload]}"
+                               + ("; KV cache as FP8 E4M3 codes with per-cache scales" if kv8 else ""),
+                   "num_seqs": B,
                    "num_tokens": T, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
                    "block_size": bs, "partition_size": P or "auto: 8192",
                    "kv_tokens": int(case.context_lens.sum()), "max_context_len": lmax,
@@ -418,7 +427,9 @@ def run_prefill(args) -> int:
                          [round(float(np.percentile(k_ms, 10)), 5), round(float(np.percentile(k_ms, 90)), 5)],
                      "algorithmic_flops_per_launch": flops},
     }
-    if not args.no_cpu_baseline:
+    if kv8:
+        rec["config"]["kv_dtype"] = "fp8_e4m3"
+    if not args.no_cpu_baseline and not kv8:
         rec["cpu_baseline"] = prefill_cpu_baseline(case)
     print(json.dumps(rec), flush=True)
     return 0
@@ -458,9 +469,6 @@ def main() -> int:
         return 0
 
     if args.workload == "c6":
-        if args.kv != "native":
-            print("--kv fp8 applies to the decode workloads c2, c3, c4", file=sys.stderr)
-            return 2
         return run_prefill(args)
 
     import torch
@@ -474,7 +482,7 @@ def main() -> int:
     beam = args.workload == "c5"
     kv8 = args.kv == "fp8"
     if kv8 and (beam or args.workload == "c1"):
-        print("--kv fp8 applies to the 16-bit workloads c2, c3, c4", file=sys.stderr)
+        print("--kv fp8 applies to the 16-bit workloads c2, c3, c4, c6", file=sys.stderr)
         return 2
     if beam:
         t, lens_np, unique_tokens = beam_setup(dev)

@@ -265,6 +265,24 @@ int pkv_paged_attention_prefill(void* out, const void* query, const void* key_ca
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same multi-query attention over an 8-bit (FP8 E4M3) KV cache, in the layouts and with
+ * the per-cache scales of pkv_paged_attention_decode_fp8 (key = code x k_scale, value =
+ * code x v_scale; k_scale, v_scale host floats, finite and > 0).  query and out stay PKV_F16
+ * or PKV_BF16 (`dtype`); the chunk's keys and values must already be in the cache
+ * (pkv_reshape_and_cache_fp8).  Everything else -- rows, partitioning, workspace
+ * (pkv_paged_attention_prefill_workspace_size), errors -- as for pkv_paged_attention_prefill.
+ */
+int pkv_paged_attention_prefill_fp8(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start_loc,
+                                    float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid (not part of the attention path): read `bytes` of device memory at `src`
  * with the non-temporal 16-byte loads the decode kernels use for the KV cache, as fast as the
  * memory system allows, to measure the achievable HBM read ceiling on the running GPU.

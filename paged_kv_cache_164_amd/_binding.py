@@ -42,6 +42,8 @@ _SIGNATURES = {
     "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
     "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
                                     + [_c_p, _c_sz, _c_p]),
+    "pkv_paged_attention_prefill_fp8": (_c_int, [_c_p] * 7 + [_c_f] * 3 + [_c_int] * 10
+                                        + [_c_p, _c_sz, _c_p]),
     "pkv_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_p]),
     "pkv_reshape_and_cache_fp8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
                                            _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
@@ -208,15 +210,22 @@ def paged_attention_prefill_workspace_size(num_seqs: int, num_tokens: int, num_h
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
                             query_start_loc, scale, max_context_len, partition_size=0,
-                            workspace=None, stream=None):
+                            workspace=None, stream=None, k_scale=None, v_scale=None):
     """Multi-query (chunked prefill / mixed batch) attention: query rows
     [query_start_loc[b], query_start_loc[b+1]) of request b are the last positions of its
-    context_lens[b]-token context and attend causally over its paged keys and values."""
+    context_lens[b]-token context and attend causally over its paged keys and values.
+    With k_scale / v_scale the caches hold 8-bit E4M3 codes (uint8)."""
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc)
     T, Hq, D = query.shape
     NB, Hkv, Dx, bs, x = key_cache.shape
     B = context_lens.numel()
-    if not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
+    kv8 = k_scale is not None
+    if kv8:
+        if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8 or v_scale is None:
+            raise PKVError("an 8-bit cache holds uint8 codes and needs k_scale and v_scale")
+        if query.dtype != out.dtype or query.element_size() != 2:
+            raise PKVError("query and out must share one 16-bit dtype")
+    elif not (query.dtype == key_cache.dtype == value_cache.dtype == out.dtype):
         raise PKVError("query, caches and out must share one dtype")
     dt = _dtype_code(query)
     if x * key_cache.element_size() != 16 or Dx * x != D:
@@ -240,11 +249,15 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(library().pkv_paged_attention_prefill(
-        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
-        block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(), float(scale),
-        B, T, Hq, Hkv, D, bs, block_tables.shape[1], int(max_context_len), dt, int(partition_size),
-        ws_ptr, ws_bytes, _stream(stream)), "pkv_paged_attention_prefill")
+    ptrs = (out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), query_start_loc.data_ptr(), float(scale))
+    rest = (B, T, Hq, Hkv, D, bs, block_tables.shape[1], int(max_context_len), dt,
+            int(partition_size), ws_ptr, ws_bytes, _stream(stream))
+    if kv8:
+        _check(library().pkv_paged_attention_prefill_fp8(*ptrs, float(k_scale), float(v_scale), *rest),
+               "pkv_paged_attention_prefill_fp8")
+    else:
+        _check(library().pkv_paged_attention_prefill(*ptrs, *rest), "pkv_paged_attention_prefill")
     return out
 
 

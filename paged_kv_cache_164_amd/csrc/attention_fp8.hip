@@ -18,6 +18,7 @@
 //   * a lane loads 16 dims of a key row at once (one 16-byte chunk); the two halves feed two
 //     k-steps, so the query operand is loaded in the matching dim order.
 #include "pkv_device.h"
+#include "pkv_fp8.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -35,25 +36,6 @@ __device__ __forceinline__ f32x4 mma(BF16, const uint4& a, const uint4& b, f32x4
 __device__ __forceinline__ f32x4 mma(F16, const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-// Two E4M3 codes (byte pair HI of w) as two 16-bit values of the query's type, packed.
-template <bool HI>
-__device__ __forceinline__ uint32_t widen2(BF16, uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  // exact values: the upper halves of the two floats are their bf16 encodings
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
-template <bool HI>
-__device__ __forceinline__ uint32_t widen2(F16, uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));  // exact
-}
-// Eight codes (8 bytes) as eight 16-bit values: one MFMA operand.
-template <class DT>
-__device__ __forceinline__ uint4 widen8(uint32_t lo, uint32_t hi) {
-  return make_uint4(widen2<false>(DT(), lo), widen2<true>(DT(), lo), widen2<false>(DT(), hi),
-                    widen2<true>(DT(), hi));
 }
 
 __device__ __forceinline__ uint32_t to_bits(BF16, float v) { return f32_to_bf16_rne(v); }

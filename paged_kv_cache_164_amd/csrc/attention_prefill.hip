@@ -31,6 +31,10 @@
 // come out of the matrix cores (a product with a ones row) from the same rounded weights.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_prefill.h"
+#include "pkv_fp8.h"
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------------------
 // Attention: NW waves x CB blocks of 16 columns = 256 columns per workgroup.
 // ---------------------------------------------------------------------------------------
-template <class DT, int D, int BS, int NW, int CB>
+template <class DT, int D, int BS, int NW, int CB, bool KV8>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   static_assert(NW * CB * 16 == kPrefillColumns, "columns per workgroup");
   static_assert(BS == 8 || BS == 16 || BS == 32, "a 32-key stage holds whole blocks");
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const bool active = qi_first < nqt;                       // the wave has a real column
   const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
 
-  const int64_t tile_bytes = (int64_t)D * BS * 2;
+  const int64_t tile_bytes = (int64_t)D * BS * (KV8 ? 1 : 2);  // one (block, KV head) tile
   const int64_t block_bytes = tile_bytes * Hkv;
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
@@ -237,32 +241,44 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const int p = min(tid + i * NT, KPIECES - 1);
     const int c8 = p >> 5, tt = p & 31, d = p >> 2, t8 = (p & 3) * 8;
     kid[i] = tt / BS;
-    koff[i] = uint32_t(c8 * BS + tt % BS) * 16u;
     vid[i] = t8 / BS;
-    voff[i] = uint32_t(d * BS + t8 % BS) * 2u;
+    if constexpr (KV8) {  // 8-bit cache: keys [D/16][bs][16], values [D][bs], one byte each
+      koff[i] = uint32_t(((c8 >> 1) * BS + tt % BS) * 16 + (c8 & 1) * 8);
+      voff[i] = uint32_t(d * BS + t8 % BS);
+    } else {
+      koff[i] = uint32_t(c8 * BS + tt % BS) * 16u;
+      voff[i] = uint32_t(d * BS + t8 % BS) * 2u;
+    }
   }
-  uint4 kA[PPT], vA[PPT], kB[PPT], vB[PPT];
-  auto load_stage = [&](int s, uint4* kst, uint4* vst) {
+  // Raw pieces as loaded (8 codes of an 8-bit cache take 8 bytes); they are widened to the
+  // 16-bit type only when stored to LDS, so no load has to be waited for early.
+  using Raw = typename std::conditional<KV8, uint2, uint4>::type;
+  Raw kA[PPT], vA[PPT], kB[PPT], vB[PPT];
+  auto widen = [&](const Raw& r) -> uint4 {
+    if constexpr (KV8) return widen8<DT>(r.x, r.y);
+    else return r;
+  };
+  auto load_stage = [&](int s, Raw* kst, Raw* vst) {
     const int sid = min(s, nst - 1) * IDS_PER_STAGE;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       if (KPIECES % NT == 0 || tid + i * NT < KPIECES) {
         const uint32_t ik = uint32_t(s_ids[sid + kid[i]]), iv = uint32_t(s_ids[sid + vid[i]]);
-        kst[i] = *reinterpret_cast<const uint4*>(kbase + (uint64_t)ik * block_bytes + koff[i]);
-        vst[i] = *reinterpret_cast<const uint4*>(vbase + (uint64_t)iv * block_bytes + voff[i]);
+        kst[i] = *reinterpret_cast<const Raw*>(kbase + (uint64_t)ik * block_bytes + koff[i]);
+        vst[i] = *reinterpret_cast<const Raw*>(vbase + (uint64_t)iv * block_bytes + voff[i]);
       }
     }
   };
   // Values of tokens past the item's range are zeroed here (selects, no branch): the cache
   // past a context's end may hold anything, and a zero weight times NaN is NaN.
-  auto store_stage = [&](int buf, int s, const uint4* kst, const uint4* vst) {
+  auto store_stage = [&](int buf, int s, const Raw* kst, const Raw* vst) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
       if (KPIECES % NT == 0 || p < KPIECES) {
-        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + (p & 31)) * 16]) = kst[i];
+        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + (p & 31)) * 16]) = widen(kst[i]);
         const int d = p >> 2, t8 = (p & 3) * 8;
-        uint4 v = vst[i];
+        uint4 v = widen(vst[i]);
         if (k0 + 32 * (s + 1) > k1) v = mask8(v, k0 + 32 * s + t8, k1);  // the last stage only
         const int q = (t8 & 15) >> 2, half = t8 >> 4;
         char* row = &s_v[buf][d * VRS + half * 8];
@@ -449,7 +465,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     if (qi_c[cb] >= nqt) continue;
     const int64_t orow = (int64_t)(row0 + qi_c[cb]) * Hq + kh * G + (c - qi_c[cb] * G);
     if (npieces == 1) {
-      const float inv = 1.f / l_tot;
+      const float inv = (KV8 ? a.v_scale : 1.f) / l_tot;
 #pragma unroll
       for (int i = 0; i < NDT; ++i) {
         const f32x4 o = oacc[i][cb] * inv;
@@ -459,8 +475,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     } else {
       const int64_t sp = orow * a.slots + slot;
 #pragma unroll
-      for (int i = 0; i < NDT; ++i)
-        *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) = oacc[i][cb];
+      for (int i = 0; i < NDT; ++i)  // the value scale of an 8-bit cache goes into the partials
+        *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) =
+            KV8 ? oacc[i][cb] * a.v_scale : oacc[i][cb];
       if (quad == 0) {
         a.part_m[sp] = m_run[cb];
         a.part_l[sp] = l_tot;
@@ -469,30 +486,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <class DT, int D, int BS>
+template <class DT, int D, int BS, bool KV8>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   constexpr int NW = 8, CB = 2;
   const int64_t grid = a.capacity * a.num_kv_heads;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, NW, CB>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, NW, CB, KV8>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <class DT, int D>
+template <class DT, int D, bool KV8>
 hipError_t by_block(const PrefillArgs& a, int bs, hipStream_t s) {
   switch (bs) {
-    case 8: return launch_t<DT, D, 8>(a, s);
-    case 16: return launch_t<DT, D, 16>(a, s);
-    case 32: return launch_t<DT, D, 32>(a, s);
+    case 8: return launch_t<DT, D, 8, KV8>(a, s);
+    case 16: return launch_t<DT, D, 16, KV8>(a, s);
+    case 32: return launch_t<DT, D, 32, KV8>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <class DT>
+template <class DT, bool KV8>
 hipError_t by_head(const PrefillArgs& a, int D, int bs, hipStream_t s) {
   switch (D) {
-    case 64: return by_block<DT, 64>(a, bs, s);
-    case 128: return by_block<DT, 128>(a, bs, s);
+    case 64: return by_block<DT, 64, KV8>(a, bs, s);
+    case 128: return by_block<DT, 128, KV8>(a, bs, s);
   }
   return hipErrorInvalidValue;
 }
@@ -505,12 +522,16 @@ bool prefill_supported(int dtype, int head_size, int block_size, int group) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const DecodeArgs& red, int dtype, int head_size,
-                          int block_size, hipStream_t stream) {
+                          int block_size, bool kv8, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = (dtype == 1) ? by_head<F16>(a, head_size, block_size, stream)
-                   : by_head<BF16>(a, head_size, block_size, stream);
+  if (kv8)
+    e = (dtype == 1) ? by_head<F16, true>(a, head_size, block_size, stream)
+                     : by_head<BF16, true>(a, head_size, block_size, stream);
+  else
+    e = (dtype == 1) ? by_head<F16, false>(a, head_size, block_size, stream)
+                     : by_head<BF16, false>(a, head_size, block_size, stream);
   if (e != hipSuccess || a.slots <= 1) return e;
   return launch_reduce(red, dtype, head_size, stream);
 }

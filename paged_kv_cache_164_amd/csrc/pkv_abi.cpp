@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "pkv_internal.h"
+#include "pkv_prefill.h"
 #include "pkv_probe.h"
 
 namespace {
@@ -214,6 +215,97 @@ namespace pkv {
 int record_error(int code, const char* msg) { return fail(code, msg); }
 }  // namespace pkv
 
+static int prefill_call(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, const int32_t* query_start_loc, float scale,
+                        const Kv8* kv8, int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                        int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+                        int32_t partition_size, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  try {
+    if (dtype != PKV_F16 && dtype != PKV_BF16)
+      return fail(dtype == PKV_F32 ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARG,
+                  "multi-query attention runs on the matrix cores: dtype must be PKV_F16 or PKV_BF16");
+    if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        max_context_len < 0 || max_num_blocks_per_seq < 0)
+      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
+    if (num_heads % num_kv_heads != 0)
+      return fail(PKV_ERR_INVALID_ARG, "num_heads must be a multiple of num_kv_heads");
+    if (!(std::isfinite(scale) && scale > 0.f))
+      return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+    if (kv8 && !(std::isfinite(kv8->k_scale) && kv8->k_scale > 0.f && std::isfinite(kv8->v_scale) &&
+                 kv8->v_scale > 0.f))
+      return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
+    const int group = num_heads / num_kv_heads;
+    if (!pkv::prefill_supported(dtype, head_size, block_size, group))
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "head_size must be 64 or 128, block_size 8, 16 or 32, num_heads/num_kv_heads <= 16");
+    const int P = prefill_partition(partition_size);
+    if (P < 0)
+      return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of 32 in [32, 8192]");
+    if ((int64_t)max_num_blocks_per_seq * block_size < max_context_len)
+      return fail(PKV_ERR_INVALID_ARG, "block table rows are shorter than max_context_len");
+    if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+        !query_start_loc)
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    const pkv::PrefillLayout w = pkv::prefill_layout(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                                     head_size, max_context_len, P);
+    if (w.capacity * num_kv_heads >= (int64_t(1) << 31))
+      return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    if (workspace == nullptr || workspace_bytes < w.total)
+      return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(w.total) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    pkv::PrefillArgs a{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.queue = reinterpret_cast<uint32_t*>(ws);
+    a.items = reinterpret_cast<uint4*>(ws + w.items_off);
+    a.np_of = reinterpret_cast<int32_t*>(ws + w.np_off);
+    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
+    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
+    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
+    a.scale_log2 = scale * pkv::kLog2e * (kv8 ? kv8->k_scale : 1.f);
+    a.v_scale = kv8 ? kv8->v_scale : 1.f;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_num_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.group = group;
+    a.q_tile = pkv::kPrefillColumns / group;
+    a.partition_size = P;
+    a.slots = (int)w.slots;
+    a.capacity = w.capacity;
+    // the split-K reduce of the decode path, with one "sequence" per query row
+    pkv::DecodeArgs red{};
+    red.out = out;
+    red.np_of = a.np_of;
+    red.part_m = a.part_m;
+    red.part_l = a.part_l;
+    red.part_acc = a.part_acc;
+    red.num_seqs = num_tokens;
+    red.num_heads = num_heads;
+    red.num_kv_heads = num_kv_heads;
+    red.slots = a.slots;
+    const hipError_t e = pkv::launch_prefill(a, red, dtype, head_size, block_size, kv8 != nullptr,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "multi-query attention launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
@@ -355,82 +447,26 @@ int pkv_paged_attention_prefill(void* out, const void* query, const void* key_ca
                                 int32_t block_size, int32_t max_num_blocks_per_seq,
                                 int32_t max_context_len, int32_t dtype, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  try {
-    if (dtype != PKV_F16 && dtype != PKV_BF16)
-      return fail(dtype == PKV_F32 ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARG,
-                  "multi-query attention runs on the matrix cores: dtype must be PKV_F16 or PKV_BF16");
-    if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
-        max_context_len < 0 || max_num_blocks_per_seq < 0)
-      return fail(PKV_ERR_INVALID_ARG, "negative or zero size");
-    if (num_heads % num_kv_heads != 0)
-      return fail(PKV_ERR_INVALID_ARG, "num_heads must be a multiple of num_kv_heads");
-    if (!(std::isfinite(scale) && scale > 0.f))
-      return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
-    const int group = num_heads / num_kv_heads;
-    if (!pkv::prefill_supported(dtype, head_size, block_size, group))
-      return fail(PKV_ERR_UNSUPPORTED,
-                  "head_size must be 64 or 128, block_size 8, 16 or 32, num_heads/num_kv_heads <= 16");
-    const int P = prefill_partition(partition_size);
-    if (P < 0)
-      return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of 32 in [32, 8192]");
-    if ((int64_t)max_num_blocks_per_seq * block_size < max_context_len)
-      return fail(PKV_ERR_INVALID_ARG, "block table rows are shorter than max_context_len");
-    if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
-    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
-        !query_start_loc)
-      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
-    const pkv::PrefillLayout w = pkv::prefill_layout(num_seqs, num_tokens, num_heads, num_kv_heads,
-                                                     head_size, max_context_len, P);
-    if (w.capacity * num_kv_heads >= (int64_t(1) << 31))
-      return fail(PKV_ERR_UNSUPPORTED, "grid too large");
-    if (workspace == nullptr || workspace_bytes < w.total)
-      return fail(PKV_ERR_WORKSPACE, "workspace missing or too small: need " + std::to_string(w.total) + " bytes");
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    char* ws = static_cast<char*>(workspace);
-    pkv::PrefillArgs a{};
-    a.out = out;
-    a.query = query;
-    a.key_cache = key_cache;
-    a.value_cache = value_cache;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.query_start_loc = query_start_loc;
-    a.queue = reinterpret_cast<uint32_t*>(ws);
-    a.items = reinterpret_cast<uint4*>(ws + w.items_off);
-    a.np_of = reinterpret_cast<int32_t*>(ws + w.np_off);
-    a.part_m = reinterpret_cast<float*>(ws + w.m_off);
-    a.part_l = reinterpret_cast<float*>(ws + w.l_off);
-    a.part_acc = reinterpret_cast<float*>(ws + w.acc_off);
-    a.scale_log2 = scale * pkv::kLog2e;
-    a.num_seqs = num_seqs;
-    a.num_tokens = num_tokens;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.max_blocks = max_num_blocks_per_seq;
-    a.max_context_len = max_context_len;
-    a.group = group;
-    a.q_tile = pkv::kPrefillColumns / group;
-    a.partition_size = P;
-    a.slots = (int)w.slots;
-    a.capacity = w.capacity;
-    // the split-K reduce of the decode path, with one "sequence" per query row
-    pkv::DecodeArgs red{};
-    red.out = out;
-    red.np_of = a.np_of;
-    red.part_m = a.part_m;
-    red.part_l = a.part_l;
-    red.part_acc = a.part_acc;
-    red.num_seqs = num_tokens;
-    red.num_heads = num_heads;
-    red.num_kv_heads = num_kv_heads;
-    red.slots = a.slots;
-    const hipError_t e = pkv::launch_prefill(a, red, dtype, head_size, block_size,
-                                             static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? PKV_OK : hip_fail(e, "multi-query attention launch");
-  } catch (...) {
-    return fail(PKV_ERR_HIP, "unexpected C++ exception");
-  }
+  return prefill_call(out, query, key_cache, value_cache, block_tables, context_lens,
+                      query_start_loc, scale, nullptr, num_seqs, num_tokens, num_heads,
+                      num_kv_heads, head_size, block_size, max_num_blocks_per_seq,
+                      max_context_len, dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_prefill_fp8(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_start_loc,
+                                    float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                    int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const Kv8 kv8{k_scale, v_scale};
+  return prefill_call(out, query, key_cache, value_cache, block_tables, context_lens,
+                      query_start_loc, scale, &kv8, num_seqs, num_tokens, num_heads,
+                      num_kv_heads, head_size, block_size, max_num_blocks_per_seq,
+                      max_context_len, dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
 int pkv_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
