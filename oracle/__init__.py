@@ -29,6 +29,8 @@ What it computes, and from where:
   book's note on chunked prefill).
 * ``fp8`` -- the OCP FP8 E4M3 codec of the 8-bit KV cache, from the format's
   definition.
+* ``int8`` -- the symmetric INT8 codec of the 8-bit KV cache (one scale per
+  cache, codes -127 .. 127, ties to even).
 * ``block_manager.OracleBlockManager`` -- the host bookkeeping that feeds
   those operations (the BlockSpaceManager of the AIGC interview book, section
   23, and the "Vllm" page's scheduler): admission with a watermark, fork,

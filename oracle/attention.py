@@ -39,8 +39,9 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
 
     ``dtype`` is 'f32' (uint32 bits), 'f16' (uint16, IEEE binary16),
     'bf16' (uint16: the upper half of an IEEE binary32, so shifting the bits
-    left by 16 gives the binary32 with the same value) or 'e4m3' (uint8, the
-    8-bit float of oracle.fp8, without its scale).
+    left by 16 gives the binary32 with the same value), 'e4m3' (uint8, the
+    8-bit float of oracle.fp8, without its scale) or 'i8' (uint8 bytes of the
+    signed integer codes of oracle.int8, without their scale).
     """
     if dtype == "f32":
         return bits.view(np.float32).astype(np.float64)
@@ -51,6 +52,9 @@ def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "e4m3":
         from oracle.fp8 import e4m3_decode
         return e4m3_decode(bits)
+    if dtype == "i8":
+        from oracle.int8 import i8_decode
+        return i8_decode(bits)
     raise ValueError(dtype)
 
 

@@ -61,6 +61,18 @@ def reshape_and_cache_fp8(key_cache: np.ndarray, value_cache: np.ndarray, key_bi
     reshape_and_cache(key_cache, value_cache, kq, vq, slot_mapping)
 
 
+def reshape_and_cache_int8(key_cache: np.ndarray, value_cache: np.ndarray, key_bits: np.ndarray,
+                           value_bits: np.ndarray, dtype: str, slot_mapping: Sequence[int],
+                           k_scale: float, v_scale: float) -> None:
+    """The same scatter into an 8-bit integer cache: each new element is quantised with
+    oracle.int8.quantize and its cache's scale first."""
+    from oracle.attention import widen
+    from oracle.int8 import quantize
+    kq = quantize(widen(key_bits, dtype).astype(np.float32), k_scale)
+    vq = quantize(widen(value_bits, dtype).astype(np.float32), v_scale)
+    reshape_and_cache(key_cache, value_cache, kq, vq, slot_mapping)
+
+
 def copy_blocks(caches: List[np.ndarray], mapping: Sequence[Tuple[int, int]]) -> None:
     """In place, for each cache array (every layer's K and V): cache[dst] = old cache[src]."""
     for cache in caches:

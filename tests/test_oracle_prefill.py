@@ -150,23 +150,27 @@ def test_flop_count_closed_form():
     assert OP.attention_flops(lens, qsl, 2, 8) == 4 * 8 * 2 * pairs
 
 
-def _fp8_step(case):
+def _kv8_step(case):
     """The caches after the step's scatter into an 8-bit cache (the chunk quantised)."""
     kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
-    OC.reshape_and_cache_fp8(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
-                             case.cfg.dtype, case.slot_mapping, case.k_scale, case.v_scale)
+    write = OC.reshape_and_cache_fp8 if case.kv_dtype == "e4m3" else OC.reshape_and_cache_int8
+    write(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
+          case.cfg.dtype, case.slot_mapping, case.k_scale, case.v_scale)
     return kb, vb
 
 
-def test_fp8_whole_prompt_equals_sdpa_on_dequantised_kv():
-    """Over an 8-bit cache: whole prompts equal causal SDPA on K, V dequantised by torch's
-    float8_e4m3fn cast (independent of the oracle's codec), times the scales."""
-    from workloads import with_fp8_cache
-    case = with_fp8_cache(make_prefill_case([(0, 29), (0, 8)], **SMALL, seed=20))
-    kb, vb = _fp8_step(case)
+@pytest.mark.parametrize("code", ["e4m3", "i8"])
+def test_kv8_whole_prompt_equals_sdpa_on_dequantised_kv(code):
+    """Over an 8-bit cache: whole prompts equal causal SDPA on K, V dequantised by torch's own
+    casts (float8_e4m3fn or int8 to float64, independent of the oracle's codecs), times the
+    scales."""
+    from workloads import with_8bit_cache
+    case = with_8bit_cache(make_prefill_case([(0, 29), (0, 8)], **SMALL, seed=20), code)
+    kb, vb = _kv8_step(case)
     out = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
                              case.context_lens, case.query_start_loc, case.scale,
-                             kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+                             kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
+    tdt = torch.float8_e4m3fn if code == "e4m3" else torch.int8
     G = case.cfg.num_heads // case.cfg.num_kv_heads
     x = kb.shape[-1]
     for b in range(2):
@@ -180,7 +184,7 @@ def test_fp8_whole_prompt_equals_sdpa_on_dequantised_kv():
             d = np.arange(case.cfg.head_size)
             kcode = kb[blk[:, None], h, (d // x)[None, :], off[:, None], (d % x)[None, :]]
             vcode = vb[blk[:, None], h, d[None, :], off[:, None]]
-            deq = lambda c, sc: (torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn)
+            deq = lambda c, sc: (torch.from_numpy(np.ascontiguousarray(c)).view(tdt)
                                  .to(torch.float64) * float(np.float32(sc)))
             Ks.append(deq(kcode, case.k_scale))
             Vs.append(deq(vcode, case.v_scale))
@@ -192,15 +196,16 @@ def test_fp8_whole_prompt_equals_sdpa_on_dequantised_kv():
         np.testing.assert_allclose(out[s0:s1], ref, rtol=0, atol=1e-12)
 
 
-def test_fp8_decode_rows_equal_fp8_paged_decode():
-    from workloads import with_fp8_cache
-    case = with_fp8_cache(make_prefill_case([(40, 1), (0, 9), (100, 1)], **SMALL, seed=21))
-    kb, vb = _fp8_step(case)
+@pytest.mark.parametrize("code", ["e4m3", "i8"])
+def test_kv8_decode_rows_equal_kv8_paged_decode(code):
+    from workloads import with_8bit_cache
+    case = with_8bit_cache(make_prefill_case([(40, 1), (0, 9), (100, 1)], **SMALL, seed=21), code)
+    kb, vb = _kv8_step(case)
     out = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
                              case.context_lens, case.query_start_loc, case.scale,
-                             kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+                             kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
     rows = [int(case.query_start_loc[b]) for b in (0, 2)]
     dec = OA.paged_decode(storage_bits(case.query)[rows], kb, vb, "bf16", case.block_tables[[0, 2]],
-                          case.context_lens[[0, 2]], case.scale, kv_dtype="e4m3",
+                          case.context_lens[[0, 2]], case.scale, kv_dtype=code,
                           k_scale=case.k_scale, v_scale=case.v_scale)
     assert np.array_equal(out[rows], dec)

@@ -140,7 +140,7 @@ class DecodeCase:
     scale: float
     used_blocks: np.ndarray     # physical ids in use, in assignment order
     free_blocks: np.ndarray     # physical ids not referenced by any table
-    kv_dtype: Optional[str] = None  # 'e4m3': caches hold uint8 FP8 codes (new K/V stay 16-bit)
+    kv_dtype: Optional[str] = None  # 'e4m3' / 'i8': caches hold 8-bit codes (new K/V stay 16-bit)
     k_scale: float = 1.0
     v_scale: float = 1.0
 
@@ -269,18 +269,43 @@ def to_e4m3_codes(t: torch.Tensor, scale: float) -> torch.Tensor:
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def with_fp8_cache(case, k_scale: float = 0.0137, v_scale: float = 0.0211):
+def to_i8_codes(t: torch.Tensor, scale: float) -> torch.Tensor:
+    """uint8 bytes of the INT8 codes of t / scale (torch's round half to even, clamped to
+    +-127); NaN elements (the unused slots of a poisoned cache) become -128, a code the cache
+    write never produces."""
+    y = t.to(torch.float32) / torch.tensor(scale, dtype=torch.float32)
+    q = torch.round(torch.nan_to_num(y, nan=0.0)).clamp(-127, 127).to(torch.int8)
+    q = torch.where(torch.isnan(y), torch.full_like(q, -128), q)
+    return q.view(torch.uint8)
+
+
+# per-cache scales of the 8-bit workloads: N(0, 1) keys and values span about +-6 within E4M3's
+# +-448 and about +-4 within INT8's +-127
+KV8_SCALES = {"e4m3": (0.0137, 0.0211), "i8": (0.0313, 0.0297)}
+
+
+def with_8bit_cache(case, code: str = "e4m3", k_scale: Optional[float] = None,
+                    v_scale: Optional[float] = None):
     """The same step with an 8-bit cache: every stored key / value (NaN in unused slots) as its
-    E4M3 code with the given per-cache scales.  Queries and the step's new tokens keep the
-    model's 16-bit type."""
+    ``code`` ('e4m3' or 'i8') with the given per-cache scales.  Queries and the step's new
+    tokens keep the model's 16-bit type."""
+    ks0, vs0 = KV8_SCALES[code]
+    k_scale = ks0 if k_scale is None else k_scale
+    v_scale = vs0 if v_scale is None else v_scale
+    enc = to_e4m3_codes if code == "e4m3" else to_i8_codes
     NB, H, Dx, bs, x = case.key_cache.shape
     D = Dx * x
     # the 16-bit key layout [.., D/8, bs, 8] as [.., D/16, bs, 16] (x = 16 / sizeof(code) = 16)
     k = case.key_cache.permute(0, 1, 3, 2, 4).reshape(NB, H, bs, D // 16, 16).permute(0, 1, 3, 2, 4)
-    return dataclasses.replace(case, key_cache=to_e4m3_codes(k.contiguous(), k_scale),
-                               value_cache=to_e4m3_codes(case.value_cache, v_scale),
-                               kv_dtype="e4m3", k_scale=float(np.float32(k_scale)),
+    return dataclasses.replace(case, key_cache=enc(k.contiguous(), k_scale),
+                               value_cache=enc(case.value_cache, v_scale),
+                               kv_dtype=code, k_scale=float(np.float32(k_scale)),
                                v_scale=float(np.float32(v_scale)))
+
+
+def with_fp8_cache(case, k_scale: float = 0.0137, v_scale: float = 0.0211):
+    """with_8bit_cache with E4M3 codes."""
+    return with_8bit_cache(case, "e4m3", k_scale, v_scale)
 
 
 def random_free_slots(case: DecodeCase, n: int, stream_seed: int = 0) -> np.ndarray:
@@ -483,7 +508,7 @@ class PrefillCase:
     new_value: torch.Tensor        # [T, Hkv, D]
     slot_mapping: np.ndarray       # int64 [T]
     scale: float
-    kv_dtype: Optional[str] = None  # 'e4m3': caches hold uint8 FP8 codes (new K/V stay 16-bit)
+    kv_dtype: Optional[str] = None  # 'e4m3' / 'i8': caches hold 8-bit codes (new K/V stay 16-bit)
     k_scale: float = 1.0
     v_scale: float = 1.0
 
