@@ -40,6 +40,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E spec peak
+# --kv: code format of an 8-bit cache, its name, and the config's kv_dtype
+KV8_CODES = {"fp8": "e4m3", "int8": "i8"}
+KV8_NAMES = {"fp8": "FP8 E4M3", "int8": "INT8 (-127..127)"}
+KV8_DTYPES = {"fp8": "fp8_e4m3", "int8": "int8"}
 WORKLOADS = {
     "c1": "tiny paged decode: batch 4, 8 heads, head 64, block 16, fp32",
     "c2": "MHA decode, 7B-like layer: batch 64, 32 heads, head 128, block 16, fp16",
@@ -353,15 +357,16 @@ def run_prefill(args) -> int:
 
     import paged_kv_cache_164_amd as pkv
     from oracle.prefill import attention_flops
-    from workloads import draw_prefill_requests, make_prefill_case, with_fp8_cache
+    from workloads import draw_prefill_requests, make_prefill_case, with_8bit_cache
 
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
     P = args.partition
     case = make_prefill_case(draw_prefill_requests(), poison=False)
-    kv8 = args.kv == "fp8"
+    kv8 = args.kv != "native"
+    code = KV8_CODES.get(args.kv)
     if kv8:
-        case = with_fp8_cache(case)
+        case = with_8bit_cache(case, code)
     q = case.query.to(dev)
     kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
@@ -381,14 +386,15 @@ def run_prefill(args) -> int:
     def step(ev=None, st=None):
         st = stream if st is None else st
         if kv8:
-            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale, stream=st)
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale, stream=st,
+                                      code=code)
         else:
             pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
         if ev is not None:
             ev[0].record(st)
         pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
                                     stream=st, k_scale=case.k_scale if kv8 else None,
-                                    v_scale=case.v_scale if kv8 else None)
+                                    v_scale=case.v_scale if kv8 else None, code=code or "e4m3")
         if ev is not None:
             ev[1].record(st)
 
@@ -412,8 +418,8 @@ def run_prefill(args) -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}{'-fp8' if kv8 else ''}: {WORKLOADS[args.workload]}"
-                               + ("; KV cache as FP8 E4M3 codes with per-cache scales" if kv8 else ""),
+        "config": {"workload": f"{args.workload}{'-' + args.kv if kv8 else ''}: {WORKLOADS[args.workload]}"
+                               + (f"; KV cache as {KV8_NAMES[args.kv]} codes with per-cache scales" if kv8 else ""),
                    "num_seqs": B,
                    "num_tokens": T, "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D,
                    "block_size": bs, "partition_size": P or "auto: 8192",
@@ -428,7 +434,7 @@ def run_prefill(args) -> int:
                      "algorithmic_flops_per_launch": flops},
     }
     if kv8:
-        rec["config"]["kv_dtype"] = "fp8_e4m3"
+        rec["config"]["kv_dtype"] = KV8_DTYPES[args.kv]
     if not args.no_cpu_baseline and not kv8:
         rec["cpu_baseline"] = prefill_cpu_baseline(case)
     print(json.dumps(rec), flush=True)
@@ -442,8 +448,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=0)
-    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
-                    help="fp8: the same workload over an 8-bit (FP8 E4M3) KV cache")
+    ap.add_argument("--kv", default="native", choices=["native", "fp8", "int8"],
+                    help="fp8 / int8: the same workload over an 8-bit KV cache (FP8 E4M3 or "
+                         "INT8 codes with per-cache scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph instead of eager steps")
@@ -474,15 +481,16 @@ def main() -> int:
     import torch
 
     import paged_kv_cache_164_amd as pkv
-    from workloads import make_decode_case, with_fp8_cache
+    from workloads import make_decode_case, with_8bit_cache
 
     t_gen = time.perf_counter()
     dev = torch.device("cuda:0")
     P = args.partition
     beam = args.workload == "c5"
-    kv8 = args.kv == "fp8"
+    kv8 = args.kv != "native"
+    code = KV8_CODES.get(args.kv)
     if kv8 and (beam or args.workload == "c1"):
-        print("--kv fp8 applies to the 16-bit workloads c2, c3, c4, c6", file=sys.stderr)
+        print("--kv fp8 / int8 apply to the 16-bit workloads c2, c3, c4, c6", file=sys.stderr)
         return 2
     if beam:
         t, lens_np, unique_tokens = beam_setup(dev)
@@ -493,7 +501,7 @@ def main() -> int:
     else:
         case = make_decode_case(args.workload)
         if kv8:
-            case = with_fp8_cache(case)
+            case = with_8bit_cache(case, code)
         q = case.query.to(dev)
         kc, vc = case.key_cache.to(dev), case.value_cache.to(dev)
         bt, cl = case.block_tables.to(dev), case.context_lens.to(dev)
@@ -516,14 +524,14 @@ def main() -> int:
             pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
         if kv8:
             pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
-                                      stream=st)
+                                      stream=st, code=code)
         else:
             pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
         if ev is not None:
             ev[0].record(st)
         if kv8:
             pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
-                                           case.v_scale, lmax, P, ws, stream=st)
+                                           case.v_scale, lmax, P, ws, stream=st, code=code)
         elif beam:
             pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
                                               P, ws, stream=st)
@@ -566,8 +574,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[q.dtype],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}{'-fp8' if kv8 else ''}: {WORKLOADS[args.workload]}"
-                               + ("; KV cache as FP8 E4M3 codes with per-cache scales" if kv8 else ""),
+        "config": {"workload": f"{args.workload}{'-' + args.kv if kv8 else ''}: {WORKLOADS[args.workload]}"
+                               + (f"; KV cache as {KV8_NAMES[args.kv]} codes with per-cache scales" if kv8 else ""),
                    "num_seqs": B,
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
                    "partition_size": P or ("auto: 2048" if eb == 2 and (bs >= 16 or kv8) else "auto: 1024"),
@@ -586,7 +594,7 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": dec_bytes},
     }
     if kv8:
-        rec["config"]["kv_dtype"] = "fp8_e4m3"
+        rec["config"]["kv_dtype"] = KV8_DTYPES[args.kv]
     if beam:
         # per-sequence (logical) bytes: every sequence's attention over all of its tokens
         rec["config"]["unique_kv_tokens"] = unique_tokens

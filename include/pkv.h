@@ -221,6 +221,24 @@ int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * The same decode over an 8-bit integer KV cache: keys and values stored as
+ * signed integer codes -127 .. 127 (two's-complement bytes; the byte 0x80
+ * reads as -128) with one float scale per cache (key = code * k_scale, value
+ * = code * v_scale): the symmetric linear reading of the 8-bit KV-cache
+ * quantisation the AIGC interview book names for TurboMind and LMDeploy.
+ * Layouts, arguments, partitioning, workspace and errors exactly as for
+ * pkv_paged_attention_decode_fp8.
+ */
+int pkv_paged_attention_decode_int8(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, float k_scale,
+                                    float v_scale, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                    int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Multi-query paged attention: chunked prefill and mixed prefill / decode
  * batches.  The query rows of num_seqs requests are flattened; request b owns
  * rows [query_start_loc[b], query_start_loc[b + 1]) (the attention metadata of
@@ -283,6 +301,21 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const void* ke
                                     size_t workspace_bytes, void* stream);
 
 /*
+ * The same multi-query attention over an 8-bit integer KV cache (codes and scales of
+ * pkv_paged_attention_decode_int8; the chunk written by pkv_reshape_and_cache_int8).
+ * Everything else as for pkv_paged_attention_prefill_fp8.
+ */
+int pkv_paged_attention_prefill_int8(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start_loc,
+                                     float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t block_size,
+                                     int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                     int32_t dtype, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Measurement aid (not part of the attention path): read `bytes` of device memory at `src`
  * with the non-temporal 16-byte loads the decode kernels use for the KV cache, as fast as the
  * memory system allows, to measure the achievable HBM read ceiling on the running GPU.
@@ -327,6 +360,19 @@ int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cach
                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                               int64_t num_blocks, int64_t key_stride, int64_t value_stride,
                               int32_t dtype, float k_scale, float v_scale, void* stream);
+
+/*
+ * pkv_reshape_and_cache into an 8-bit integer cache (codes of
+ * pkv_paged_attention_decode_int8): each element x is stored as the integer
+ * nearest to x / scale (the division rounded to float32; ties to even),
+ * clamped to [-127, 127]; a NaN input gives code 0.  Everything else as for
+ * pkv_reshape_and_cache_fp8.
+ */
+int pkv_reshape_and_cache_int8(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                               int32_t dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * Copy whole blocks inside the device cache, for every layer (CacheEngine

@@ -17,9 +17,11 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_shared,
     paged_attention_decode_fp8,
+    paged_attention_decode_int8,
     paged_attention_prefill,
     paged_attention_prefill_workspace_size,
     reshape_and_cache_fp8,
+    reshape_and_cache_int8,
     paged_attention_partitions,
     paged_attention_reduce,
     paged_attention_workspace_size,

@@ -39,14 +39,20 @@ _SIGNATURES = {
                                           + _DECODE_ARGTYPES[6:]),
     "pkv_paged_attention_decode_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                        + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_decode_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                        + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
     "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
                                     + [_c_p, _c_sz, _c_p]),
     "pkv_paged_attention_prefill_fp8": (_c_int, [_c_p] * 7 + [_c_f] * 3 + [_c_int] * 10
                                         + [_c_p, _c_sz, _c_p]),
+    "pkv_paged_attention_prefill_int8": (_c_int, [_c_p] * 7 + [_c_f] * 3 + [_c_int] * 10
+                                         + [_c_p, _c_sz, _c_p]),
     "pkv_stream_read": (_c_int, [_c_p, _c_sz, _c_p, _c_p]),
     "pkv_reshape_and_cache_fp8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
                                            _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
+    "pkv_reshape_and_cache_int8": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int,
+                                            _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_f, _c_f, _c_p]),
     "pkv_reshape_and_cache": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
                                        _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
     "pkv_copy_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_p]),
@@ -210,17 +216,20 @@ def paged_attention_prefill_workspace_size(num_seqs: int, num_tokens: int, num_h
 
 def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, context_lens,
                             query_start_loc, scale, max_context_len, partition_size=0,
-                            workspace=None, stream=None, k_scale=None, v_scale=None):
+                            workspace=None, stream=None, k_scale=None, v_scale=None,
+                            code="e4m3"):
     """Multi-query (chunked prefill / mixed batch) attention: query rows
     [query_start_loc[b], query_start_loc[b+1]) of request b are the last positions of its
     context_lens[b]-token context and attend causally over its paged keys and values.
-    With k_scale / v_scale the caches hold 8-bit E4M3 codes (uint8)."""
+    With k_scale / v_scale the caches hold 8-bit codes (uint8): ``code`` 'e4m3' (FP8) or
+    'i8' (integers -127..127)."""
     _on_gpu(out, query, key_cache, value_cache, block_tables, context_lens, query_start_loc)
     T, Hq, D = query.shape
     NB, Hkv, Dx, bs, x = key_cache.shape
     B = context_lens.numel()
     kv8 = k_scale is not None
     if kv8:
+        _kv8_entry(code)
         if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8 or v_scale is None:
             raise PKVError("an 8-bit cache holds uint8 codes and needs k_scale and v_scale")
         if query.dtype != out.dtype or query.element_size() != 2:
@@ -254,23 +263,42 @@ def paged_attention_prefill(out, query, key_cache, value_cache, block_tables, co
     rest = (B, T, Hq, Hkv, D, bs, block_tables.shape[1], int(max_context_len), dt,
             int(partition_size), ws_ptr, ws_bytes, _stream(stream))
     if kv8:
-        _check(library().pkv_paged_attention_prefill_fp8(*ptrs, float(k_scale), float(v_scale), *rest),
-               "pkv_paged_attention_prefill_fp8")
+        name = "pkv_paged_attention_prefill_" + _kv8_entry(code)
+        _check(getattr(library(), name)(*ptrs, float(k_scale), float(v_scale), *rest), name)
     else:
         _check(library().pkv_paged_attention_prefill(*ptrs, *rest), "pkv_paged_attention_prefill")
     return out
 
 
+def _kv8_entry(code: str) -> str:
+    """Suffix of the C entry points for an 8-bit cache's code format."""
+    try:
+        return {"e4m3": "fp8", "i8": "int8"}[code]
+    except KeyError:
+        raise PKVError(f"8-bit cache code must be 'e4m3' or 'i8', got {code!r}") from None
+
+
 def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
                                scale, k_scale, v_scale, max_context_len, partition_size=0,
-                               workspace=None, stream=None):
-    """Decode over an 8-bit (FP8 E4M3) cache: key_cache uint8 [NB, Hkv, D/16, bs, 16],
-    value_cache uint8 [NB, Hkv, D, bs]; key = code * k_scale, value = code * v_scale."""
+                               workspace=None, stream=None, code="e4m3"):
+    """Decode over an 8-bit cache: key_cache uint8 [NB, Hkv, D/16, bs, 16], value_cache uint8
+    [NB, Hkv, D, bs]; key = code * k_scale, value = code * v_scale, the codes FP8 E4M3
+    (``code`` 'e4m3') or integers -127..127 ('i8')."""
+    name = "pkv_paged_attention_decode_" + _kv8_entry(code)
     args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                             max_context_len, partition_size, workspace, stream, kv8=True)
     args = args[:7] + (float(k_scale), float(v_scale)) + args[7:]
-    _check(library().pkv_paged_attention_decode_fp8(*args), "pkv_paged_attention_decode_fp8")
+    _check(getattr(library(), name)(*args), name)
     return out
+
+
+def paged_attention_decode_int8(out, query, key_cache, value_cache, block_tables, context_lens,
+                                scale, k_scale, v_scale, max_context_len, partition_size=0,
+                                workspace=None, stream=None):
+    """paged_attention_decode_fp8 over INT8 codes."""
+    return paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, scale, k_scale, v_scale, max_context_len,
+                                      partition_size, workspace, stream, code="i8")
 
 
 def paged_attention_partitions(out, query, key_cache, value_cache, block_tables, context_lens,
@@ -323,8 +351,10 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=N
 
 
 def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
-                         stream=None):
-    """key/value [N, Hkv, D] fp16/bf16 -> FP8 E4M3 codes in the 8-bit caches (x = 16)."""
+                         stream=None, code="e4m3"):
+    """key/value [N, Hkv, D] fp16/bf16 -> 8-bit codes in the 8-bit caches (x = 16): FP8 E4M3
+    (``code`` 'e4m3') or integers -127..127 ('i8')."""
+    name = "pkv_reshape_and_cache_" + _kv8_entry(code)
     _on_gpu(key, value, key_cache, value_cache, slot_mapping)
     N, Hkv, D = key.shape
     NB, Hkv2, Dx, bs, x = key_cache.shape
@@ -341,12 +371,17 @@ def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_sc
         raise PKVError("caches must be contiguous")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N or not slot_mapping.is_contiguous():
         raise PKVError("slot_mapping must be contiguous int64 with one entry per token")
-    _check(library().pkv_reshape_and_cache_fp8(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
-                                               value_cache.data_ptr(), slot_mapping.data_ptr(), N,
-                                               Hkv, D, bs, NB, key.stride(0), value.stride(0),
-                                               _dtype_code(key), float(k_scale), float(v_scale),
-                                               _stream(stream)),
-           "pkv_reshape_and_cache_fp8")
+    _check(getattr(library(), name)(key.data_ptr(), value.data_ptr(), key_cache.data_ptr(),
+                                    value_cache.data_ptr(), slot_mapping.data_ptr(), N, Hkv, D,
+                                    bs, NB, key.stride(0), value.stride(0), _dtype_code(key),
+                                    float(k_scale), float(v_scale), _stream(stream)), name)
+
+
+def reshape_and_cache_int8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                           stream=None):
+    """reshape_and_cache_fp8 writing INT8 codes."""
+    return reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale,
+                                 v_scale, stream, code="i8")
 
 
 def copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch.Tensor],

@@ -1,10 +1,10 @@
-// Paged decode attention over an 8-bit KV cache (FP8 E4M3 with one float scale per cache),
-// query and output in fp16 / bf16, on the matrix cores.
+// Paged decode attention over an 8-bit KV cache (FP8 E4M3 or INT8 codes, one float scale per
+// cache), query and output in fp16 / bf16, on the matrix cores.
 //
 // The cache layout is the "Vllm" page's ("CacheEngine") with x = 16 / sizeof = 16: a
 // (block, KV head) key tile is [D/16][bs][16] bytes, a value tile [D][bs] bytes.  Codes are
-// widened in registers to the query's type (exact: every E4M3 value is a bf16 and an fp16
-// value); the key scale is folded into the logit scale and the value scale into the output,
+// widened in registers to the query's type (exact: every E4M3 value and every integer code is a
+// bf16 and an fp16 value); the key scale is folded into the logit scale and the value scale into the output,
 // so no per-element multiply is spent on them.
 //
 // Same work items, scheduling, online softmax and epilogue as the 16-bit kernel
@@ -18,8 +18,9 @@
 //   * a lane loads 16 dims of a key row at once (one 16-byte chunk); the two halves feed two
 //     k-steps, so the query operand is loaded in the matching dim order.
 #include "pkv_device.h"
-#include "pkv_fp8.h"
+#include "pkv_kv8.h"
 #include "pkv_internal.h"
+#include "pkv_kv8_host.h"
 
 namespace pkv {
 namespace {
@@ -53,7 +54,7 @@ __device__ __forceinline__ uint32_t keep4(int base, int limit) {
          ((base + 2 < limit) ? 0x00ff0000u : 0u) | ((base + 3 < limit) ? 0xff000000u : 0u);
 }
 
-template <class DT, int D, int BS>
+template <class DT, int D, int BS, int CODE>
 __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int b0, int nseq,
                                          int tok0, int tok_end, int slot) {
   constexpr int TT = 32;        // tokens per tile
@@ -166,8 +167,8 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
       s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KJ; ++j) {
-        s[r] = mma(DT(), widen8<DT>(tl.k[r][j].x, tl.k[r][j].y), qop[j][0], s[r]);
-        s[r] = mma(DT(), widen8<DT>(tl.k[r][j].z, tl.k[r][j].w), qop[j][1], s[r]);
+        s[r] = mma(DT(), widen8<DT, CODE>(tl.k[r][j].x, tl.k[r][j].y), qop[j][0], s[r]);
+        s[r] = mma(DT(), widen8<DT, CODE>(tl.k[r][j].z, tl.k[r][j].w), qop[j][1], s[r]);
       }
     }
     // lane: logits of tokens t0 + vtok + 4 r + e (e < 4) of its column
@@ -205,7 +206,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
       for (int i = 0; i < NDT; ++i) tl.v[i] = make_uint2(tl.v[i].x & m0, tl.v[i].y & m1);
     }
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) oacc[i] = mma(DT(), widen8<DT>(tl.v[i].x, tl.v[i].y), pop, oacc[i]);
+    for (int i = 0; i < NDT; ++i) oacc[i] = mma(DT(), widen8<DT, CODE>(tl.v[i].x, tl.v[i].y), pop, oacc[i]);
   };
 
   // Computes of tiles past the end are not skipped (see attention_gqa.hip).
@@ -244,41 +245,51 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   }
 }
 
-template <class DT, int D, int BS>
+template <class DT, int D, int BS, int CODE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void fp8_grid_kernel(DecodeArgs a, int G) {
   const int Hkv = a.num_kv_heads;
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
   const uint4 it = a.items[t / Hkv];
-  fp8_item<DT, D, BS>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.w),
+  fp8_item<DT, D, BS, CODE>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.w),
                       int(it.y >> 8));
 }
 
-template <class DT, int D, int BS>
+template <class DT, int D, int BS, int CODE>
 hipError_t launch_t(const DecodeArgs& a, int group, hipStream_t stream) {
   hipError_t e = launch_plan(a, BS, 16 / group, stream);
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.slots;
-  hipLaunchKernelGGL((fp8_grid_kernel<DT, D, BS>), dim3((unsigned)grid), dim3(64), 0, stream, a,
+  hipLaunchKernelGGL((fp8_grid_kernel<DT, D, BS, CODE>), dim3((unsigned)grid), dim3(64), 0, stream, a,
                      group);
   return hipGetLastError();
 }
 
-template <class DT, int D>
+template <class DT, int D, int CODE>
 hipError_t by_block(const DecodeArgs& a, int bs, int group, hipStream_t s) {
   switch (bs) {
-    case 8: return launch_t<DT, D, 8>(a, group, s);
-    case 16: return launch_t<DT, D, 16>(a, group, s);
-    case 32: return launch_t<DT, D, 32>(a, group, s);
+    case 8: return launch_t<DT, D, 8, CODE>(a, group, s);
+    case 16: return launch_t<DT, D, 16, CODE>(a, group, s);
+    case 32: return launch_t<DT, D, 32, CODE>(a, group, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <class DT>
+template <class DT, int CODE>
 hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s) {
   switch (D) {
-    case 64: return by_block<DT, 64>(a, bs, group, s);
-    case 128: return by_block<DT, 128>(a, bs, group, s);
+    case 64: return by_block<DT, 64, CODE>(a, bs, group, s);
+    case 128: return by_block<DT, 128, CODE>(a, bs, group, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int CODE>
+hipError_t by_dtype(const DecodeArgs& a, int dtype, int head_size, int block_size, int group,
+                    hipStream_t stream) {
+  switch (dtype) {
+    case 1: return by_head<F16, CODE>(a, head_size, block_size, group, stream);
+    case 2: return by_head<BF16, CODE>(a, head_size, block_size, group, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -287,11 +298,12 @@ hipError_t by_head(const DecodeArgs& a, int D, int bs, int group, hipStream_t s)
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int dtype, int head_size, int block_size,
                              int group, hipStream_t stream) {
-  switch (dtype) {
-    case 1: return by_head<F16>(a, head_size, block_size, group, stream);
-    case 2: return by_head<BF16>(a, head_size, block_size, group, stream);
-  }
-  return hipErrorInvalidValue;
+  return by_dtype<kCodeE4M3>(a, dtype, head_size, block_size, group, stream);
+}
+
+hipError_t launch_decode_i8(const DecodeArgs& a, int dtype, int head_size, int block_size,
+                            int group, hipStream_t stream) {
+  return by_dtype<kCodeI8>(a, dtype, head_size, block_size, group, stream);
 }
 
 }  // namespace pkv

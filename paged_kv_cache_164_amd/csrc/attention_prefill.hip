@@ -32,7 +32,7 @@
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_prefill.h"
-#include "pkv_fp8.h"
+#include "pkv_kv8.h"
 
 #include <type_traits>
 
@@ -152,8 +152,9 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------------------
 // Attention: NW waves x CB blocks of 16 columns = 256 columns per workgroup.
 // ---------------------------------------------------------------------------------------
-template <class DT, int D, int BS, int NW, int CB, bool KV8>
+template <class DT, int D, int BS, int NW, int CB, int KVC>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
+  constexpr bool KV8 = KVC != 0;  // KVC: 0 a 16-bit cache, else the 8-bit code format
   static_assert(NW * CB * 16 == kPrefillColumns, "columns per workgroup");
   static_assert(BS == 8 || BS == 16 || BS == 32, "a 32-key stage holds whole blocks");
   constexpr int NT = NW * 64;
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using Raw = typename std::conditional<KV8, uint2, uint4>::type;
   Raw kA[PPT], vA[PPT], kB[PPT], vB[PPT];
   auto widen = [&](const Raw& r) -> uint4 {
-    if constexpr (KV8) return widen8<DT>(r.x, r.y);
+    if constexpr (KV8) return widen8<DT, KVC>(r.x, r.y);
     else return r;
   };
   auto load_stage = [&](int s, Raw* kst, Raw* vst) {
@@ -486,30 +487,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <class DT, int D, int BS, bool KV8>
+template <class DT, int D, int BS, int KVC>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   constexpr int NW = 8, CB = 2;
   const int64_t grid = a.capacity * a.num_kv_heads;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, NW, CB, KV8>), dim3((unsigned)grid), dim3(NW * 64),
+  hipLaunchKernelGGL((prefill_kernel<DT, D, BS, NW, CB, KVC>), dim3((unsigned)grid), dim3(NW * 64),
                      0, stream, a);
   return hipGetLastError();
 }
 
-template <class DT, int D, bool KV8>
+template <class DT, int D, int KVC>
 hipError_t by_block(const PrefillArgs& a, int bs, hipStream_t s) {
   switch (bs) {
-    case 8: return launch_t<DT, D, 8, KV8>(a, s);
-    case 16: return launch_t<DT, D, 16, KV8>(a, s);
-    case 32: return launch_t<DT, D, 32, KV8>(a, s);
+    case 8: return launch_t<DT, D, 8, KVC>(a, s);
+    case 16: return launch_t<DT, D, 16, KVC>(a, s);
+    case 32: return launch_t<DT, D, 32, KVC>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <class DT, bool KV8>
+template <class DT, int KVC>
 hipError_t by_head(const PrefillArgs& a, int D, int bs, hipStream_t s) {
   switch (D) {
-    case 64: return by_block<DT, 64, KV8>(a, bs, s);
-    case 128: return by_block<DT, 128, KV8>(a, bs, s);
+    case 64: return by_block<DT, 64, KVC>(a, bs, s);
+    case 128: return by_block<DT, 128, KVC>(a, bs, s);
   }
   return hipErrorInvalidValue;
 }
@@ -522,16 +523,26 @@ bool prefill_supported(int dtype, int head_size, int block_size, int group) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, const DecodeArgs& red, int dtype, int head_size,
-                          int block_size, bool kv8, hipStream_t stream) {
+                          int block_size, int kv_code, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (kv8)
-    e = (dtype == 1) ? by_head<F16, true>(a, head_size, block_size, stream)
-                     : by_head<BF16, true>(a, head_size, block_size, stream);
-  else
-    e = (dtype == 1) ? by_head<F16, false>(a, head_size, block_size, stream)
-                     : by_head<BF16, false>(a, head_size, block_size, stream);
+  switch (kv_code) {
+    case 0:
+      e = (dtype == 1) ? by_head<F16, 0>(a, head_size, block_size, stream)
+                       : by_head<BF16, 0>(a, head_size, block_size, stream);
+      break;
+    case kCodeE4M3:
+      e = (dtype == 1) ? by_head<F16, kCodeE4M3>(a, head_size, block_size, stream)
+                       : by_head<BF16, kCodeE4M3>(a, head_size, block_size, stream);
+      break;
+    case kCodeI8:
+      e = (dtype == 1) ? by_head<F16, kCodeI8>(a, head_size, block_size, stream)
+                       : by_head<BF16, kCodeI8>(a, head_size, block_size, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   if (e != hipSuccess || a.slots <= 1) return e;
   return launch_reduce(red, dtype, head_size, stream);
 }

@@ -10,6 +10,8 @@
 // for each (src, dst) copy-on-write pair.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_kv8.h"
+#include "pkv_kv8_host.h"
 
 namespace pkv {
 namespace {
@@ -132,9 +134,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
   }
 }
 
-// The same scatter into an 8-bit cache (FP8 E4M3, x = 16): each new element of the model's
-// 16-bit type is quantised as code = E4M3(clamp(x / scale, -448, 448)), the division rounded
-// to float32 and the conversion to nearest, ties to even (a NaN stays NaN).
+// The same scatter into an 8-bit cache (x = 16): each new element of the model's 16-bit type is
+// quantised with its cache's scale, the division x / scale rounded to float32, then
+//   E4M3: code = E4M3(clamp(x / scale, -448, 448)), to nearest, ties to even (NaN stays NaN);
+//   INT8: code = clamp(x / scale, -127, 127) rounded to the nearest integer, ties to even
+//         (NaN gives 0).
 __device__ __forceinline__ float widen16(F16, uint16_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, b));
 }
@@ -143,13 +147,22 @@ __device__ __forceinline__ float to_e4m3_range(float x, float scale) {
   const float y = __fdiv_rn(x, scale);
   return (y != y) ? y : fminf(fmaxf(y, -448.f), 448.f);
 }
+__device__ __forceinline__ uint32_t to_i8(float x, float scale) {
+  const float y = __fdiv_rn(x, scale);
+  if (y != y) return 0u;
+  return uint32_t(static_cast<int>(rintf(fminf(fmaxf(y, -127.f), 127.f)))) & 0xffu;
+}
 // two codes, in the low 16 bits (byte 0 = first)
+template <int CODE>
 __device__ __forceinline__ uint32_t quant2(float x0, float x1, float scale) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(to_e4m3_range(x0, scale), to_e4m3_range(x1, scale), 0,
-                                         false) & 0xffffu;
+  if constexpr (CODE == kCodeE4M3)
+    return __builtin_amdgcn_cvt_pk_fp8_f32(to_e4m3_range(x0, scale), to_e4m3_range(x1, scale), 0,
+                                           false) & 0xffffu;
+  else
+    return to_i8(x0, scale) | (to_i8(x1, scale) << 8);
 }
 
-template <class IN>
+template <class IN, int CODE>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
@@ -175,15 +188,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint16_t* e = krow + (int64_t)c * 16 + 4 * k;
-      w[k] = quant2(widen16(IN(), e[0]), widen16(IN(), e[1]), k_scale) |
-             (quant2(widen16(IN(), e[2]), widen16(IN(), e[3]), k_scale) << 16);
+      w[k] = quant2<CODE>(widen16(IN(), e[0]), widen16(IN(), e[1]), k_scale) |
+             (quant2<CODE>(widen16(IN(), e[2]), widen16(IN(), e[3]), k_scale) << 16);
     }
     *reinterpret_cast<uint4*>(kdst + h * tile + ((int64_t)cc * block_size + off) * 16) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
   // values: one byte per element, two elements per conversion
   for (int e = 2 * threadIdx.x; e < n; e += 2 * blockDim.x) {
-    const uint32_t q = quant2(widen16(IN(), vrow[e]), widen16(IN(), vrow[e + 1]), v_scale);
+    const uint32_t q = quant2<CODE>(widen16(IN(), vrow[e]), widen16(IN(), vrow[e + 1]), v_scale);
     const int h = e / D, d = e % D;
     vdst[h * tile + (int64_t)d * block_size + off] = uint8_t(q & 0xff);
     vdst[h * tile + (int64_t)(d + 1) * block_size + off] = uint8_t(q >> 8);
@@ -258,16 +271,15 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
   return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
-                                        void* value_cache, const int64_t* slot_mapping,
-                                        int num_tokens, int num_kv_heads, int head_size,
-                                        int block_size, int64_t num_blocks, int64_t key_stride,
-                                        int64_t value_stride, int dtype, float k_scale,
-                                        float v_scale, hipStream_t stream) {
+template <int CODE>
+hipError_t launch_rc8(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_size,
+                      int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                      int dtype, float k_scale, float v_scale, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const dim3 grid(num_tokens), block(256);
 #define PKV_RC8(IN)                                                                             \
-  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<IN>), grid, block, 0, stream,                \
+  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<IN, CODE>), grid, block, 0, stream,          \
                      static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),    \
                      static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),      \
                      slot_mapping, num_kv_heads, head_size, block_size, num_blocks, key_stride, \
@@ -275,6 +287,28 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
   if (dtype == 1) PKV_RC8(F16); else PKV_RC8(BF16);
 #undef PKV_RC8
   return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                        void* value_cache, const int64_t* slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_size,
+                                        int block_size, int64_t num_blocks, int64_t key_stride,
+                                        int64_t value_stride, int dtype, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+  return launch_rc8<kCodeE4M3>(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                               num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                               value_stride, dtype, k_scale, v_scale, stream);
+}
+
+hipError_t launch_reshape_and_cache_i8(const void* key, const void* value, void* key_cache,
+                                       void* value_cache, const int64_t* slot_mapping,
+                                       int num_tokens, int num_kv_heads, int head_size,
+                                       int block_size, int64_t num_blocks, int64_t key_stride,
+                                       int64_t value_stride, int dtype, float k_scale,
+                                       float v_scale, hipStream_t stream) {
+  return launch_rc8<kCodeI8>(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                             num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                             value_stride, dtype, k_scale, v_scale, stream);
 }
 
 hipError_t launch_copy_blocks(const uint64_t* key_ptrs, const uint64_t* value_ptrs, int num_layers,

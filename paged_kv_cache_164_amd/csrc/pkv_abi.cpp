@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "pkv_internal.h"
+#include "pkv_kv8_host.h"
 #include "pkv_prefill.h"
 #include "pkv_probe.h"
 
@@ -44,12 +45,13 @@ struct Resolved {
   int group;
   int block_size;
   bool use_mfma;
-  bool kv8;
+  int kv_code;  // 0: 16/32-bit cache, else pkv::kCodeE4M3 or pkv::kCodeI8
 };
 
-// Scales of an 8-bit (FP8 E4M3) cache; null for 16/32-bit caches.
+// Code format and scales of an 8-bit cache; null for 16/32-bit caches.
 struct Kv8 {
   float k_scale, v_scale;
+  int code;  // pkv::kCodeE4M3 or pkv::kCodeI8
 };
 
 // Prefix groups of the shared-prefix decode (null for the plain decode).
@@ -166,13 +168,16 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
   r->group = group;
   r->block_size = block_size;
   r->use_mfma = use_mfma;
-  r->kv8 = kv8 != nullptr;
+  r->kv_code = kv8 ? kv8->code : 0;
   return PKV_OK;
 }
 
 int launch_phase1(const Resolved& r, int dtype, int head_size, int block_size, hipStream_t s) {
   if (r.args.num_seqs == 0) return PKV_OK;
-  hipError_t e = r.kv8 ? pkv::launch_decode_fp8(r.args, dtype, head_size, block_size, r.group, s)
+  hipError_t e = r.kv_code == pkv::kCodeE4M3
+      ? pkv::launch_decode_fp8(r.args, dtype, head_size, block_size, r.group, s)
+      : r.kv_code == pkv::kCodeI8
+      ? pkv::launch_decode_i8(r.args, dtype, head_size, block_size, r.group, s)
       : r.use_mfma
       ? pkv::launch_decode_gqa(r.args, dtype, head_size, block_size, r.group, s)
       : pkv::launch_decode_valu(r.args, dtype, head_size, block_size, r.group, s);
@@ -297,8 +302,8 @@ static int prefill_call(void* out, const void* query, const void* key_cache,
     red.num_heads = num_heads;
     red.num_kv_heads = num_kv_heads;
     red.slots = a.slots;
-    const hipError_t e = pkv::launch_prefill(a, red, dtype, head_size, block_size, kv8 != nullptr,
-                                             static_cast<hipStream_t>(stream));
+    const hipError_t e = pkv::launch_prefill(a, red, dtype, head_size, block_size,
+                                             kv8 ? kv8->code : 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PKV_OK : hip_fail(e, "multi-query attention launch");
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
@@ -362,15 +367,14 @@ int pkv_paged_attention_decode_shared(
   }
 }
 
-int pkv_paged_attention_decode_fp8(
-    void* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
-    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+static int decode_kv8(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      const Kv8& kv8, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,
+                      int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   try {
     Resolved r;
-    const Kv8 kv8{k_scale, v_scale};
     int rc = resolve_decode(PKV_DECODE_ARGS, &r, nullptr, &kv8);
     if (rc != PKV_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -380,6 +384,27 @@ int pkv_paged_attention_decode_fp8(
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+#define PKV_DECODE_KV8_PARAMS                                                                   \
+  void *out, const void *query, const void *key_cache, const void *value_cache,                 \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, float k_scale,     \
+      float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,                 \
+      int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,                    \
+      int32_t max_context_len, int32_t dtype, int32_t partition_size, void *workspace,          \
+      size_t workspace_bytes, void *stream
+#define PKV_DECODE_KV8_CALL(CODE)                                                               \
+  decode_kv8(out, query, key_cache, value_cache, block_tables, context_lens, scale,             \
+             Kv8{k_scale, v_scale, CODE}, num_seqs, num_heads, num_kv_heads, head_size,         \
+             block_size, max_num_blocks_per_seq, max_context_len, dtype, partition_size,        \
+             workspace, workspace_bytes, stream)
+
+int pkv_paged_attention_decode_fp8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeE4M3);
+}
+
+int pkv_paged_attention_decode_int8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeI8);
 }
 
 int pkv_paged_attention_partitions(PKV_DECODE_PARAMS) {
@@ -462,7 +487,23 @@ int pkv_paged_attention_prefill_fp8(void* out, const void* query, const void* ke
                                     int32_t max_num_blocks_per_seq, int32_t max_context_len,
                                     int32_t dtype, int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  const Kv8 kv8{k_scale, v_scale};
+  const Kv8 kv8{k_scale, v_scale, pkv::kCodeE4M3};
+  return prefill_call(out, query, key_cache, value_cache, block_tables, context_lens,
+                      query_start_loc, scale, &kv8, num_seqs, num_tokens, num_heads,
+                      num_kv_heads, head_size, block_size, max_num_blocks_per_seq,
+                      max_context_len, dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attention_prefill_int8(void* out, const void* query, const void* key_cache,
+                                     const void* value_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* query_start_loc,
+                                     float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t block_size,
+                                     int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                     int32_t dtype, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const Kv8 kv8{k_scale, v_scale, pkv::kCodeI8};
   return prefill_call(out, query, key_cache, value_cache, block_tables, context_lens,
                       query_start_loc, scale, &kv8, num_seqs, num_tokens, num_heads,
                       num_kv_heads, head_size, block_size, max_num_blocks_per_seq,
@@ -508,11 +549,12 @@ int pkv_reshape_and_cache(const void* key, const void* value, void* key_cache, v
   }
 }
 
-int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
-                              void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
-                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                              int64_t num_blocks, int64_t key_stride, int64_t value_stride,
-                              int32_t dtype, float k_scale, float v_scale, void* stream) {
+static int reshape_and_cache_kv8(const void* key, const void* value, void* key_cache,
+                                 void* value_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t block_size, int64_t num_blocks, int64_t key_stride,
+                                 int64_t value_stride, int32_t dtype, float k_scale, float v_scale,
+                                 int code, void* stream) {
   try {
     if (dtype != PKV_F16 && dtype != PKV_BF16)
       return fail(PKV_ERR_INVALID_ARG, "key and value must be PKV_F16 or PKV_BF16");
@@ -528,14 +570,35 @@ int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cach
       return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
     if (reinterpret_cast<uintptr_t>(key_cache) % 16 != 0)
       return fail(PKV_ERR_INVALID_ARG, "key_cache must be 16-byte aligned");
-    hipError_t e = pkv::launch_reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping,
-                                                     num_tokens, num_kv_heads, head_size, block_size,
-                                                     num_blocks, key_stride, value_stride, dtype,
-                                                     k_scale, v_scale, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? PKV_OK : hip_fail(e, "reshape_and_cache_fp8 launch");
+    auto* launch = code == pkv::kCodeE4M3 ? pkv::launch_reshape_and_cache_fp8
+                                          : pkv::launch_reshape_and_cache_i8;
+    hipError_t e = launch(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                          num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                          value_stride, dtype, k_scale, v_scale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "8-bit reshape_and_cache launch");
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+int pkv_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                              void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                              int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                              int32_t dtype, float k_scale, float v_scale, void* stream) {
+  return reshape_and_cache_kv8(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                               num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                               value_stride, dtype, k_scale, v_scale, pkv::kCodeE4M3, stream);
+}
+
+int pkv_reshape_and_cache_int8(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int64_t num_blocks, int64_t key_stride, int64_t value_stride,
+                               int32_t dtype, float k_scale, float v_scale, void* stream) {
+  return reshape_and_cache_kv8(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                               num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                               value_stride, dtype, k_scale, v_scale, pkv::kCodeI8, stream);
 }
 
 int pkv_copy_blocks(const uint64_t* key_cache_ptrs, const uint64_t* value_cache_ptrs,

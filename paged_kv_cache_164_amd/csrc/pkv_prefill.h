@@ -68,9 +68,10 @@ inline PrefillLayout prefill_layout(int num_seqs, int num_tokens, int num_heads,
   return w;
 }
 bool prefill_supported(int dtype, int head_size, int block_size, int group);
-// plan + attention kernel (+ the split-K reduce, given as `red`, when a.slots > 1); kv8: the
-// caches hold E4M3 codes (uint8), queries and output stay 16-bit (dtype)
+// plan + attention kernel (+ the split-K reduce, given as `red`, when a.slots > 1); kv_code: 0
+// for a 16-bit cache, else the caches hold 8-bit codes (1: E4M3, 2: INT8) and queries and output
+// stay 16-bit (dtype)
 hipError_t launch_prefill(const PrefillArgs& a, const DecodeArgs& red, int dtype, int head_size,
-                          int block_size, bool kv8, hipStream_t stream);
+                          int block_size, int kv_code, hipStream_t stream);
 
 }  // namespace pkv

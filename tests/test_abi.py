@@ -25,7 +25,7 @@ def test_exports_every_header_symbol():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         declared |= set(re.findall(r"\b(pkv_\w+)\s*\(", open(h).read()))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 30
+    assert len(declared) == 33
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -196,3 +196,49 @@ def test_prefill_nothing_to_do():
     lib = _lib()
     assert _prefill(lib, num_tokens=0) == 0
     assert _prefill(lib, num_seqs=0, num_tokens=0) == 0
+
+
+@pytest.mark.parametrize("entry", ["pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_int8"])
+@pytest.mark.parametrize("over,code", [
+    (dict(k_scale=0.0), -1),
+    (dict(v_scale=float("nan")), -1),
+    (dict(k_scale=float("inf")), -1),
+    (dict(dtype=0), -2),                  # the queries of an 8-bit cache are 16-bit
+    (dict(head_size=96), -2),
+    (dict(query=None), -3),
+])
+def test_kv8_decode_argument_errors(entry, over, code):
+    lib = _lib()
+    args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
+                scale=0.125, k_scale=0.02, v_scale=0.03, num_seqs=2, num_heads=8, num_kv_heads=2,
+                head_size=128, block_size=16, max_blocks=4, max_context_len=64, dtype=2,
+                partition_size=0, workspace=None, ws_bytes=0, stream=None)
+    args.update(over)
+    assert getattr(lib, entry)(*args.values()) == code
+    assert lib.pkv_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("entry", ["pkv_paged_attention_prefill_fp8", "pkv_paged_attention_prefill_int8"])
+def test_kv8_prefill_argument_errors(entry):
+    lib = _lib()
+    base = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
+                query_start_loc=1, scale=0.125, k_scale=0.02, v_scale=0.03, num_seqs=2,
+                num_tokens=10, num_heads=8, num_kv_heads=2, head_size=128, block_size=16,
+                max_blocks=4, max_context_len=64, dtype=2, partition_size=0, workspace=None,
+                ws_bytes=0, stream=None)
+    for over, code in [(dict(k_scale=-1.0), -1), (dict(v_scale=0.0), -1), (dict(dtype=0), -2),
+                       (dict(), -4)]:
+        args = dict(base, **over)
+        assert getattr(lib, entry)(*args.values()) == code, over
+
+
+@pytest.mark.parametrize("entry", ["pkv_reshape_and_cache_fp8", "pkv_reshape_and_cache_int8"])
+def test_kv8_cache_write_argument_errors(entry):
+    lib = _lib()
+    f = getattr(lib, entry)
+    #               key value kc vc slots N  H  D   bs NB  kstr vstr dtype ks    vs    stream
+    assert f(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 128, 0, 0.02, 0.03, None) == -1   # fp32 input
+    assert f(1, 1, 1, 1, 1, 4, 2, 40, 16, 10, 128, 128, 2, 0.02, 0.03, None) == -1   # D % 16
+    assert f(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 128, 2, 0.0, 0.03, None) == -1    # scale 0
+    assert f(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 100, 2, 0.02, 0.03, None) == -1   # stride
+    assert f(None, None, None, None, None, 0, 2, 64, 16, 10, 128, 128, 2, 0.02, 0.03, None) == 0

@@ -1,5 +1,5 @@
-"""GPU parity of the 8-bit (FP8 E4M3) KV cache through the C ABI: the cache write is compared
-bit for bit with the oracle's quantisation, decode against the fp64 oracle over the
+"""GPU parity of the 8-bit KV cache (FP8 E4M3 and INT8 codes) through the C ABI: the cache write
+is compared bit for bit with the oracle's quantisation, decode against the fp64 oracle over the
 dequantised codes (spec tolerance for the 16-bit output)."""
 import numpy as np
 import pytest
@@ -9,9 +9,14 @@ import paged_kv_cache_164_amd as pkv
 from gpu_cases import DEV, log, within_tolerance
 from oracle import attention as OA
 from oracle import cache_ops as OC
-from workloads import draw_normal, make_decode_case, storage_bits, with_fp8_cache
+from workloads import draw_normal, make_decode_case, storage_bits, with_8bit_cache
 
 pytestmark = pytest.mark.gpu
+CODES = ["e4m3", "i8"]
+
+
+def _oracle_write(code):
+    return OC.reshape_and_cache_fp8 if code == "e4m3" else OC.reshape_and_cache_int8
 
 
 def _decode(case, P=0):
@@ -19,11 +24,12 @@ def _decode(case, P=0):
     q = case.query.to(DEV)
     kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
     pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
-                              case.slot_mapping.to(DEV), case.k_scale, case.v_scale)
+                              case.slot_mapping.to(DEV), case.k_scale, case.v_scale,
+                              code=case.kv_dtype)
     out = torch.full_like(q, float("nan"))
     pkv.paged_attention_decode_fp8(out, q, kc, vc, case.block_tables.to(DEV),
                                    case.context_lens.to(DEV), case.scale, case.k_scale,
-                                   case.v_scale, case.max_context_len, P)
+                                   case.v_scale, case.max_context_len, P, code=case.kv_dtype)
     torch.cuda.synchronize()
     return out
 
@@ -31,11 +37,13 @@ def _decode(case, P=0):
 def _oracle(case, pairs=None):
     """The step in the oracle: the new tokens quantised into a copy of the cache, then decode."""
     kb, vb = case.key_cache.numpy().copy(), case.value_cache.numpy().copy()
-    OC.reshape_and_cache_fp8(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
-                             case.cfg.dtype, case.slot_mapping.numpy(), case.k_scale, case.v_scale)
+    _oracle_write(case.kv_dtype)(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
+                                 case.cfg.dtype, case.slot_mapping.numpy(), case.k_scale,
+                                 case.v_scale)
     return OA.paged_decode(storage_bits(case.query), kb, vb, case.cfg.dtype,
                            case.block_tables.numpy(), case.context_lens.numpy(), case.scale,
-                           pairs=pairs, kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+                           pairs=pairs, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
+                           v_scale=case.v_scale)
 
 
 def _check(case, got, ref, tag, pairs=None):
@@ -49,9 +57,10 @@ def _check(case, got, ref, tag, pairs=None):
     return got
 
 
+@pytest.mark.parametrize("code", CODES)
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_reshape_and_cache_fp8_bit_exact(dtype):
-    case = with_fp8_cache(make_decode_case("c3", num_seqs=4, len_cap=200, dtype=dtype))
+def test_reshape_and_cache_kv8_bit_exact(dtype, code):
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=4, len_cap=200, dtype=dtype), code)
     N, Hkv, D = 37, case.key_cache.shape[1], case.query.shape[2]
     key = draw_normal((N, Hkv, D), dtype, 77, 1) * 3
     val = draw_normal((N, Hkv, D), dtype, 77, 2) * 3
@@ -62,21 +71,22 @@ def test_reshape_and_cache_fp8_bit_exact(dtype):
                      replace=False).astype(np.int64)
     slots[[3, 11]] = -1
     kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
-    log(f"reshape fp8 {dtype} N={N}")
+    log(f"reshape {code} {dtype} N={N}")
     pkv.reshape_and_cache_fp8(key.to(DEV), val.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV),
-                              case.k_scale, case.v_scale)
+                              case.k_scale, case.v_scale, code=code)
     torch.cuda.synchronize()
     kb, vb = case.key_cache.numpy().copy(), case.value_cache.numpy().copy()
-    OC.reshape_and_cache_fp8(kb, vb, storage_bits(key), storage_bits(val), dtype, slots,
-                             case.k_scale, case.v_scale)
+    _oracle_write(code)(kb, vb, storage_bits(key), storage_bits(val), dtype, slots,
+                        case.k_scale, case.v_scale)
     assert np.array_equal(kc.cpu().numpy(), kb)
     assert np.array_equal(vc.cpu().numpy(), vb)
 
 
-def test_fp8_step_c3_small():
-    """reshape_and_cache_fp8 of the step's new tokens, then decode, against the oracle."""
-    case = with_fp8_cache(make_decode_case("c3", num_seqs=12))
-    _check(case, _decode(case), _oracle(case), "fp8 step c3")
+@pytest.mark.parametrize("code", CODES)
+def test_kv8_step_c3_small(code):
+    """The 8-bit cache write of the step's new tokens, then decode, against the oracle."""
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=12), code)
+    _check(case, _decode(case), _oracle(case), f"{code} step c3")
 
 
 @pytest.mark.parametrize("dtype,D,bs,heads,P", [
@@ -84,32 +94,35 @@ def test_fp8_step_c3_small():
     ("f16", 128, 32, (16, 2), 256), ("bf16", 128, 16, (16, 1), 16), ("f16", 64, 32, (12, 4), 2048),
     ("bf16", 128, 8, (40, 8), 1024), ("bf16", 128, 16, (32, 8), 4096), ("f16", 128, 32, (8, 2), 0),
 ])
-def test_fp8_decode_shapes(dtype, D, bs, heads, P):
+@pytest.mark.parametrize("code", CODES)
+def test_kv8_decode_shapes(dtype, D, bs, heads, P, code):
     lens = [0, 1, 31, 32, 33, 63, 64, 65, 300, 511, 512, 513, 1500, 2047, 2048, 2049, 2600,
             4095, 4096, 4097, 6200]
-    case = with_fp8_cache(make_decode_case("c3", lens=lens, dtype=dtype, head_size=D,
-                                           block_size=bs, num_heads=heads[0],
-                                           num_kv_heads=heads[1]))
-    tag = f"fp8 {dtype} D={D} bs={bs} {heads} P={P}"
+    case = with_8bit_cache(make_decode_case("c3", lens=lens, dtype=dtype, head_size=D,
+                                            block_size=bs, num_heads=heads[0],
+                                            num_kv_heads=heads[1]), code)
+    tag = f"{code} {dtype} D={D} bs={bs} {heads} P={P}"
     log(tag)
     got = _check(case, _decode(case, P), _oracle(case), tag)
     assert np.all(got[0] == 0.0)
 
 
+@pytest.mark.parametrize("code", CODES)
 @pytest.mark.parametrize("key", ["c3", "c4"])
-def test_fp8_full_size_sampled(key):
-    case = with_fp8_cache(make_decode_case(key))
+def test_kv8_full_size_sampled(key, code):
+    case = with_8bit_cache(make_decode_case(key), code)
     lens = case.context_lens.numpy()
     B, H = case.query.shape[:2]
     g = np.random.default_rng(1)
     pairs = sorted({(int(np.argmax(lens)), 0), (int(np.argmin(lens)), H - 1)} |
                    {(int(g.integers(B)), int(g.integers(H))) for _ in range(40)})
-    log(f"fp8 full {key} B={B}")
-    _check(case, _decode(case), _oracle(case, pairs=pairs), f"fp8 full {key}", pairs)
+    log(f"{code} full {key} B={B}")
+    _check(case, _decode(case), _oracle(case, pairs=pairs), f"{code} full {key}", pairs)
 
 
-def test_fp8_run_to_run_bit_determinism():
-    case = with_fp8_cache(make_decode_case("c3", num_seqs=32))
+@pytest.mark.parametrize("code", CODES)
+def test_kv8_run_to_run_bit_determinism(code):
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=32), code)
     a = _decode(case)
     b = _decode(case)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -145,33 +145,38 @@ def test_full_chunked_prefill_workload_sampled(P):
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("code", ["e4m3", "i8"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [0, 2, 3])
 @pytest.mark.parametrize("P", [0, 96])
-def test_fp8_cache_mixed_batch_matches_oracle(dtype, shape, P):
-    """The multi-query call over an 8-bit (E4M3) cache: the chunk quantised into the cache by
-    reshape_and_cache_fp8 (bit-exact), then attention against the oracle over the codes."""
+def test_kv8_cache_mixed_batch_matches_oracle(dtype, shape, P, code):
+    """The multi-query call over an 8-bit cache (E4M3 or INT8 codes): the chunk quantised into
+    the cache by the 8-bit cache write (bit-exact), then attention against the oracle over the
+    codes."""
     from oracle import cache_ops as OC8
-    from workloads import with_fp8_cache
+    from workloads import with_8bit_cache
     kw = SHAPES[shape]
-    log(f"prefill fp8 mixed {dtype} {kw} P={P}")
-    case = with_fp8_cache(make_prefill_case(MIXED, dtype=dtype, seed=400 + shape, **kw))
+    log(f"prefill {code} mixed {dtype} {kw} P={P}")
+    case = with_8bit_cache(make_prefill_case(MIXED, dtype=dtype, seed=400 + shape, **kw), code)
     kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
     pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
-                              torch.from_numpy(case.slot_mapping).to(DEV), case.k_scale, case.v_scale)
+                              torch.from_numpy(case.slot_mapping).to(DEV), case.k_scale, case.v_scale,
+                              code=code)
     q = case.query.to(DEV)
     out = torch.full_like(q, float("nan"))
     pkv.paged_attention_prefill(out, q, kc, vc, torch.from_numpy(case.block_tables).to(DEV),
                                 torch.from_numpy(case.context_lens).to(DEV),
                                 torch.from_numpy(case.query_start_loc).to(DEV), case.scale,
-                                case.max_context_len, P, k_scale=case.k_scale, v_scale=case.v_scale)
+                                case.max_context_len, P, k_scale=case.k_scale, v_scale=case.v_scale,
+                                code=code)
     torch.cuda.synchronize()
     kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
-    OC8.reshape_and_cache_fp8(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
-                              dtype, case.slot_mapping, case.k_scale, case.v_scale)
+    write = OC8.reshape_and_cache_fp8 if code == "e4m3" else OC8.reshape_and_cache_int8
+    write(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value), dtype,
+          case.slot_mapping, case.k_scale, case.v_scale)
     assert np.array_equal(kc.cpu().numpy(), kb) and np.array_equal(vc.cpu().numpy(), vb)
     ref = OP.chunked_prefill(storage_bits(case.query), kb, vb, dtype, case.block_tables,
                              case.context_lens, case.query_start_loc, case.scale,
-                             kv_dtype="e4m3", k_scale=case.k_scale, v_scale=case.v_scale)
+                             kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
     ok, err, ratio = within_tolerance(_as_f64(out), ref, dtype)
     assert ok, f"max err {err}, worst ratio {ratio}"
