@@ -560,7 +560,8 @@ def main() -> int:
     step_bytes = dec_bytes + write_bytes
     gbs = step_bytes / (ms_step / 1e3) / 1e9
     kernel_gbs = dec_bytes / (k_avg / 1e3) / 1e9
-    traffic = traffic_from_profile(args.workload)
+    # the stored counters were taken on the 16-bit cache's partition kernel
+    traffic = None if kv8 else traffic_from_profile(args.workload)
     rec = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) and KV-tokens/s, 1 GPU",
         "value": round(gbs, 2),
