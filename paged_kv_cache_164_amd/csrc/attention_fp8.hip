@@ -8,11 +8,14 @@
 // so no per-element multiply is spent on them.
 //
 // Same work items, scheduling, online softmax and epilogue as the 16-bit kernel
-// (attention_gqa.hip), with 32-token tiles so that the P.V product is a 16x16x32 MFMA fed by
-// 8-byte value loads:
-//   * key rows are permuted: row i of row group r (r = 0, 1) is tile token
-//     8 * (i / 4) + 4 * r + i % 4, so after the two 16x16x32 logit products lane l holds the
-//     logits of tokens 8 * (l / 16) .. + 8 of its column -- exactly the B operand of the
+// (attention_gqa.hip), with 32-token tiles so that the P.V product is a 16x16x32 MFMA:
+//   * row i of key row group r (r = 0, 1) is tile token 16 r + i, so the 16 lanes of a key
+//     load read 16 consecutive tokens: whole 128-byte lines of the [D/16][bs][16] chunk (a
+//     permuted order reading 4-token pieces cost 5% in a load-only probe);
+//   * after the two 16x16x32 logit products lane (col, quad) holds the logits of tokens
+//     4 quad .. + 4 (group 0) and 16 + 4 quad .. + 4 (group 1) of its column; two lane swaps
+//     (v_permlane32_swap, then v_permlane16_swap, per dword of packed weights) regroup them so
+//     that lane (col, quad) holds the weights of tokens 8 quad .. + 8 -- the B operand of the
 //     16x16x32 P.V product, whose A operand (lane: one head dim, 8 consecutive tokens) is
 //     one 8-byte load of a value row;
 //   * a lane loads 16 dims of a key row at once (one 16-byte chunk); the two halves feed two
@@ -110,8 +113,10 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
     return (j < 128) ? ((j < 64) ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r))
                      : ((j < 192) ? __builtin_amdgcn_readlane(ids2, r) : __builtin_amdgcn_readlane(ids3, r));
   };
-  // this lane's tokens within a tile: key rows of the two row groups, and 8 value tokens
-  const int ktok0 = 8 * (col / 4) + (col % 4), ktok1 = ktok0 + 4;
+  // this lane's tokens within a tile: key rows of the two row groups, the two 4-token runs of
+  // its logits, and the 8 tokens of its value operand
+  const int ktok0 = col, ktok1 = 16 + col;
+  const int stok0 = 4 * quad, stok1 = 16 + 4 * quad;
   const int vtok = 8 * quad;
   struct Tile {
     uint4 k[2][KJ];
@@ -123,16 +128,23 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   // tiles past the last one read the prefetch pad.
   auto load_tile = [&](int t0, Tile& tl) {
     const int j0 = t0 / BS;
-    int64_t cand[NBT];
+    int cand[NBT];
 #pragma unroll
-    for (int k = 0; k < NBT; ++k) cand[k] = block_of(j0 + k);
+    for (int k = 0; k < NBT; ++k) cand[k] = int(block_of(j0 + k));
     // A lane whose token lies past the item's last block (a tile can reach beyond it) reads
-    // block 0 instead: table entries there are not block ids; its data is masked.
-    auto pick = [&](int t) {
-      int64_t r = cand[0];
-#pragma unroll
-      for (int k = 1; k < NBT; ++k) r = (t / BS == k) ? cand[k] : r;
-      return (t0 + t < nslots) ? r : int64_t(0);
+    // block 0 instead: table entries there are not block ids; its data is masked.  The block
+    // of tile token t is chosen by a select tree on t / BS (a compare chain over four
+    // candidates was turned into an indexed scratch array).
+    auto pick = [&](int t) -> int64_t {
+      int r = cand[0];
+      if constexpr (NBT == 2) {
+        r = (t >= BS) ? cand[1] : cand[0];
+      } else if constexpr (NBT == 4) {
+        const int j = t / BS;
+        const int lo = (j & 1) ? cand[1] : cand[0], hi = (j & 1) ? cand[3] : cand[2];
+        r = (j & 2) ? hi : lo;
+      }
+      return (t0 + t < nslots) ? int64_t(r) : int64_t(0);
     };
     const bool pad = t0 > last * TT;
     const char* kp0 = (pad ? a.prefetch_pad : kbase + pick(ktok0) * block_bytes) + (ktok0 % BS) * 16;
@@ -171,13 +183,13 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
         s[r] = mma(DT(), widen8<DT, CODE>(tl.k[r][j].z, tl.k[r][j].w), qop[j][1], s[r]);
       }
     }
-    // lane: logits of tokens t0 + vtok + 4 r + e (e < 4) of its column
+    // lane: logits of tokens t0 + 16 r + 4 quad + e (e < 4) of its column
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s[r][e] = (t0 + vtok + 4 * r + e < ntok) ? s[r][e] * a.scale_log2 : -INFINITY;
+        s[r][e] = (t0 + (r ? stok1 : stok0) + e < ntok) ? s[r][e] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, s[r][e]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -197,8 +209,16 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
         hw[4 * r + e] = to_bits(DT(), exp2f(s[r][e] - m_new));
         l_run += from_bits(DT(), hw[4 * r + e]);
       }
-    const uint4 pop = make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
-                                 hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16));
+    // weights of tokens 4 quad .. + 4 (w0) and 16 + 4 quad .. + 4 (w1), two per dword; after
+    // the swaps lane (col, quad) holds tokens 8 quad .. + 8: rows (16 lanes) 2-3 of w0 trade
+    // with rows 0-1 of w1, then odd rows of the first with even rows of the second
+    const uint32_t w0x = hw[0] | (hw[1] << 16), w0y = hw[2] | (hw[3] << 16);
+    const uint32_t w1x = hw[4] | (hw[5] << 16), w1y = hw[6] | (hw[7] << 16);
+    const auto sx = __builtin_amdgcn_permlane32_swap(w0x, w1x, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(w0y, w1y, false, false);
+    const auto tx = __builtin_amdgcn_permlane16_swap(sx[0], sx[1], false, false);
+    const auto ty = __builtin_amdgcn_permlane16_swap(sy[0], sy[1], false, false);
+    const uint4 pop = make_uint4(tx[0], ty[0], tx[1], ty[1]);
     const int tv = t0 + vtok;
     if (tv + 8 > ntok) {  // value codes past the context (possibly NaN) become 0 before use
       const uint32_t m0 = keep4(tv, ntok), m1 = keep4(tv + 4, ntok);
