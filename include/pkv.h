@@ -135,6 +135,39 @@ int pkv_paged_attention_partitions(void* out, const void* query, const void* key
                                    int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_partitions split once more, so that one work list can serve several
+ * calls: a decode step's block tables and lengths are the same for every layer of the model,
+ * so the list can be built once per step and each layer's attention run on it.
+ *   pkv_paged_attention_plan: the work-list kernel alone; it writes the list (and each
+ *     sequence's item count) into `workspace`.
+ *   pkv_paged_attention_partitions_planned: the attention kernel alone, on the list in
+ *     `workspace`; with pkv_paged_attention_reduce after it, bit-identical to
+ *     pkv_paged_attention_decode.
+ * Both take the arguments and rules of pkv_paged_attention_decode (16- and 32-bit caches).
+ * A planned call must use the block_tables, context_lens, num_seqs, num_kv_heads, head_size,
+ * block_size, max_num_blocks_per_seq, max_context_len, dtype and partition_size of the plan
+ * (query, caches and out may change), unchanged on the device since the plan ran; otherwise
+ * the behaviour is undefined.  (The kernel skips list entries that do not fit the call's
+ * sequence count, partial slots and length limit, but an entry made for longer contexts would
+ * reach block-table entries past a sequence's blocks.)  A workspace no plan has written since
+ * it was zeroed holds an empty list: the call then writes nothing. */
+int pkv_paged_attention_plan(void* out, const void* query, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, float scale, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                             int32_t block_size, int32_t max_num_blocks_per_seq,
+                             int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_partitions_planned(void* out, const void* query, const void* key_cache,
+                                           const void* value_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, float scale,
+                                           int32_t num_seqs, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_size,
+                                           int32_t block_size, int32_t max_num_blocks_per_seq,
+                                           int32_t max_context_len, int32_t dtype,
+                                           int32_t partition_size, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* The second kernel alone: for each sequence with more than one work item,
  * out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p,
  * over its items p in token order.  Sequences with one item are left

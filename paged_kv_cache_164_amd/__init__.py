@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     reshape_and_cache_fp8,
     reshape_and_cache_int8,
     paged_attention_partitions,
+    paged_attention_partitions_planned,
+    paged_attention_plan,
     paged_attention_reduce,
     paged_attention_workspace_size,
     reshape_and_cache,

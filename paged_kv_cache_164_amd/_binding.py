@@ -32,6 +32,8 @@ _DECODE_ARGTYPES = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_int, _c_int, _c
 _SIGNATURES = {
     "pkv_paged_attention_decode": (_c_int, _DECODE_ARGTYPES),
     "pkv_paged_attention_partitions": (_c_int, _DECODE_ARGTYPES),
+    "pkv_paged_attention_plan": (_c_int, _DECODE_ARGTYPES),
+    "pkv_paged_attention_partitions_planned": (_c_int, _DECODE_ARGTYPES),
     "pkv_paged_attention_reduce": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_p, _c_sz, _c_p]),
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -308,6 +310,29 @@ def paged_attention_partitions(out, query, key_cache, value_cache, block_tables,
     args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                             max_context_len, partition_size, workspace, stream)
     _check(library().pkv_paged_attention_partitions(*args), "pkv_paged_attention_partitions")
+    return ws
+
+
+def paged_attention_plan(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size=0, workspace=None, stream=None):
+    """The work-list kernel alone; returns the workspace holding the list (for
+    paged_attention_partitions_planned calls with the same tables, lengths and shapes)."""
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream)
+    _check(library().pkv_paged_attention_plan(*args), "pkv_paged_attention_plan")
+    return ws
+
+
+def paged_attention_partitions_planned(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, scale, max_context_len, partition_size=0,
+                                       workspace=None, stream=None):
+    """The attention kernel alone, on the list a paged_attention_plan call left in workspace."""
+    if workspace is None:
+        raise PKVError("a planned call needs the workspace its plan was written to")
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream)
+    _check(library().pkv_paged_attention_partitions_planned(*args),
+           "pkv_paged_attention_partitions_planned")
     return ws
 
 

@@ -271,14 +271,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void fp
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
   const uint4 it = a.items[t / Hkv];
+  if (!item_fits(a, it)) return;
   fp8_item<DT, D, BS, CODE>(a, G, t % Hkv, int(it.x), int(it.y & 255u), int(it.z), int(it.w),
                       int(it.y >> 8));
 }
 
 template <class DT, int D, int BS, int CODE>
 hipError_t launch_t(const DecodeArgs& a, int group, hipStream_t stream) {
-  hipError_t e = launch_plan(a, BS, 16 / group, stream);
-  if (e != hipSuccess) return e;
+  if (a.plan_mode != 2) {
+    const hipError_t e = launch_plan(a, BS, 16 / group, stream);
+    if (e != hipSuccess || a.plan_mode == 1) return e;
+  }
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.slots;
   hipLaunchKernelGGL((fp8_grid_kernel<DT, D, BS, CODE>), dim3((unsigned)grid), dim3(64), 0, stream, a,
                      group);

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;
   const uint4 it = a.items[t / Hkv];
+  if (!item_fits(a, it)) return;
   const int kh = t % Hkv;
   const int b = int(it.x);
   const int slot = int(it.y >> 8);
@@ -236,8 +237,10 @@ template <class DT, int D, int BS, int G>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = valu_lds_bytes(G, D, a.partition_size);
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.slots;
-  hipError_t e = launch_plan(a, BS, 1, stream);
-  if (e != hipSuccess) return e;
+  if (a.plan_mode != 2) {
+    const hipError_t e = launch_plan(a, BS, 1, stream);
+    if (e != hipSuccess || a.plan_mode == 1) return e;
+  }
   hipLaunchKernelGGL((decode_valu_kernel<DT, D, BS, G>), dim3((unsigned)grid), dim3(kThreads), lds,
                      stream, a);
   return hipGetLastError();

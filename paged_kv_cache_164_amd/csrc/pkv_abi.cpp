@@ -418,6 +418,26 @@ int pkv_paged_attention_partitions(PKV_DECODE_PARAMS) {
   }
 }
 
+// Phase 1 split in two: the plan kernel alone (plan_mode 1), and the attention kernel on the
+// plan already in the workspace (plan_mode 2).
+static int phase1_mode(PKV_DECODE_PARAMS, int mode) {
+  try {
+    Resolved r;
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r);
+    if (rc != PKV_OK) return rc;
+    r.args.plan_mode = mode;
+    return launch_phase1(r, dtype, head_size, block_size, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+int pkv_paged_attention_plan(PKV_DECODE_PARAMS) { return phase1_mode(PKV_DECODE_ARGS, stream, 1); }
+
+int pkv_paged_attention_partitions_planned(PKV_DECODE_PARAMS) {
+  return phase1_mode(PKV_DECODE_ARGS, stream, 2);
+}
+
 int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t head_size, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size, const void* workspace,

@@ -70,7 +70,18 @@ struct DecodeArgs {
   int partition_size;   // P: tokens of a whole partition
   int tail_chunk;       // Q: tokens of a remainder chunk
   int slots;            // partial slots per (sequence, head); also items per sequence
+  int plan_mode;        // 0: plan, then attention; 1: plan only; 2: attention on the plan
+                        // already in the workspace
 };
+
+// A work item as the attention kernels read it from the list, which may come from an earlier
+// call (plan_mode 2): an item whose sequences, partial slot or token range do not fit this
+// call's shapes is skipped, a guard against lists planned for other shapes.
+__host__ __device__ inline bool item_fits(const DecodeArgs& a, uint4 it) {
+  const uint32_t b0 = it.x, nseq = it.y & 255u, slot = it.y >> 8;
+  return nseq >= 1u && b0 < uint32_t(a.num_seqs) && nseq <= uint32_t(a.num_seqs) - b0 &&
+         slot < uint32_t(a.slots) && it.z <= it.w && it.w <= uint32_t(a.len_limit);
+}
 
 // Workspace: [queue header | prefetch pad | per-sequence partial counts | work items (16 B) |
 // split-K partials], each region 256-byte aligned.

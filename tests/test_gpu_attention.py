@@ -5,6 +5,8 @@ Sizes: every workload at a size the oracle covers completely (several partitions
 ragged last block), and every workload at its full size with sampled (sequence, head)
 outputs, in the launch configuration the benchmark times (auto partition size).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -135,6 +137,48 @@ def test_two_phase_entry_points_equal_fused_call():
     pkv.paged_attention_reduce(out2, g.cl, case.max_context_len, ws, 0)
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("key,dtype", [("c3", None), ("c2", None), ("c1", None), ("c3", "f32")])
+def test_plan_reused_across_layers(key, dtype):
+    """One plan serves several layers: per layer a different query and cache, the same block
+    tables and lengths.  Planned attention + reduce must equal the one-call decode of each layer
+    bit for bit."""
+    over = {} if dtype is None else {"dtype": dtype}
+    c0 = make_decode_case(key, num_seqs=4 if key == "c1" else 24, len_cap=3000, **over)
+    # layers: the same tables and lengths, other queries and cache contents (rolled and
+    # rescaled copies of the first layer's; NaN poison stays NaN)
+    cases = [c0] + [dataclasses.replace(
+        c0, query=torch.roll(c0.query, layer, dims=1) * (1.0 + 0.5 * layer),
+        key_cache=c0.key_cache * (1.0 - 0.25 * layer), value_cache=c0.value_cache + layer,
+        new_key=c0.new_key * 0.5, new_value=c0.new_value - layer) for layer in (1, 2)]
+    gs = [GpuDecode(c, 0) for c in cases]
+    base = [g.step().clone() for g in gs]   # also writes each layer's new token
+    g0 = gs[0]
+    ws = torch.zeros_like(g0.ws)
+    pkv.paged_attention_plan(torch.empty_like(base[0]), g0.q, g0.kc, g0.vc, g0.bt, g0.cl,
+                             c0.scale, c0.max_context_len, 0, ws)
+    for layer, (c, g) in enumerate(zip(cases, gs)):
+        out = torch.full_like(base[layer], float("nan"))
+        pkv.paged_attention_partitions_planned(out, g.q, g.kc, g.vc, g0.bt, g0.cl, c.scale,
+                                               c.max_context_len, 0, ws)
+        pkv.paged_attention_reduce(out, g0.cl, c.max_context_len, ws, 0)
+        torch.cuda.synchronize()
+        log(f"plan reuse {key} {dtype} layer {layer}")
+        assert torch.equal(out.view(torch.int16 if out.element_size() == 2 else torch.int32),
+                           base[layer].view(torch.int16 if out.element_size() == 2 else torch.int32))
+
+
+def test_planned_call_on_an_unplanned_workspace_writes_nothing():
+    case = make_decode_case("c3", num_seqs=8, len_cap=2000)
+    g = GpuDecode(case, 0)
+    ws = torch.zeros_like(g.ws)   # no plan since it was zeroed: an empty list
+    out = torch.full_like(g.q, 7.0)
+    pkv.paged_attention_partitions_planned(out, g.q, g.kc, g.vc, g.bt, g.cl, case.scale,
+                                           case.max_context_len, 0, ws)
+    pkv.paged_attention_reduce(out, g.cl, case.max_context_len, ws, 0)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
 
 
 def test_gqa_matches_mha_with_repeated_kv_on_gpu():
