@@ -75,3 +75,69 @@ def test_multi_query_graph_replays(P):
                                     P, ws)
 
     _check_replays(step, out)
+
+
+def test_planned_step_graph_replays():
+    """Plan, cache write, attention on the plan and reduce, captured as one graph."""
+    case = make_decode_case("c3", num_seqs=40, len_cap=6000)
+    q, kc, vc = case.query.to(DEV), case.key_cache.to(DEV), case.value_cache.to(DEV)
+    bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+    nk, nv, slots = case.new_key.to(DEV), case.new_value.to(DEV), case.slot_mapping.to(DEV)
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.paged_attention_workspace_size(case.num_seqs, 32, 128, case.max_context_len),
+                     dtype=torch.uint8, device=DEV)
+    log(f"graph planned decode: {case.num_seqs} sequences")
+
+    def step():
+        pkv.paged_attention_plan(out, q, kc, vc, bt, cl, case.scale, case.max_context_len, 0, ws)
+        pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+        pkv.paged_attention_partitions_planned(out, q, kc, vc, bt, cl, case.scale,
+                                               case.max_context_len, 0, ws)
+        pkv.paged_attention_reduce(out, cl, case.max_context_len, ws, 0)
+
+    _check_replays(step, out)
+
+
+@pytest.mark.parametrize("code", ["e4m3", "i8"])
+def test_8bit_decode_and_multi_query_graph_replays(code):
+    from workloads import with_8bit_cache
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=24, len_cap=4000), code)
+    q, kc, vc = case.query.to(DEV), case.key_cache.to(DEV), case.value_cache.to(DEV)
+    bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+    nk, nv, slots = case.new_key.to(DEV), case.new_value.to(DEV), case.slot_mapping.to(DEV)
+    out = torch.empty_like(q)
+    ws = torch.empty(pkv.paged_attention_workspace_size(case.num_seqs, 32, 128, case.max_context_len),
+                     dtype=torch.uint8, device=DEV)
+    log(f"graph 8-bit decode {code}")
+
+    def step():
+        pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale, code=code)
+        pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, case.scale, case.k_scale,
+                                       case.v_scale, case.max_context_len, 0, ws, code=code)
+
+    _check_replays(step, out)
+
+    pcase = with_8bit_cache(make_prefill_case([(300, 130), (0, 77), (1000, 1)], poison=False,
+                                              num_heads=16, num_kv_heads=4, head_size=128,
+                                              block_size=16), code)
+    pkc, pvc = pcase.key_cache.to(DEV), pcase.value_cache.to(DEV)
+    pkv.reshape_and_cache_fp8(pcase.new_key.to(DEV), pcase.new_value.to(DEV), pkc, pvc,
+                              torch.from_numpy(pcase.slot_mapping).to(DEV), pcase.k_scale,
+                              pcase.v_scale, code=code)
+    pq = pcase.query.to(DEV)
+    pbt = torch.from_numpy(pcase.block_tables).to(DEV)
+    pcl = torch.from_numpy(pcase.context_lens).to(DEV)
+    pqsl = torch.from_numpy(pcase.query_start_loc).to(DEV)
+    pout = torch.empty_like(pq)
+    B = len(pcase.context_lens)
+    pws = torch.empty(max(pkv.paged_attention_prefill_workspace_size(
+        B, pcase.num_tokens, 16, 4, 128, pcase.max_context_len, 64), 256), dtype=torch.uint8,
+        device=DEV)
+    log(f"graph 8-bit multi-query {code}")
+
+    def pstep():
+        pkv.paged_attention_prefill(pout, pq, pkc, pvc, pbt, pcl, pqsl, pcase.scale,
+                                    pcase.max_context_len, 64, pws, k_scale=pcase.k_scale,
+                                    v_scale=pcase.v_scale, code=code)
+
+    _check_replays(pstep, pout)
