@@ -203,6 +203,83 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   }
 }
 
+// The 8-bit write for many tokens: 16 tokens per workgroup, as reshape_and_cache_runs_kernel.
+// A run of 8 consecutive tokens landing in 8 consecutive, 8-aligned slots of one block writes
+// its codes of a value row as one 8-byte store; other runs fall back to byte stores.  Keys are
+// 16-byte chunks (16 codes) either way.
+template <class IN, int CODE>
+__global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int head_size,
+    int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride, float k_scale,
+    float v_scale) {
+  __shared__ int64_t s_slot[kRunTokens];
+  __shared__ int s_vec[2];
+  const int64_t i0 = (int64_t)blockIdx.x * kRunTokens;
+  const int ntok = (int)min<int64_t>(kRunTokens, num_tokens - i0);
+  const int tid = threadIdx.x;
+  if (tid < kRunTokens) {
+    int64_t sl = (tid < ntok) ? slot_mapping[i0 + tid] : -1;
+    s_slot[tid] = (sl < 0 || sl >= num_blocks * block_size) ? -1 : sl;  // skipped: -1
+  }
+  __syncthreads();
+  if (tid < 2) {
+    const int64_t a = s_slot[8 * tid];
+    bool ok = a >= 0 && a % 8 == 0 && a % block_size + 8 <= block_size;
+    for (int k = 1; k < 8; ++k) ok = ok && s_slot[8 * tid + k] == a + k;
+    s_vec[tid] = ok;
+  }
+  __syncthreads();
+  const int D = head_size;
+  const int n = num_kv_heads * D;
+  const int64_t tile = (int64_t)D * block_size;  // bytes of one (block, head) tile
+  // keys: one 16-byte chunk (16 dims) of one token per thread, token index fastest
+  for (int t = tid; t < kRunTokens * (n / 16); t += blockDim.x) {
+    const int j = t % kRunTokens, c = t / kRunTokens;
+    const int64_t sl = s_slot[j];
+    if (sl < 0) continue;
+    const int h = c / (D / 16), cc = c % (D / 16);
+    const uint16_t* e = key + (i0 + j) * key_stride + (int64_t)c * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = quant2<CODE>(widen16(IN(), e[4 * k]), widen16(IN(), e[4 * k + 1]), k_scale) |
+             (quant2<CODE>(widen16(IN(), e[4 * k + 2]), widen16(IN(), e[4 * k + 3]), k_scale) << 16);
+    *reinterpret_cast<uint4*>(key_cache + ((sl / block_size) * num_kv_heads + h) * tile +
+                              ((int64_t)cc * block_size + sl % block_size) * 16) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2)
+  for (int t = tid; t < 2 * n; t += blockDim.x) {
+    const int e = t >> 1, half = t & 1;
+    const int h = e / D, d = e % D;
+    const int kb = 8 * half;
+    uint32_t v[2];
+#pragma unroll
+    for (int k = 0; k < 8; k += 4) {
+      float x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        x[q] = (kb + k + q < ntok) ? widen16(IN(), value[(i0 + kb + k + q) * value_stride + e]) : 0.f;
+      v[k / 4] = quant2<CODE>(x[0], x[1], v_scale) | (quant2<CODE>(x[2], x[3], v_scale) << 16);
+    }
+    if (s_vec[half]) {
+      const int64_t sl = s_slot[kb];
+      *reinterpret_cast<uint2*>(value_cache + ((sl / block_size) * num_kv_heads + h) * tile +
+                                (int64_t)d * block_size + sl % block_size) = make_uint2(v[0], v[1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t sl = s_slot[kb + k];
+        if (sl < 0) continue;
+        value_cache[((sl / block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
+                    sl % block_size] = uint8_t(v[k / 4] >> (8 * (k & 3)));
+      }
+    }
+  }
+}
+
 constexpr int kCopyThreads = 256;
 constexpr int64_t kCopyChunk16 = kCopyThreads * 8;  // 16-byte words per workgroup (32 KiB)
 
@@ -277,6 +354,19 @@ hipError_t launch_rc8(const void* key, const void* value, void* key_cache, void*
                       int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride,
                       int dtype, float k_scale, float v_scale, hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
+  // many tokens: the run kernel (its 8-byte value stores need an 8-byte aligned cache)
+  if (num_tokens >= kRunMinTokens && reinterpret_cast<uintptr_t>(value_cache) % 8 == 0) {
+    const dim3 rgrid((unsigned)((num_tokens + kRunTokens - 1) / kRunTokens));
+#define PKV_RUNS8(IN)                                                                           \
+  hipLaunchKernelGGL((reshape_and_cache_kv8_runs_kernel<IN, CODE>), rgrid, dim3(256), 0, stream, \
+                     static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),    \
+                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),      \
+                     slot_mapping, num_tokens, num_kv_heads, head_size, block_size, num_blocks, \
+                     key_stride, value_stride, k_scale, v_scale)
+    if (dtype == 1) PKV_RUNS8(F16); else PKV_RUNS8(BF16);
+#undef PKV_RUNS8
+    return hipGetLastError();
+  }
   const dim3 grid(num_tokens), block(256);
 #define PKV_RC8(IN)                                                                             \
   hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<IN, CODE>), grid, block, 0, stream,          \

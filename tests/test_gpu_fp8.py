@@ -126,3 +126,48 @@ def test_kv8_run_to_run_bit_determinism(code):
     a = _decode(case)
     b = _decode(case)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("code", CODES)
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 8), ("bf16", 32)])
+def test_reshape_and_cache_kv8_many_tokens(dtype, bs, code):
+    """A prefill-sized batch (the 8-bit many-token path): runs of consecutive slots filling
+    blocks, runs starting mid-block, a run with a hole, skipped (-1) and out-of-range slots,
+    random singles, and a ragged tail; compared byte for byte with the oracle's write."""
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=8, len_cap=1500, dtype=dtype,
+                                            block_size=bs, pool=("plus", 160)), code)
+    Hkv, D = case.key_cache.shape[1], case.query.shape[2]
+    NB = case.key_cache.shape[0]
+    free = [int(b) for b in case.free_blocks]
+    whole = 768 // bs
+    free, blocks = free[whole:], free[:whole]
+    assert len(free) >= 40
+    slots = []
+    for b in blocks:
+        slots += [b * bs + o for o in range(bs)]
+    b0, b1 = free[0], free[1]
+    slots += [b0 * bs + o for o in range(3, bs)] + [b1 * bs + o for o in range(bs)]
+    run = [free[2] * bs + o for o in range(bs)]
+    run[5] = -1
+    slots += run
+    slots += [NB * bs + 9, -3]
+    g = np.random.default_rng(3)
+    singles = g.choice(np.array([b * bs + o for b in free[3:40] for o in range(bs)]), size=37,
+                       replace=False)
+    slots += [int(x) for x in singles]
+    slots = np.array(slots, dtype=np.int64)
+    N = len(slots)
+    assert N >= 512 and N % 16 != 0
+    key = draw_normal((N, Hkv, D), dtype, 79, 0) * 3
+    val = draw_normal((N, Hkv, D), dtype, 79, 1) * 3
+    log(f"reshape {code} many tokens {dtype} bs{bs} N={N}")
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    pkv.reshape_and_cache_fp8(key.to(DEV), val.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV),
+                              case.k_scale, case.v_scale, code=code)
+    torch.cuda.synchronize()
+    kb, vb = case.key_cache.numpy().copy(), case.value_cache.numpy().copy()
+    ref_slots = np.where(slots < NB * bs, slots, -1)
+    _oracle_write(code)(kb, vb, storage_bits(key), storage_bits(val), dtype, ref_slots,
+                        case.k_scale, case.v_scale)
+    assert np.array_equal(kc.cpu().numpy(), kb)
+    assert np.array_equal(vc.cpu().numpy(), vb)
