@@ -323,14 +323,30 @@ def ceilings(steps: int = 20) -> None:
     m_in = np.stack([np.arange(pairs), perm[pairs:2 * pairs]], 1).astype(np.int64)
     ms_out = timed(lambda: pkv.swap_blocks(kc, host, m_out, stream=stream), max(steps // 4, 3))
     ms_in = timed(lambda: pkv.swap_blocks(host, kc, m_in, stream=stream), max(steps // 4, 3))
+    # the link itself: one contiguous copy of the same bytes each way (copy engines)
+    ms_lo = timed(lambda: host.copy_(kc[:pairs], non_blocking=True), max(steps // 4, 3))
+    ms_li = timed(lambda: kc[:pairs].copy_(host, non_blocking=True), max(steps // 4, 3))
+    # the copy engines block by block (one asynchronous copy per scattered block)
+    src_ids, dst_ids = [int(v) for v in perm[:pairs]], [int(v) for v in perm[pairs:2 * pairs]]
+
+    def per_block_out():
+        for i, s in enumerate(src_ids):
+            host[i].copy_(kc[s], non_blocking=True)
+
+    def per_block_in():
+        for i, d in enumerate(dst_ids):
+            kc[d].copy_(host[i], non_blocking=True)
+    ms_bo = timed(per_block_out, max(steps // 4, 3))
+    ms_bi = timed(per_block_in, max(steps // 4, 3))
+    gbs = lambda ms: round(pairs * block_bytes / (ms / 1e3) / 1e9, 2)  # noqa: E731
     print(json.dumps({
         "ceilings": "reference rates on this GPU",
         "stream_read_GBs": round(read_gbs, 1), "stream_read_frac_of_8TBs": round(read_gbs / HBM_PEAK_GBS, 4),
         "stream_read_back_to_back_GBs": round(read10_gbs, 1), "stream_read_bytes": 4 << 30,
         "copy_blocks_GBs": round(copy_gbs, 1), "copy_blocks_pairs": pairs, "block_bytes": block_bytes,
-        "swap_out_GBs": round(pairs * block_bytes / (ms_out / 1e3) / 1e9, 2),
-        "swap_in_GBs": round(pairs * block_bytes / (ms_in / 1e3) / 1e9, 2),
-        "swap_bytes": pairs * block_bytes,
+        "swap_out_GBs": gbs(ms_out), "swap_in_GBs": gbs(ms_in), "swap_bytes": pairs * block_bytes,
+        "host_link_contiguous_out_GBs": gbs(ms_lo), "host_link_contiguous_in_GBs": gbs(ms_li),
+        "copy_engine_per_block_out_GBs": gbs(ms_bo), "copy_engine_per_block_in_GBs": gbs(ms_bi),
     }), flush=True)
 
 

@@ -437,10 +437,14 @@ int pkv_copy_blocks(const uint64_t* key_cache_ptrs, const uint64_t* value_cache_
  *   block_mapping  HOST int64 [num_pairs, 2] = (src block, dst block), read
  *                  before the call returns
  *   src_num_blocks, dst_num_blocks  pool sizes, for range checks
- * Runs of consecutive ids become one asynchronous copy.  Returns
- * PKV_ERR_NOT_PINNED if the host side is not page-locked host memory and
- * PKV_ERR_INVALID_ARG for an id out of range.  The host buffer must stay
- * alive and untouched until the stream reaches the copies.
+ * When the device addresses the pinned memory at the host pointer itself
+ * (mapped host memory; both bases 8-byte aligned, block_bytes a multiple
+ * of 8), one kernel launch moves up to 112 blocks, the pair list passed in
+ * its arguments; otherwise runs of consecutive ids become one asynchronous
+ * copy each.  Returns PKV_ERR_NOT_PINNED if the host side is not page-locked
+ * host memory and PKV_ERR_INVALID_ARG for an id out of range.  The host
+ * buffer must stay alive and untouched until the stream has passed the
+ * call's work.
  */
 int pkv_swap_blocks(void* dst, const void* src, const int64_t* block_mapping, int32_t num_pairs,
                     int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,

@@ -282,6 +282,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
 
 constexpr int kCopyThreads = 256;
 constexpr int64_t kCopyChunk16 = kCopyThreads * 8;  // 16-byte words per workgroup (32 KiB)
+constexpr int64_t kSwapChunk8 = kCopyThreads * 16;  // 8-byte words per workgroup (32 KiB)
 
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     const uint64_t* __restrict__ key_ptrs, const uint64_t* __restrict__ value_ptrs,
@@ -305,6 +306,45 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     const unsigned char* s = reinterpret_cast<const unsigned char*>(base + src * block_bytes);
     unsigned char* d = reinterpret_cast<unsigned char*>(base + dst * block_bytes);
     for (int64_t k = lo * 16 + threadIdx.x; k < hi * 16; k += kCopyThreads) d[k] = s[k];
+  }
+}
+
+// swap_blocks: whole blocks between the device cache and page-locked host memory that the device
+// addresses directly (CacheEngine swap_in / swap_out).  One launch moves up to kSwapPairs blocks;
+// the pair list travels in the kernel arguments, so nothing is allocated.  The host side is read
+// and written with system-scope relaxed 8-byte atomics (coherent with the host whatever the
+// allocation's coherence flag); the lanes of a wave touch 512 contiguous bytes per access, whole
+// lines, on both sides.
+template <bool TO_HOST>
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    unsigned char* __restrict__ dst, const unsigned char* __restrict__ src, SwapList list,
+    int64_t block_bytes, int chunks_per_block) {
+  const int pair = blockIdx.x / chunks_per_block;
+  const int chunk = blockIdx.x % chunks_per_block;
+  const int64_t n8 = block_bytes / 8;
+  const int64_t lo = chunk * kSwapChunk8;
+  const int64_t hi = min(n8, lo + kSwapChunk8);
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(src + list.src[pair] * block_bytes);
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst + list.dst[pair] * block_bytes);
+  constexpr int U = 8;  // 8-byte words in flight per thread
+  for (int64_t k0 = lo + threadIdx.x; k0 < hi; k0 += U * kCopyThreads) {
+    uint64_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u * kCopyThreads;
+      if (k < hi) {
+        if constexpr (TO_HOST) w[u] = s[k];
+        else w[u] = __hip_atomic_load(s + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u * kCopyThreads;
+      if (k < hi) {
+        if constexpr (TO_HOST) __hip_atomic_store(d + k, w[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        else d[k] = w[u];
+      }
+    }
   }
 }
 
@@ -409,6 +449,22 @@ hipError_t launch_copy_blocks(const uint64_t* key_ptrs, const uint64_t* value_pt
   const dim3 grid((unsigned)(num_pairs * chunks), (unsigned)num_layers, 2);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, key_ptrs, value_ptrs,
                      mapping, block_bytes, num_blocks, (int)chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(void* dst, const void* src, const SwapList& list, int num_pairs,
+                              int64_t block_bytes, bool to_host, hipStream_t stream) {
+  if (num_pairs <= 0) return hipSuccess;
+  const int64_t chunks = (block_bytes / 8 + kSwapChunk8 - 1) / kSwapChunk8;
+  const dim3 grid((unsigned)(num_pairs * chunks));
+  auto* d = static_cast<unsigned char*>(dst);
+  auto* s = static_cast<const unsigned char*>(src);
+  if (to_host)
+    hipLaunchKernelGGL(swap_blocks_kernel<true>, grid, dim3(kCopyThreads), 0, stream, d, s, list,
+                       block_bytes, (int)chunks);
+  else
+    hipLaunchKernelGGL(swap_blocks_kernel<false>, grid, dim3(kCopyThreads), 0, stream, d, s, list,
+                       block_bytes, (int)chunks);
   return hipGetLastError();
 }
 

@@ -655,9 +655,9 @@ int pkv_swap_blocks(void* dst, const void* src, const int64_t* block_mapping, in
     if (!dst || !src || !block_mapping) return fail(PKV_ERR_NULL_POINTER, "null pointer");
     const void* host = direction == PKV_SWAP_IN ? src : dst;
     const void* dev = direction == PKV_SWAP_IN ? dst : src;
-    hipPointerAttribute_t attr{};
-    hipError_t e = hipPointerGetAttributes(&attr, host);
-    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    hipPointerAttribute_t hattr{}, attr{};
+    hipError_t e = hipPointerGetAttributes(&hattr, host);
+    if (e != hipSuccess || hattr.type != hipMemoryTypeHost) {
       (void)hipGetLastError();  // clear the sticky error of an unregistered pointer
       return fail(PKV_ERR_NOT_PINNED, "host side of swap_blocks is not page-locked host memory");
     }
@@ -671,9 +671,25 @@ int pkv_swap_blocks(void* dst, const void* src, const int64_t* block_mapping, in
       if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
         return fail(PKV_ERR_INVALID_ARG, "block id out of range at pair " + std::to_string(i));
     }
-    const hipMemcpyKind kind = direction == PKV_SWAP_IN ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    // Coalesce runs where both ids advance by one into a single copy.
+    // The device reaches the pinned memory at the host pointer itself (mapped host memory under
+    // unified addressing): one kernel per kSwapPairs blocks, all blocks' bytes in flight at once.
+    if (hattr.devicePointer == host && block_bytes % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(dst) % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 8 == 0) {
+      pkv::SwapList list;
+      for (int32_t i0 = 0; i0 < num_pairs; i0 += pkv::kSwapPairs) {
+        const int32_t n = std::min<int32_t>(pkv::kSwapPairs, num_pairs - i0);
+        for (int32_t j = 0; j < n; ++j) {
+          list.src[j] = block_mapping[2 * (i0 + j)];
+          list.dst[j] = block_mapping[2 * (i0 + j) + 1];
+        }
+        e = pkv::launch_swap_blocks(dst, src, list, n, block_bytes, direction == PKV_SWAP_OUT, st);
+        if (e != hipSuccess) return hip_fail(e, "swap_blocks launch");
+      }
+      return PKV_OK;
+    }
+    // Otherwise the copy engines, runs of consecutive ids as one asynchronous copy each.
+    const hipMemcpyKind kind = direction == PKV_SWAP_IN ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
     int32_t i = 0;
     while (i < num_pairs) {
       const int64_t s0 = block_mapping[2 * i], d0 = block_mapping[2 * i + 1];

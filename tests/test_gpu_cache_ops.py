@@ -155,3 +155,53 @@ def test_swap_rejects_pageable_host_memory():
     host = torch.zeros((4, 2, 16, 16, 4))        # not pinned
     with pytest.raises(pkv.PKVError, match="code -6"):
         pkv.swap_blocks(dev, host, [[0, 1]])
+
+
+@pytest.mark.parametrize("offset", [0, 3])
+def test_swap_many_pairs_both_ways(offset):
+    """More pairs than one launch carries (the pair list is split over launches), blocks of the
+    beam-search shape (40 heads x 128 x 16 fp16 = 160 KiB), the host side as the whole pinned
+    buffer or a view that starts `offset` blocks in; out and back in, byte for byte."""
+    NB_dev, NB_host, pairs = 512, 300, 290
+    dev_k = draw_normal((NB_dev, 40, 16, 16, 8), "f16", 61, offset).to(DEV)
+    pinned = torch.zeros((NB_host + offset, 40, 16, 16, 8), dtype=torch.float16).pin_memory()
+    host_k = pinned[offset:]
+    rng = np.random.default_rng(5 + offset)
+    src = rng.choice(NB_dev, pairs, replace=False)
+    dst = rng.permutation(NB_host)[:pairs]
+    out_map = np.stack([src, dst], axis=1).astype(np.int64)
+    log(f"swap out {pairs} pairs, host offset {offset}")
+    before = storage_bits(dev_k.cpu()).copy()
+    pkv.swap_blocks(dev_k, host_k, out_map)
+    torch.cuda.synchronize()
+    ref_host = np.zeros_like(storage_bits(host_k))
+    OC.swap_blocks(ref_host, before, out_map)
+    assert np.array_equal(storage_bits(host_k), ref_host)
+    # the host rewrites some swapped-out blocks before the swap in: the device must see the new bytes
+    host_k[torch.from_numpy(dst[:7])] = 2.5
+    ref_host[dst[:7]] = storage_bits(host_k[torch.from_numpy(dst[:7])])
+    back = rng.permutation(NB_dev)[:pairs]
+    in_map = np.stack([dst, back], axis=1).astype(np.int64)
+    dev_k[torch.from_numpy(back).to(DEV)] = float("nan")
+    log(f"swap in {pairs} pairs, host offset {offset}")
+    pkv.swap_blocks(host_k, dev_k, in_map)
+    torch.cuda.synchronize()
+    got = storage_bits(dev_k.cpu())
+    assert np.array_equal(got[back], ref_host[dst])
+
+
+def test_swap_odd_block_bytes():
+    """Blocks whose size is not a multiple of 16 bytes (3 x 5 x 2 bytes) take the copy engines."""
+    dev = torch.arange(40 * 15, dtype=torch.int16).reshape(40, 3, 5).to(DEV)
+    host = torch.zeros((20, 3, 5), dtype=torch.int16).pin_memory()
+    m = np.array([[7, 0], [8, 1], [9, 2], [31, 19], [0, 5]], dtype=np.int64)
+    pkv.swap_blocks(dev, host, m)
+    torch.cuda.synchronize()
+    ref = dev.cpu()
+    for s, d in m:
+        assert torch.equal(host[d], ref[s])
+    back = torch.zeros_like(dev)
+    pkv.swap_blocks(host, back, m[:, ::-1].copy())
+    torch.cuda.synchronize()
+    for s, d in m:
+        assert torch.equal(back[s].cpu(), ref[s])
