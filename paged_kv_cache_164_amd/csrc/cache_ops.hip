@@ -16,40 +16,75 @@
 namespace pkv {
 namespace {
 
-template <typename E, bool VEC_KEY>
+// A valid (non-negative) slot's block and offset: shift and mask for a power-of-two block size
+// (every size the attention kernels take), a 64-bit division otherwise.
+__device__ inline int64_t slot_block(int64_t slot, int block_size) {
+  if ((block_size & (block_size - 1)) == 0)
+    return slot >> __builtin_ctz(static_cast<unsigned>(block_size));
+  return slot / block_size;
+}
+__device__ inline int slot_offset(int64_t slot, int block_size) {
+  if ((block_size & (block_size - 1)) == 0) return static_cast<int>(slot & (block_size - 1));
+  return static_cast<int>(slot % block_size);
+}
+
+// One workgroup per new token.  VEC (16-byte aligned rows and key cache): a thread takes 16-byte
+// chunks of the key row and of the value row, all its loads in flight together; a key chunk is
+// one 16-byte store, a value chunk X element stores down the value rows.  Otherwise element by
+// element.
+template <typename E, bool VEC>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ key_cache,
     E* __restrict__ value_cache, const int64_t* __restrict__ slot_mapping, int num_kv_heads,
     int head_size, int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride) {
   constexpr int X = 16 / sizeof(E);
   const int64_t i = blockIdx.x;
-  const int64_t slot = slot_mapping[i];
-  if (slot < 0 || slot >= num_blocks * block_size) return;
-  const int64_t blk = slot / block_size;
-  const int off = static_cast<int>(slot % block_size);
   const int D = head_size;
   const int n = num_kv_heads * D;
   const int64_t tile = (int64_t)D * block_size;  // elements of one (block, head) tile
-  E* kdst = key_cache + blk * num_kv_heads * tile;
-  E* vdst = value_cache + blk * num_kv_heads * tile;
   const E* krow = key + i * key_stride;
   const E* vrow = value + i * value_stride;
-  if constexpr (VEC_KEY) {
-    const int chunks_per_head = D / X;
-    for (int c = threadIdx.x; c < n / X; c += blockDim.x) {
-      const int h = c / chunks_per_head, cc = c % chunks_per_head;
-      *reinterpret_cast<uint4*>(kdst + h * tile + ((int64_t)cc * block_size + off) * X) =
-          *reinterpret_cast<const uint4*>(krow + (int64_t)c * X);
-    }
+  if constexpr (VEC) {
+    const int nc = n / X, cph = D / X;
+    const uint4* k4 = reinterpret_cast<const uint4*>(krow);
+    const uint4* v4 = reinterpret_cast<const uint4*>(vrow);
+    // the first two chunks per thread (all of a row up to 512 chunks) without a branch: indices
+    // past the row are clamped to its last chunk and their values dropped
+    const int c0 = threadIdx.x, c1 = c0 + blockDim.x;
+    const int l0 = min(c0, nc - 1), l1 = min(c1, nc - 1);
+    const uint4 ka = k4[l0], va = v4[l0], kb = k4[l1], vb = v4[l1];
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * block_size) return;
+    const int64_t blk = slot_block(slot, block_size);
+    const int off = slot_offset(slot, block_size);
+    E* kdst = key_cache + blk * num_kv_heads * tile;
+    E* vdst = value_cache + blk * num_kv_heads * tile;
+    auto put = [&](int c, const uint4& kq, const uint4& vq) {
+      const int h = c / cph, cc = c % cph;
+      *reinterpret_cast<uint4*>(kdst + h * tile + ((int64_t)cc * block_size + off) * X) = kq;
+      const E* ve = reinterpret_cast<const E*>(&vq);
+      E* vd = vdst + h * tile + (int64_t)(cc * X) * block_size + off;
+#pragma unroll
+      for (int e = 0; e < X; ++e) vd[(int64_t)e * block_size] = ve[e];
+    };
+    if (c0 < nc) put(c0, ka, va);
+    if (c1 < nc) put(c1, kb, vb);
+    for (int c = c0 + 2 * blockDim.x; c < nc; c += blockDim.x) put(c, k4[c], v4[c]);
   } else {
+    const int64_t slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_blocks * block_size) return;
+    const int64_t blk = slot_block(slot, block_size);
+    const int off = slot_offset(slot, block_size);
+    E* kdst = key_cache + blk * num_kv_heads * tile;
+    E* vdst = value_cache + blk * num_kv_heads * tile;
     for (int e = threadIdx.x; e < n; e += blockDim.x) {
       const int h = e / D, d = e % D;
       kdst[h * tile + ((int64_t)(d / X) * block_size + off) * X + d % X] = krow[e];
     }
-  }
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int h = e / D, d = e % D;
-    vdst[h * tile + (int64_t)d * block_size + off] = vrow[e];
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+      const int h = e / D, d = e % D;
+      vdst[h * tile + (int64_t)d * block_size + off] = vrow[e];
+    }
   }
 }
 
@@ -82,7 +117,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
   __syncthreads();
   if (tid < 2) {
     const int64_t a = s_slot[8 * tid];
-    bool ok = a >= 0 && a % 8 == 0 && a % block_size + 8 <= block_size;
+    // the vector store needs every value row 8-element aligned: block_size a multiple of 8
+    bool ok = block_size % 8 == 0 && a >= 0 && a % 8 == 0 &&
+              slot_offset(a, block_size) + 8 <= block_size;
     for (int k = 1; k < 8; ++k) ok = ok && s_slot[8 * tid + k] == a + k;
     s_vec[tid] = ok;
   }
@@ -95,8 +132,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
     const int64_t sl = s_slot[j];
     if (sl < 0) continue;
     const int h = c / (D / X), cc = c % (D / X);
-    uint16_t* dst = key_cache + ((sl / block_size) * num_kv_heads + h) * tile +
-                    ((int64_t)cc * block_size + sl % block_size) * X;
+    uint16_t* dst = key_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
+                    ((int64_t)cc * block_size + slot_offset(sl, block_size)) * X;
     const uint16_t* src = key + (i0 + j) * key_stride + (int64_t)c * X;
     if constexpr (VEC_KEY) {
       *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
@@ -119,16 +156,16 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
     }
     if (s_vec[half]) {
       const int64_t sl = s_slot[kb];
-      uint16_t* dst = value_cache + ((sl / block_size) * num_kv_heads + h) * tile +
-                      (int64_t)d * block_size + sl % block_size;
+      uint16_t* dst = value_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
+                      (int64_t)d * block_size + slot_offset(sl, block_size);
       *reinterpret_cast<uint4*>(dst) = make_uint4(v[0], v[1], v[2], v[3]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int64_t sl = s_slot[kb + k];
         if (sl < 0) continue;
-        value_cache[((sl / block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
-                    sl % block_size] = uint16_t(v[k / 2] >> (16 * (k & 1)));
+        value_cache[(slot_block(sl, block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
+                    slot_offset(sl, block_size)] = uint16_t(v[k / 2] >> (16 * (k & 1)));
       }
     }
   }
@@ -171,8 +208,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   const int64_t i = blockIdx.x;
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_blocks * block_size) return;
-  const int64_t blk = slot / block_size;
-  const int off = static_cast<int>(slot % block_size);
+  const int64_t blk = slot_block(slot, block_size);
+  const int off = slot_offset(slot, block_size);
   const int D = head_size;
   const int n = num_kv_heads * D;
   const int64_t tile = (int64_t)D * block_size;  // bytes of one (block, head) tile
@@ -226,7 +263,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
   __syncthreads();
   if (tid < 2) {
     const int64_t a = s_slot[8 * tid];
-    bool ok = a >= 0 && a % 8 == 0 && a % block_size + 8 <= block_size;
+    // the vector store needs every value row 8-element aligned: block_size a multiple of 8
+    bool ok = block_size % 8 == 0 && a >= 0 && a % 8 == 0 &&
+              slot_offset(a, block_size) + 8 <= block_size;
     for (int k = 1; k < 8; ++k) ok = ok && s_slot[8 * tid + k] == a + k;
     s_vec[tid] = ok;
   }
@@ -246,8 +285,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
     for (int k = 0; k < 4; ++k)
       w[k] = quant2<CODE>(widen16(IN(), e[4 * k]), widen16(IN(), e[4 * k + 1]), k_scale) |
              (quant2<CODE>(widen16(IN(), e[4 * k + 2]), widen16(IN(), e[4 * k + 3]), k_scale) << 16);
-    *reinterpret_cast<uint4*>(key_cache + ((sl / block_size) * num_kv_heads + h) * tile +
-                              ((int64_t)cc * block_size + sl % block_size) * 16) =
+    *reinterpret_cast<uint4*>(key_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
+                              ((int64_t)cc * block_size + slot_offset(sl, block_size)) * 16) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
   // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2)
@@ -266,15 +305,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
     }
     if (s_vec[half]) {
       const int64_t sl = s_slot[kb];
-      *reinterpret_cast<uint2*>(value_cache + ((sl / block_size) * num_kv_heads + h) * tile +
-                                (int64_t)d * block_size + sl % block_size) = make_uint2(v[0], v[1]);
+      *reinterpret_cast<uint2*>(value_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
+                                (int64_t)d * block_size + slot_offset(sl, block_size)) = make_uint2(v[0], v[1]);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int64_t sl = s_slot[kb + k];
         if (sl < 0) continue;
-        value_cache[((sl / block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
-                    sl % block_size] = uint8_t(v[k / 4] >> (8 * (k & 3)));
+        value_cache[(slot_block(sl, block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
+                    slot_offset(sl, block_size)] = uint8_t(v[k / 4] >> (8 * (k & 3)));
       }
     }
   }
@@ -373,6 +412,8 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
 #undef PKV_RUNS
     return hipGetLastError();
   }
+  const bool vec_both = vec && (reinterpret_cast<uintptr_t>(value) % 16 == 0) &&
+                        ((value_stride * elem_bytes) % 16 == 0);
   const dim3 grid(num_tokens), block(256);
 #define PKV_RC(E, V)                                                                          \
   hipLaunchKernelGGL((reshape_and_cache_kernel<E, V>), grid, block, 0, stream,                \
@@ -380,9 +421,9 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
                      static_cast<E*>(key_cache), static_cast<E*>(value_cache), slot_mapping, \
                      num_kv_heads, head_size, block_size, num_blocks, key_stride, value_stride)
   if (elem_bytes == 2) {
-    if (vec) PKV_RC(uint16_t, true); else PKV_RC(uint16_t, false);
+    if (vec_both) PKV_RC(uint16_t, true); else PKV_RC(uint16_t, false);
   } else {
-    if (vec) PKV_RC(uint32_t, true); else PKV_RC(uint32_t, false);
+    if (vec_both) PKV_RC(uint32_t, true); else PKV_RC(uint32_t, false);
   }
 #undef PKV_RC
   return hipGetLastError();

@@ -16,12 +16,17 @@ def _bits_equal(gpu_t, cpu_bits):
     return np.array_equal(storage_bits(gpu_t.cpu()), cpu_bits)
 
 
-@pytest.mark.parametrize("key,dtype,bs,stride_pad", [
-    ("c2", "f16", 16, 0), ("c2", "bf16", 8, 3), ("c1", "f32", 16, 4), ("c3", "bf16", 32, 0),
+@pytest.mark.parametrize("key,dtype,bs,stride_pad,shape", [
+    ("c2", "f16", 16, 0, None), ("c2", "bf16", 8, 3, None), ("c1", "f32", 16, 4, None),
+    ("c3", "bf16", 32, 0, None),
+    # rows of more than 512 16-byte chunks (more than two per thread)
+    ("c2", "bf16", 16, 0, (72, 72, 128)), ("c1", "f32", 8, 0, (24, 24, 128)),
 ])
-def test_reshape_and_cache_random_free_slots(key, dtype, bs, stride_pad):
+def test_reshape_and_cache_random_free_slots(key, dtype, bs, stride_pad, shape):
     """N tokens scattered to uniformly random free slots, some skipped (-1) and some out of range."""
-    case = make_decode_case(key, num_seqs=4, len_cap=700, dtype=dtype, block_size=bs)
+    extra = {} if shape is None else dict(num_heads=shape[0], num_kv_heads=shape[1],
+                                          head_size=shape[2])
+    case = make_decode_case(key, num_seqs=4, len_cap=700, dtype=dtype, block_size=bs, **extra)
     N = 64
     Hkv, D = case.key_cache.shape[1], case.query.shape[2]
     slots = random_free_slots(case, N)
@@ -205,3 +210,38 @@ def test_swap_odd_block_bytes():
     torch.cuda.synchronize()
     for s, d in m:
         assert torch.equal(back[s].cpu(), ref[s])
+
+
+@pytest.mark.parametrize("N", [40, 600])
+@pytest.mark.parametrize("kind", ["bf16", "f32", "e4m3", "i8"])
+def test_reshape_and_cache_block_size_not_power_of_two(kind, N):
+    """The cache write takes any block size (the attention kernels only 8, 16 and 32): 12 tokens
+    per block, one workgroup per token (40 tokens) and the many-token run path (600), with
+    consecutive runs, skipped and out-of-range slots."""
+    NB, H, D, bs = 64, 4, 64, 12
+    eight = kind in ("e4m3", "i8")
+    dt = "bf16" if eight else kind
+    x = 16 if eight else 16 // (4 if kind == "f32" else 2)
+    key = draw_normal((N, H, D), dt, 83, 0) * 2
+    val = draw_normal((N, H, D), dt, 83, 1) * 2
+    rng = np.random.default_rng(9)
+    slots = np.concatenate([np.arange(30, 30 + N // 2), rng.choice(np.arange(30 + N // 2, NB * bs),
+                                                                    N - N // 2, replace=False)])
+    slots[3], slots[N - 5] = -1, NB * bs + 1
+    cdt = torch.uint8 if eight else key.dtype
+    kc = torch.zeros((NB, H, D // x, bs, x), dtype=cdt)
+    vc = torch.zeros((NB, H, D, bs), dtype=cdt)
+    kcd, vcd = kc.to(DEV), vc.to(DEV)
+    sl = torch.from_numpy(slots.astype(np.int64)).to(DEV)
+    log(f"reshape {kind} bs{bs} N={N}")
+    ref_slots = np.where(slots < NB * bs, slots, -1)
+    kb, vb = storage_bits(kc).copy(), storage_bits(vc).copy()
+    if eight:
+        pkv.reshape_and_cache_fp8(key.to(DEV), val.to(DEV), kcd, vcd, sl, 0.02, 0.03, code=kind)
+        write = OC.reshape_and_cache_fp8 if kind == "e4m3" else OC.reshape_and_cache_int8
+        write(kb, vb, storage_bits(key), storage_bits(val), dt, ref_slots, 0.02, 0.03)
+    else:
+        pkv.reshape_and_cache(key.to(DEV), val.to(DEV), kcd, vcd, sl)
+        OC.reshape_and_cache(kb, vb, storage_bits(key), storage_bits(val), ref_slots)
+    torch.cuda.synchronize()
+    assert _bits_equal(kcd, kb) and _bits_equal(vcd, vb)
