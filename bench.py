@@ -274,6 +274,47 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def cache_ops_cpu_baseline(budget_s: float = 3.0) -> dict:
+    """The oracle's cache operations (unchanged) on the host: copy_blocks and swap_blocks over a
+    512-block cache of 160 KiB blocks (128 random pairs per call), reshape_and_cache of the
+    decode-step write of 256 tokens x 8 KV heads x 128 bf16 (block 16); each repeated until
+    its share of the time budget is spent."""
+    from oracle import cache_ops as OC
+
+    g = np.random.default_rng(11)
+    nb, pairs = 512, 128
+    cache = g.integers(0, 1 << 16, size=(nb, 40, 16, 16, 8), dtype=np.uint16)
+    host = np.zeros((pairs,) + cache.shape[1:], dtype=np.uint16)
+    perm = g.permutation(nb)
+    mapping = np.stack([perm[:pairs], perm[pairs:2 * pairs]], 1)
+    out_map = np.stack([perm[:pairs], np.arange(pairs)], 1)
+    block_bytes = cache[0].nbytes
+
+    def rate(fn, share):
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < budget_s * share:
+            fn()
+            n += 1
+        return n, time.perf_counter() - t0
+
+    n, dt = rate(lambda: OC.copy_blocks([cache], mapping), 0.3)
+    copy_gbs = 2 * n * pairs * block_bytes / dt / 1e9  # read + write, as for the device
+    n, dt = rate(lambda: OC.swap_blocks(host, cache, out_map), 0.2)
+    swap_gbs = n * pairs * block_bytes / dt / 1e9
+    kc = np.zeros((nb, 8, 16, 16, 8), dtype=np.uint16)
+    vc = np.zeros((nb, 8, 128, 16), dtype=np.uint16)
+    key = g.integers(0, 1 << 16, size=(256, 8, 128), dtype=np.uint16)
+    val = g.integers(0, 1 << 16, size=(256, 8, 128), dtype=np.uint16)
+    slots = g.choice(nb * 16, 256, replace=False)
+    n, dt = rate(lambda: OC.reshape_and_cache(kc, vc, key, val, slots), 0.5)
+    # plain numpy copies and Python loops: one thread
+    return {"kind": "oracle", "copy_blocks_GBs": round(copy_gbs, 2), "swap_GBs": round(swap_gbs, 2),
+            "reshape_tokens_per_s": round(n * 256 / dt, 1), "cores": 1,
+            "sample": "copy_blocks / swap_blocks: 128 random pairs of 160 KiB blocks in a 512-block "
+                      "host cache; reshape_and_cache: 256 tokens x 8 KV heads x 128 (bf16 bits), "
+                      f"block 16; about {budget_s:.0f} s in all"}
+
+
 def ceilings(steps: int = 20) -> None:
     """Reference rates on the running machine: the HBM read ceiling of the decode kernels' load
     type (a plain streaming read of 4 GiB), copy_blocks (device copy of whole blocks) and
@@ -318,6 +359,21 @@ def ceilings(steps: int = 20) -> None:
     block_bytes = kc[0].numel() * kc.element_size()
     ms = timed(lambda: pkv.copy_blocks([kc], [vc], mapping, stream=stream, _ptr_buffers=ptrs), steps)
     copy_gbs = 2 * 2 * pairs * block_bytes / (ms / 1e3) / 1e9  # read + write, keys and values
+    # a plain contiguous device copy of the same bytes (torch's copy kernel), for comparison
+    flat = kc.view(-1)
+    nbytes = 2 * pairs * block_bytes  # keys and values
+    n_el = nbytes // kc.element_size()
+    assert 2 * n_el <= flat.numel()
+    ms_dev = timed(lambda: flat[n_el:2 * n_el].copy_(flat[:n_el]), steps)
+    dev_copy_gbs = 2 * nbytes / (ms_dev / 1e3) / 1e9  # read + write
+    # the decode step's cache write alone: 256 tokens x 8 KV heads x 128 bf16, block 16
+    rk = torch.empty((4096, 8, 16, 16, 8), dtype=torch.bfloat16, device=dev)
+    rv = torch.empty((4096, 8, 128, 16), dtype=torch.bfloat16, device=dev)
+    nk = torch.randn((256, 8, 128), device=dev).to(torch.bfloat16)
+    nv = torch.randn((256, 8, 128), device=dev).to(torch.bfloat16)
+    rs = torch.from_numpy(np.random.default_rng(5).choice(4096 * 16, 256, replace=False)).to(dev)
+    ms_rc = timed(lambda: pkv.reshape_and_cache(nk, nv, rk, rv, rs, stream=stream), steps)
+    del rk, rv
     host = torch.empty((pairs,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
     m_out = np.stack([perm[:pairs], np.arange(pairs)], 1).astype(np.int64)
     m_in = np.stack([np.arange(pairs), perm[pairs:2 * pairs]], 1).astype(np.int64)
@@ -344,9 +400,13 @@ def ceilings(steps: int = 20) -> None:
         "stream_read_GBs": round(read_gbs, 1), "stream_read_frac_of_8TBs": round(read_gbs / HBM_PEAK_GBS, 4),
         "stream_read_back_to_back_GBs": round(read10_gbs, 1), "stream_read_bytes": 4 << 30,
         "copy_blocks_GBs": round(copy_gbs, 1), "copy_blocks_pairs": pairs, "block_bytes": block_bytes,
+        "device_contiguous_copy_GBs": round(dev_copy_gbs, 1),
+        "reshape_and_cache_256x8x128_us": round(ms_rc * 1e3, 2),
+        "reshape_and_cache_tokens_per_s": round(256 / (ms_rc / 1e3), 1),
         "swap_out_GBs": gbs(ms_out), "swap_in_GBs": gbs(ms_in), "swap_bytes": pairs * block_bytes,
         "host_link_contiguous_out_GBs": gbs(ms_lo), "host_link_contiguous_in_GBs": gbs(ms_li),
         "copy_engine_per_block_out_GBs": gbs(ms_bo), "copy_engine_per_block_in_GBs": gbs(ms_bi),
+        "cpu_baseline": cache_ops_cpu_baseline(),
     }), flush=True)
 
 
