@@ -12,6 +12,7 @@
 #include "pkv_internal.h"
 #include "pkv_kv8.h"
 #include "pkv_kv8_host.h"
+#include "pkv_swap.h"
 
 namespace pkv {
 namespace {

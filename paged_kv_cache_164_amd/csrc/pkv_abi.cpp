@@ -14,6 +14,7 @@
 #include "pkv_kv8_host.h"
 #include "pkv_prefill.h"
 #include "pkv_probe.h"
+#include "pkv_swap.h"
 
 namespace {
 
