@@ -11,9 +11,11 @@ written) divided by the step time: achieved GB/s.  `roofline` covers the dominan
 events on the stream they are launched on;
 `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded sample.
 
-The beam-search workload (c5) times its own step: copy-on-write of each beam's partial last
-block (copy_blocks), the new tokens (reshape_and_cache), then the shared-prefix decode, whose
-bytes count each shared prompt block once (the per-sequence count is reported beside).
+The beam-search workload (c5) times its own step: the shared-prefix work list (it depends on
+the groups, tables and lengths only), copy-on-write of each beam's partial last block
+(copy_blocks), the new tokens (reshape_and_cache), the shared-prefix partition kernel on that
+list, then the reduce; its bytes count each shared prompt block once (the per-sequence count
+is reported beside).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload c3]
 
@@ -616,6 +618,9 @@ def main() -> int:
         plain = not beam and not kv8
         if plain:  # the work list depends on tables and lengths only: built before the write
             pkv.paged_attention_plan(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=st)
+        if beam:  # likewise with the groups: the shared-prefix work list
+            pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
+                                            P, ws, stream=st)
         if beam:  # device pointer table made once, outside any graph capture
             pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
         if kv8:
@@ -629,14 +634,14 @@ def main() -> int:
             pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
                                            case.v_scale, lmax, P, ws, stream=st, code=code)
         elif beam:
-            pkv.paged_attention_decode_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
-                                              P, ws, stream=st)
+            pkv.paged_attention_partitions_planned_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"],
+                                                          scale, lmax, P, ws, stream=st)
         else:
             pkv.paged_attention_partitions_planned(out, q, kc, vc, bt, cl, scale, lmax, P, ws,
                                                    stream=st)
         if ev is not None:
             ev[1].record(st)
-        if not beam and not kv8:
+        if not kv8:
             pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=st)
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
@@ -684,7 +689,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": ("shared-prefix decode: plan + partition kernel + split-K reduce" if beam
+                     "kernel": ("shared-prefix partition kernel (its work list planned before the timed region)" if beam
                                 else "8-bit cache decode: plan + partition kernel + split-K reduce" if kv8
                                 else "partition kernel (its work list planned before the timed region)"),
                      "kernel_ms": round(k_avg, 5), "kernel_ms_median": round(float(np.median(k_ms)), 5),

@@ -225,6 +225,39 @@ int pkv_paged_attention_decode_shared(void* out, const void* query, const void* 
                                       int32_t dtype, int32_t partition_size, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* The shared-prefix decode in two stages, as pkv_paged_attention_plan and
+ * pkv_paged_attention_partitions_planned are for the plain one (the groups,
+ * tables and lengths of a decode step serve every layer, so one plan serves all
+ * of them):
+ *   pkv_paged_attention_plan_shared: the work-list kernel alone (prefix items
+ *     carry a group's query rows), written into `workspace`;
+ *   pkv_paged_attention_partitions_planned_shared: the attention kernel alone on
+ *     that list; with pkv_paged_attention_reduce after it (same num_seqs,
+ *     num_heads, head_size, max_context_len, dtype, partition_size, workspace),
+ *     bit-identical to pkv_paged_attention_decode_shared.
+ * Arguments and rules as for pkv_paged_attention_decode_shared.  A planned call
+ * must use the plan's group_starts, prefix_lens, num_groups, block_tables,
+ * context_lens and sizes, unchanged on the device since the plan ran (query,
+ * caches and out may change); otherwise the behaviour is undefined.  A
+ * workspace no plan has written since it was zeroed holds an empty list: the
+ * call then writes nothing. */
+int pkv_paged_attention_plan_shared(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* group_starts,
+                                    const int32_t* prefix_lens, int32_t num_groups, float scale,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t block_size,
+                                    int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+int pkv_paged_attention_partitions_planned_shared(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Decode attention over an 8-bit KV cache: keys and values stored as OCP FP8
  * E4M3 codes with one float scale per cache (key = code * k_scale, value =

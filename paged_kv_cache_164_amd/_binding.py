@@ -39,6 +39,11 @@ _SIGNATURES = {
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_decode_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
                                           + _DECODE_ARGTYPES[6:]),
+    "pkv_paged_attention_plan_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
+                                        + _DECODE_ARGTYPES[6:]),
+    "pkv_paged_attention_partitions_planned_shared": (_c_int, _DECODE_ARGTYPES[:6]
+                                                      + [_c_p, _c_p, _c_int]
+                                                      + _DECODE_ARGTYPES[6:]),
     "pkv_paged_attention_decode_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                        + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_decode_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
@@ -196,6 +201,15 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
                                   partition_size=0, workspace=None, stream=None):
     """Decode where the sequences [group_starts[g], group_starts[g+1]) share their first
     prefix_lens[g] tokens' blocks: each shared block is read once per group."""
+    _shared_call("pkv_paged_attention_decode_shared", out, query, key_cache, value_cache,
+                 block_tables, context_lens, group_starts, prefix_lens, scale, max_context_len,
+                 partition_size, workspace, stream)
+    return out
+
+
+def _shared_call(name, out, query, key_cache, value_cache, block_tables, context_lens,
+                 group_starts, prefix_lens, scale, max_context_len, partition_size, workspace,
+                 stream):
     args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                             max_context_len, partition_size, workspace, stream)
     _on_gpu(group_starts, prefix_lens)
@@ -205,8 +219,31 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
             or not (group_starts.is_contiguous() and prefix_lens.is_contiguous())):
         raise PKVError("group_starts must be int32 [num_groups + 1], prefix_lens int32 [num_groups]")
     args = args[:6] + (group_starts.data_ptr(), prefix_lens.data_ptr(), ng) + args[6:]
-    _check(library().pkv_paged_attention_decode_shared(*args), "pkv_paged_attention_decode_shared")
-    return out
+    _check(getattr(library(), name)(*args), name)
+    return ws
+
+
+def paged_attention_plan_shared(out, query, key_cache, value_cache, block_tables, context_lens,
+                                group_starts, prefix_lens, scale, max_context_len,
+                                partition_size=0, workspace=None, stream=None):
+    """The shared-prefix work-list kernel alone; returns the workspace holding the list (for
+    paged_attention_partitions_planned_shared calls with the same groups, tables and lengths)."""
+    return _shared_call("pkv_paged_attention_plan_shared", out, query, key_cache, value_cache,
+                        block_tables, context_lens, group_starts, prefix_lens, scale,
+                        max_context_len, partition_size, workspace, stream)
+
+
+def paged_attention_partitions_planned_shared(out, query, key_cache, value_cache, block_tables,
+                                              context_lens, group_starts, prefix_lens, scale,
+                                              max_context_len, partition_size=0, workspace=None,
+                                              stream=None):
+    """The shared-prefix attention kernel alone, on the list a paged_attention_plan_shared call
+    left in workspace (paged_attention_reduce completes the decode)."""
+    if workspace is None:
+        raise PKVError("a planned call needs the workspace its plan was written to")
+    return _shared_call("pkv_paged_attention_partitions_planned_shared", out, query, key_cache,
+                        value_cache, block_tables, context_lens, group_starts, prefix_lens, scale,
+                        max_context_len, partition_size, workspace, stream)
 
 
 def paged_attention_prefill_workspace_size(num_seqs: int, num_tokens: int, num_heads: int,

@@ -346,13 +346,17 @@ int pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   }
 }
 
-int pkv_paged_attention_decode_shared(
-    void* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
-    const int32_t* prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-    int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+#define PKV_SHARED_PARAMS                                                                     \
+  void *out, const void *query, const void *key_cache, const void *value_cache,               \
+      const int32_t *block_tables, const int32_t *context_lens, const int32_t *group_starts,  \
+      const int32_t *prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,          \
+      int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,         \
+      int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,                 \
+      int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream
+
+// The shared-prefix decode, whole (mode 0: plan, attention kernel, reduce), the plan alone
+// (mode 1) or the attention kernel on the plan already in the workspace (mode 2).
+static int decode_shared_mode(PKV_SHARED_PARAMS, int mode) {
   try {
     Resolved r;
     const Groups groups{group_starts, prefix_lens, num_groups};
@@ -360,12 +364,31 @@ int pkv_paged_attention_decode_shared(
     if (rc != PKV_OK) return rc;
     if (num_seqs == 0) return PKV_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    r.args.plan_mode = mode;
     rc = launch_phase1(r, dtype, head_size, block_size, s);
-    if (rc != PKV_OK) return rc;
+    if (rc != PKV_OK || mode != 0) return rc;
     return launch_phase2(r, dtype, head_size, s);
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+#define PKV_SHARED_ARGS                                                                       \
+  out, query, key_cache, value_cache, block_tables, context_lens, group_starts, prefix_lens,  \
+      num_groups, scale, num_seqs, num_heads, num_kv_heads, head_size, block_size,            \
+      max_num_blocks_per_seq, max_context_len, dtype, partition_size, workspace,              \
+      workspace_bytes, stream
+
+int pkv_paged_attention_decode_shared(PKV_SHARED_PARAMS) {
+  return decode_shared_mode(PKV_SHARED_ARGS, 0);
+}
+
+int pkv_paged_attention_plan_shared(PKV_SHARED_PARAMS) {
+  return decode_shared_mode(PKV_SHARED_ARGS, 1);
+}
+
+int pkv_paged_attention_partitions_planned_shared(PKV_SHARED_PARAMS) {
+  return decode_shared_mode(PKV_SHARED_ARGS, 2);
 }
 
 static int decode_kv8(void* out, const void* query, const void* key_cache, const void* value_cache,

@@ -115,3 +115,61 @@ def test_shared_prefix_repeatable_and_workspace_reuse():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     _check_vs_oracle(c, a, "workspace reuse")
+
+
+def _planned_layers(c, P, layers):
+    """One shared-prefix plan, then for each layer's (query, caches) the attention kernel on it
+    and the reduce."""
+    _, _, _, bt, cl = _gpu_inputs(c)
+    gs = torch.from_numpy(c.group_starts).to(DEV)
+    pl = torch.from_numpy(c.prefix_lens).to(DEV)
+    L = int(c.context_lens.max())
+    q0, kc0, vc0 = layers[0]
+    need = pkv.paged_attention_workspace_size(len(c.context_lens), q0.shape[1], q0.shape[2], L, P)
+    ws = torch.full((max(need, 256),), 0xCD, dtype=torch.uint8, device=DEV)
+    pkv.paged_attention_plan_shared(torch.empty_like(q0), q0, kc0, vc0, bt, cl, gs, pl, c.scale,
+                                    L, P, ws)
+    outs = []
+    for q, kc, vc in layers:
+        out = torch.full_like(q, float("nan"))
+        pkv.paged_attention_partitions_planned_shared(out, q, kc, vc, bt, cl, gs, pl, c.scale, L,
+                                                      P, ws)
+        pkv.paged_attention_reduce(out, cl, L, ws, P)
+        outs.append(out)
+    return outs
+
+
+@pytest.mark.parametrize("dtype,D,bs,Hq,Hkv,sizes,prefixes,private,P",
+                         [CASES[0], CASES[1], CASES[4], CASES[5]])
+def test_shared_plan_reused_across_layers(dtype, D, bs, Hq, Hkv, sizes, prefixes, private, P):
+    """One plan_shared, three layers (other queries and caches over the same tables, groups and
+    lengths): each layer's planned kernel + reduce equals decode_shared bit for bit, and the first
+    layer matches the oracle."""
+    c = make_prefix_case(sizes, prefixes, private, num_heads=Hq, num_kv_heads=Hkv, head_size=D,
+                         block_size=bs, dtype=dtype)
+    q, kc, vc, bt, cl = _gpu_inputs(c)
+    layers = [(q, kc, vc), (q.flip(-1).contiguous(), -kc, vc * 2), (q * 0.5, kc * 2, -vc)]
+    log(f"shared plan reuse {dtype} D={D} bs={bs} {Hq}/{Hkv} P={P}")
+    got = _planned_layers(c, P, layers)
+    for i, (lq, lk, lv) in enumerate(layers):
+        ref = _shared(c, P, (lq, lk, lv, bt, cl))
+        torch.cuda.synchronize()
+        assert torch.equal(got[i].view(torch.int16), ref.view(torch.int16)), f"layer {i}"
+    _check_vs_oracle(c, got[0], "planned shared, layer 0")
+
+
+def test_shared_planned_call_on_an_unplanned_workspace_writes_nothing():
+    c = make_prefix_case([4, 2], [512, 160], (0, 700), num_heads=8, num_kv_heads=8,
+                         head_size=128, block_size=16, dtype="f16")
+    q, kc, vc, bt, cl = _gpu_inputs(c)
+    gs = torch.from_numpy(c.group_starts).to(DEV)
+    pl = torch.from_numpy(c.prefix_lens).to(DEV)
+    L = int(c.context_lens.max())
+    need = pkv.paged_attention_workspace_size(len(c.context_lens), 8, 128, L, 256)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_partitions_planned_shared(out, q, kc, vc, bt, cl, gs, pl, c.scale, L, 256,
+                                                  ws)
+    pkv.paged_attention_reduce(out, cl, L, ws, 256)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
