@@ -615,12 +615,15 @@ def main() -> int:
 
     def step(ev=None, st=None):
         st = stream if st is None else st
-        plain = not beam and not kv8
-        if plain:  # the work list depends on tables and lengths only: built before the write
-            pkv.paged_attention_plan(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=st)
-        if beam:  # likewise with the groups: the shared-prefix work list
+        # the work list depends on tables, lengths (and groups) only: built before the write
+        if kv8:
+            pkv.paged_attention_plan_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale, case.v_scale,
+                                         lmax, P, ws, stream=st, code=code)
+        elif beam:
             pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
                                             P, ws, stream=st)
+        else:
+            pkv.paged_attention_plan(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=st)
         if beam:  # device pointer table made once, outside any graph capture
             pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
         if kv8:
@@ -631,8 +634,9 @@ def main() -> int:
         if ev is not None:
             ev[0].record(st)
         if kv8:
-            pkv.paged_attention_decode_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
-                                           case.v_scale, lmax, P, ws, stream=st, code=code)
+            pkv.paged_attention_partitions_planned_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
+                                                       case.v_scale, lmax, P, ws, stream=st,
+                                                       code=code)
         elif beam:
             pkv.paged_attention_partitions_planned_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"],
                                                           scale, lmax, P, ws, stream=st)
@@ -641,8 +645,7 @@ def main() -> int:
                                                    stream=st)
         if ev is not None:
             ev[1].record(st)
-        if not kv8:
-            pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=st)
+        pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=st)
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
@@ -690,7 +693,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": ("shared-prefix partition kernel (its work list planned before the timed region)" if beam
-                                else "8-bit cache decode: plan + partition kernel + split-K reduce" if kv8
+                                else "8-bit cache partition kernel (its work list planned before the timed region)" if kv8
                                 else "partition kernel (its work list planned before the timed region)"),
                      "kernel_ms": round(k_avg, 5), "kernel_ms_median": round(float(np.median(k_ms)), 5),
                      "kernel_ms_p10_p90":

@@ -304,6 +304,43 @@ int pkv_paged_attention_decode_int8(void* out, const void* query, const void* ke
                                     int32_t dtype, int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* The 8-bit decode in two stages, as pkv_paged_attention_plan and
+ * pkv_paged_attention_partitions_planned are for the 16-bit one: the work-list
+ * kernel alone (pkv_paged_attention_plan_fp8 / _int8), then the attention
+ * kernel alone on that list (pkv_paged_attention_partitions_planned_fp8 /
+ * _int8), then pkv_paged_attention_reduce (same num_seqs, num_heads, head_size,
+ * max_context_len, dtype, partition_size, workspace): bit-identical to
+ * pkv_paged_attention_decode_fp8 / _int8.  Arguments and rules as for those
+ * calls; a planned call must use the tables, lengths and sizes of its plan,
+ * unchanged on the device since the plan ran (query, caches, scales and out may
+ * change), otherwise the behaviour is undefined.  A workspace no plan has
+ * written since it was zeroed holds an empty list: the call then writes
+ * nothing. */
+int pkv_paged_attention_plan_fp8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_partitions_planned_fp8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_plan_int8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_partitions_planned_int8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Multi-query paged attention: chunked prefill and mixed prefill / decode
  * batches.  The query rows of num_seqs requests are flattened; request b owns

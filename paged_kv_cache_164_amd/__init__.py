@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_shared,
     paged_attention_partitions_planned_shared,
+    paged_attention_partitions_planned_fp8,
     paged_attention_decode_fp8,
     paged_attention_decode_int8,
     paged_attention_prefill,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     paged_attention_partitions,
     paged_attention_partitions_planned,
     paged_attention_plan,
+    paged_attention_plan_fp8,
     paged_attention_plan_shared,
     paged_attention_reduce,
     paged_attention_workspace_size,

@@ -48,6 +48,14 @@ _SIGNATURES = {
                                        + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_decode_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                         + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_plan_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                        + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_partitions_planned_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                        + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_plan_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                        + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_partitions_planned_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                        + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
     "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
                                     + [_c_p, _c_sz, _c_p]),
@@ -329,6 +337,35 @@ def paged_attention_decode_fp8(out, query, key_cache, value_cache, block_tables,
     args = args[:7] + (float(k_scale), float(v_scale)) + args[7:]
     _check(getattr(library(), name)(*args), name)
     return out
+
+
+def paged_attention_plan_fp8(out, query, key_cache, value_cache, block_tables, context_lens,
+                             scale, k_scale, v_scale, max_context_len, partition_size=0,
+                             workspace=None, stream=None, code="e4m3"):
+    """The 8-bit decode's work-list kernel alone; returns the workspace holding the list (for
+    paged_attention_partitions_planned_fp8 calls with the same tables, lengths and shapes)."""
+    name = "pkv_paged_attention_plan_" + _kv8_entry(code)
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream, kv8=True)
+    args = args[:7] + (float(k_scale), float(v_scale)) + args[7:]
+    _check(getattr(library(), name)(*args), name)
+    return ws
+
+
+def paged_attention_partitions_planned_fp8(out, query, key_cache, value_cache, block_tables,
+                                           context_lens, scale, k_scale, v_scale, max_context_len,
+                                           partition_size=0, workspace=None, stream=None,
+                                           code="e4m3"):
+    """The 8-bit attention kernel alone, on the list a paged_attention_plan_fp8 call left in
+    workspace (paged_attention_reduce completes the decode)."""
+    if workspace is None:
+        raise PKVError("a planned call needs the workspace its plan was written to")
+    name = "pkv_paged_attention_partitions_planned_" + _kv8_entry(code)
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream, kv8=True)
+    args = args[:7] + (float(k_scale), float(v_scale)) + args[7:]
+    _check(getattr(library(), name)(*args), name)
+    return ws
 
 
 def paged_attention_decode_int8(out, query, key_cache, value_cache, block_tables, context_lens,

@@ -391,19 +391,22 @@ int pkv_paged_attention_partitions_planned_shared(PKV_SHARED_PARAMS) {
   return decode_shared_mode(PKV_SHARED_ARGS, 2);
 }
 
+// The 8-bit decode, whole (mode 0), the plan alone (mode 1) or the attention kernel on the plan
+// already in the workspace (mode 2).
 static int decode_kv8(void* out, const void* query, const void* key_cache, const void* value_cache,
                       const int32_t* block_tables, const int32_t* context_lens, float scale,
                       const Kv8& kv8, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                       int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,
                       int32_t max_context_len, int32_t dtype, int32_t partition_size,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream, int mode) {
   try {
     Resolved r;
     int rc = resolve_decode(PKV_DECODE_ARGS, &r, nullptr, &kv8);
     if (rc != PKV_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    r.args.plan_mode = mode;
     rc = launch_phase1(r, dtype, head_size, block_size, s);
-    if (rc != PKV_OK) return rc;
+    if (rc != PKV_OK || mode != 0) return rc;
     return launch_phase2(r, dtype, head_size, s);
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
@@ -417,18 +420,34 @@ static int decode_kv8(void* out, const void* query, const void* key_cache, const
       int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,                    \
       int32_t max_context_len, int32_t dtype, int32_t partition_size, void *workspace,          \
       size_t workspace_bytes, void *stream
-#define PKV_DECODE_KV8_CALL(CODE)                                                               \
+#define PKV_DECODE_KV8_CALL(CODE, MODE)                                                         \
   decode_kv8(out, query, key_cache, value_cache, block_tables, context_lens, scale,             \
              Kv8{k_scale, v_scale, CODE}, num_seqs, num_heads, num_kv_heads, head_size,         \
              block_size, max_num_blocks_per_seq, max_context_len, dtype, partition_size,        \
-             workspace, workspace_bytes, stream)
+             workspace, workspace_bytes, stream, MODE)
 
 int pkv_paged_attention_decode_fp8(PKV_DECODE_KV8_PARAMS) {
-  return PKV_DECODE_KV8_CALL(pkv::kCodeE4M3);
+  return PKV_DECODE_KV8_CALL(pkv::kCodeE4M3, 0);
 }
 
 int pkv_paged_attention_decode_int8(PKV_DECODE_KV8_PARAMS) {
-  return PKV_DECODE_KV8_CALL(pkv::kCodeI8);
+  return PKV_DECODE_KV8_CALL(pkv::kCodeI8, 0);
+}
+
+int pkv_paged_attention_plan_fp8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeE4M3, 1);
+}
+
+int pkv_paged_attention_partitions_planned_fp8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeE4M3, 2);
+}
+
+int pkv_paged_attention_plan_int8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeI8, 1);
+}
+
+int pkv_paged_attention_partitions_planned_int8(PKV_DECODE_KV8_PARAMS) {
+  return PKV_DECODE_KV8_CALL(pkv::kCodeI8, 2);
 }
 
 int pkv_paged_attention_partitions(PKV_DECODE_PARAMS) {

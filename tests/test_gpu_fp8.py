@@ -171,3 +171,36 @@ def test_reshape_and_cache_kv8_many_tokens(dtype, bs, code):
                         case.k_scale, case.v_scale)
     assert np.array_equal(kc.cpu().numpy(), kb)
     assert np.array_equal(vc.cpu().numpy(), vb)
+
+
+@pytest.mark.parametrize("code", CODES)
+@pytest.mark.parametrize("P", [0, 512])
+def test_kv8_plan_reused_across_layers(code, P):
+    """One 8-bit plan, three layers (other queries and scales over the same tables and lengths):
+    each layer's planned kernel + reduce equals the whole 8-bit decode bit for bit; the first
+    layer matches the oracle."""
+    case = with_8bit_cache(make_decode_case("c3", num_seqs=24, len_cap=5000), code)
+    q = case.query.to(DEV)
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+    L, ks, vs = case.max_context_len, case.k_scale, case.v_scale
+    pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
+                              case.slot_mapping.to(DEV), ks, vs, code=code)
+    layers = [(q, ks, vs), (q.flip(-1).contiguous(), 2 * ks, 0.5 * vs), (q * 0.5, ks, 3 * vs)]
+    need = pkv.paged_attention_workspace_size(q.shape[0], q.shape[1], q.shape[2], L, P)
+    ws = torch.full((max(need, 256),), 0xCD, dtype=torch.uint8, device=DEV)
+    log(f"{code} plan reuse P={P}")
+    pkv.paged_attention_plan_fp8(torch.empty_like(q), q, kc, vc, bt, cl, case.scale, ks, vs, L, P,
+                                 ws, code=code)
+    for i, (lq, lks, lvs) in enumerate(layers):
+        got = torch.full_like(q, float("nan"))
+        pkv.paged_attention_partitions_planned_fp8(got, lq, kc, vc, bt, cl, case.scale, lks, lvs,
+                                                   L, P, ws, code=code)
+        pkv.paged_attention_reduce(got, cl, L, ws, P)
+        ref = torch.full_like(q, float("nan"))
+        pkv.paged_attention_decode_fp8(ref, lq, kc, vc, bt, cl, case.scale, lks, lvs, L, P,
+                                       code=code)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"layer {i}"
+        if i == 0:
+            _check(case, got, _oracle(case), f"{code} planned layer 0")
