@@ -54,13 +54,13 @@ def test_workspace_size():
     assert pkv.paged_attention_workspace_size(4, 8, 64, 100, -1) == 0
 
 
-def _shared(lib, **over):
+def _shared(lib, entry="pkv_paged_attention_decode_shared", **over):
     args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
                 group_starts=1, prefix_lens=1, num_groups=1, scale=0.125, num_seqs=2, num_heads=8,
                 num_kv_heads=8, head_size=64, block_size=16, max_blocks=4, max_context_len=64,
                 dtype=1, partition_size=0, workspace=None, ws_bytes=0, stream=None)
     args.update(over)
-    return lib.pkv_paged_attention_decode_shared(*args.values())
+    return getattr(lib, entry)(*args.values())
 
 
 @pytest.mark.parametrize("over,code", [
@@ -72,19 +72,22 @@ def _shared(lib, **over):
     (dict(num_groups=3), -1),                    # more groups than sequences
     (dict(), -4),                                # needs a workspace
 ])
-def test_shared_decode_argument_errors(over, code):
+@pytest.mark.parametrize("entry", ["pkv_paged_attention_decode_shared",
+                                   "pkv_paged_attention_plan_shared",
+                                   "pkv_paged_attention_partitions_planned_shared"])
+def test_shared_decode_argument_errors(entry, over, code):
     lib = _lib()
-    assert _shared(lib, **over) == code
+    assert _shared(lib, entry, **over) == code
     assert lib.pkv_last_error().decode() != ""
 
 
-def _decode(lib, **over):
+def _decode(lib, entry="pkv_paged_attention_decode", **over):
     args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1,
                 scale=0.125, num_seqs=2, num_heads=8, num_kv_heads=8, head_size=64, block_size=16,
                 max_blocks=4, max_context_len=64, dtype=0, partition_size=0, workspace=None,
                 ws_bytes=0, stream=None)
     args.update(over)
-    return lib.pkv_paged_attention_decode(*args.values())
+    return getattr(lib, entry)(*args.values())
 
 
 @pytest.mark.parametrize("over,code", [
@@ -101,9 +104,12 @@ def _decode(lib, **over):
     (dict(max_context_len=4096), -4),    # needs a workspace
     (dict(num_heads=24, num_kv_heads=8, dtype=0), -2),   # group 3 unsupported for fp32
 ])
-def test_decode_argument_errors(over, code):
+@pytest.mark.parametrize("entry", ["pkv_paged_attention_decode", "pkv_paged_attention_plan",
+                                   "pkv_paged_attention_partitions_planned",
+                                   "pkv_paged_attention_partitions"])
+def test_decode_argument_errors(entry, over, code):
     lib = _lib()
-    assert _decode(lib, **over) == code
+    assert _decode(lib, entry, **over) == code
     assert lib.pkv_last_error().decode() != ""
 
 
@@ -198,7 +204,8 @@ def test_prefill_nothing_to_do():
     assert _prefill(lib, num_seqs=0, num_tokens=0) == 0
 
 
-@pytest.mark.parametrize("entry", ["pkv_paged_attention_decode_fp8", "pkv_paged_attention_decode_int8"])
+@pytest.mark.parametrize("entry", [f"pkv_paged_attention_{stage}_{fmt}" for fmt in ("fp8", "int8")
+                                   for stage in ("decode", "plan", "partitions_planned")])
 @pytest.mark.parametrize("over,code", [
     (dict(k_scale=0.0), -1),
     (dict(v_scale=float("nan")), -1),
