@@ -317,6 +317,16 @@ def cache_ops_cpu_baseline(budget_s: float = 3.0) -> dict:
                       f"block 16; about {budget_s:.0f} s in all"}
 
 
+def auto_partition_label(elem_bytes: int, block_size: int, kv8: bool, max_context_len: int) -> str:
+    """The decode entries' auto partition size (include/pkv.h), for the JSON line."""
+    if elem_bytes != 2:
+        return "auto: 1024"
+    max_blocks = 256 if kv8 else 128
+    if max_context_len >= 32768 and block_size * max_blocks >= 4096:
+        return "auto: 4096"
+    return "auto: 2048" if block_size * max_blocks >= 2048 else "auto: 1024"
+
+
 def ceilings(steps: int = 20) -> None:
     """Reference rates on the running machine: the HBM read ceiling of the decode kernels' load
     type (a plain streaming read of 4 GiB), copy_blocks (device copy of whole blocks) and
@@ -684,7 +694,7 @@ def main() -> int:
                                + (f"; KV cache as {KV8_NAMES[args.kv]} codes with per-cache scales" if kv8 else ""),
                    "num_seqs": B,
                    "num_heads": Hq, "num_kv_heads": Hkv, "head_size": D, "block_size": bs,
-                   "partition_size": P or ("auto: 2048" if eb == 2 and (bs >= 16 or kv8) else "auto: 1024"),
+                   "partition_size": P or auto_partition_label(eb, bs, kv8, lmax),
                    "kv_tokens": int(lens.sum()), "max_context_len": lmax,
                    "step_bytes": step_bytes, "timing": "graph replay" if args.graph else "eager"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

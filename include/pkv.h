@@ -92,6 +92,7 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  *                in {1, 2, 4, 8} for PKV_F32, 1..16 for PKV_F16/PKV_BF16
  *   max_context_len  host upper bound of context_lens (sizes the grid)
  *   partition_size   0 = auto: 2048 for PKV_F16/PKV_BF16 with block_size >= 16,
+ *                4096 instead with block_size 32 when max_context_len >= 32768,
  *                else 1024; otherwise a multiple of block_size in
  *                [block_size, 4096], at most 128 blocks for PKV_F16/PKV_BF16;
  *                at most 8192 partitions per sequence
@@ -274,7 +275,8 @@ int pkv_paged_attention_partitions_planned_shared(
  * All other arguments, the partitioning, the workspace
  * (pkv_paged_attention_workspace_size) and the error codes as for
  * pkv_paged_attention_decode, except the partition size: auto is 2048 for
- * every block size, and a partition may span up to 256 blocks.  Group sizes
+ * every block size (4096 with block_size 16 or 32 when max_context_len >=
+ * 32768), and a partition may span up to 256 blocks.  Group sizes
  * 1..16.
  */
 int pkv_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,

@@ -108,7 +108,8 @@ int resolve_decode(void* out, const void* query, const void* key_cache, const vo
       (partition_size > 0 && (partition_size < block_size || partition_size % block_size != 0)))
     return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of block_size in [block_size, 4096]");
   const int P = partition_size > 0 ? partition_size
-                                   : pkv::auto_partition(use_mfma, kv8 != nullptr, block_size);
+                                   : pkv::auto_partition(use_mfma, kv8 != nullptr, block_size,
+                                                         max_context_len);
   if (kv8 && P > pkv::kMaxItemBlocks8 * block_size)
     return fail(PKV_ERR_INVALID_ARG, "partition_size may span at most 256 blocks (8-bit cache)");
   if (use_mfma && !kv8 && P > pkv::kMaxItemBlocks * block_size)

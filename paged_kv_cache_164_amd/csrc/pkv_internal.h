@@ -18,13 +18,19 @@ constexpr int kThreads = 256;  // VALU workgroup: 4 wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;  // logits are kept in base-2 units
 
-// partition_size 0 ("auto"): 2048 tokens on the matrix cores when an item's block ids fit its
-// lane registers (block_size >= 16 for a 16-bit cache, >= 8 for an 8-bit one), else 1024.
-// (4096-token items of an 8-bit cache carry the same bytes as 2048 of a 16-bit one; they are
-// faster for a few very long contexts but slower for many mixed ones, so auto stays at 2048.)
-inline int auto_partition(bool mfma, bool kv8, int block_size) {
+// partition_size 0 ("auto"): on the matrix cores, 2048 tokens when an item's block ids fit its
+// lane registers (block_size >= 16 for a 16-bit cache, >= 8 for an 8-bit one), else 1024; and
+// for very long contexts (max_context_len >= kLongContext) 4096 where the ids fit (block_size
+// 32 for a 16-bit cache, >= 16 for an 8-bit one): fewer, longer items halve the per-item
+// overhead and the partials to merge (8 x 131072 tokens, block 32: 703 vs 717 us for the
+// 16-bit kernel, 389 vs 403 us for the 8-bit one), while for many mixed lengths of a few
+// thousand tokens 4096-token items were slower (8-bit, block 16: 285 vs 269 us).
+constexpr int kLongContext = 32768;
+inline int auto_partition(bool mfma, bool kv8, int block_size, int max_context_len) {
   const int max_blocks = kv8 ? kMaxItemBlocks8 : kMaxItemBlocks;
-  return (mfma && block_size * max_blocks >= 2048) ? 2048 : 1024;
+  if (!mfma) return 1024;
+  if (max_context_len >= kLongContext && block_size * max_blocks >= 4096) return 4096;
+  return block_size * max_blocks >= 2048 ? 2048 : 1024;
 }
 // Remainders (the tokens after a range's last whole partition) are cut into chunks of at most
 // ceil(P / 2) rounded up to whole blocks, so the last items of a call are short.
