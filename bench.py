@@ -327,6 +327,70 @@ def auto_partition_label(elem_bytes: int, block_size: int, kv8: bool, max_contex
     return "auto: 2048" if block_size * max_blocks >= 2048 else "auto: 1024"
 
 
+def block_manager_session(bm, prompts: int = 32, beams: int = 4, prompt_len: int = 3000,
+                          steps: int = 64, swap_every: int = 16, swap_seqs: int = 8) -> int:
+    """A beam-search session on a block manager (the library's or the oracle's): each prompt
+    allocated, forked into `beams` sequences, `steps` decode appends per sequence (copy-on-write
+    on the first append after a fork), every `swap_every` steps `swap_seqs` sequences swapped out
+    and back in, then everything freed.  Returns the number of manager calls made."""
+    calls = 0
+    seqs = []
+    for p in range(prompts):
+        sid = p * beams
+        bm.allocate(sid, prompt_len)
+        calls += 1
+        seqs.append(sid)
+        for k in range(1, beams):
+            bm.fork(sid, sid + k)
+            calls += 1
+            seqs.append(sid + k)
+    for t in range(steps):
+        for sid in seqs:
+            bm.append(sid)
+            calls += 1
+        if (t + 1) % swap_every == 0:
+            group = seqs[(t * swap_seqs) % len(seqs):][:swap_seqs]
+            bm.swap_out(group)
+            bm.swap_in(group)
+            calls += 2
+    for sid in seqs:
+        bm.free(sid)
+        calls += 1
+    return calls
+
+
+def block_manager_bench(repeats: int = 5) -> None:
+    """Host block manager rates: the library (C++ behind the C ABI, called through the Python
+    binding) and the oracle's Python manager on the same session."""
+    import paged_kv_cache_164_amd as pkv
+    from oracle.block_manager import OracleBlockManager
+
+    def run(make, n):
+        best = None
+        for _ in range(n):
+            bm = make()
+            t0 = time.perf_counter()
+            calls = block_manager_session(bm)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+            if hasattr(bm, "close"):
+                bm.close()
+        return calls, best
+
+    calls, dt_lib = run(lambda: pkv.BlockManager(16, 65536, 16384), repeats)
+    _, dt_or = run(lambda: OracleBlockManager(16, 65536, 16384), max(1, repeats // 2))
+    print(json.dumps({
+        "block_manager": "host operations per second, best of several sessions",
+        "session": "32 prompts x 3000 tokens, 4 beams each (fork), 64 decode appends per beam "
+                   "(copy-on-write after the fork), 8 sequences swapped out and in every 16 "
+                   "steps, all freed; block 16, 65536 GPU + 16384 CPU blocks",
+        "calls": calls, "library_calls_per_s": round(calls / dt_lib, 1),
+        "library_session_ms": round(dt_lib * 1e3, 2),
+        "cpu_baseline": {"kind": "oracle", "calls_per_s": round(calls / dt_or, 1),
+                         "session_ms": round(dt_or * 1e3, 2), "cores": 1},
+    }), flush=True)
+
+
 def ceilings(steps: int = 20) -> None:
     """Reference rates on the running machine: the HBM read ceiling of the decode kernels' load
     type (a plain streaming read of 4 GiB), copy_blocks (device copy of whole blocks) and
@@ -562,6 +626,8 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mib", type=int, default=0)
     ap.add_argument("--derive-traffic", nargs=4, metavar="CSV")
     ap.add_argument("--calibration-mib", type=int, default=512)
+    ap.add_argument("--block-manager", action="store_true",
+                    help="print host block-manager rates (library and oracle) instead")
     ap.add_argument("--ceilings", action="store_true",
                     help="print reference rates (streaming read, block copy, host-link swap) instead")
     args = ap.parse_args()
@@ -575,6 +641,9 @@ def main() -> int:
 
     if args.ceilings:
         ceilings()
+        return 0
+    if args.block_manager:
+        block_manager_bench()
         return 0
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
