@@ -7,9 +7,10 @@
 // which equals the softmax-weighted sum over the whole context (the log-sum-exp identity
 // behind split-K / FlashDecoding decoding; the "Vllm" page, "Prefill vs decoding" item 5).
 //
-// One workgroup per (sequence, query head).  Its threads form S strands of D/4 threads; a
-// thread holds 4 dims of one strand, and strand s takes items s, s + S, ... with its own
-// running maximum (so all of its loads go out at once, with no workgroup-wide max first).  The
+// One workgroup per (sequence, query head): one wave for many rows, else 256 threads.  Its
+// threads form S strands of D/4 threads; a thread holds 4 dims of one strand, and strand s takes
+// items s, s + S, ..., four loaded at a time, with its own running maximum (so its loads go out
+// together, with no workgroup-wide max first).  The
 // strands are then merged in LDS, always in strand order: the result is run-to-run
 // deterministic.
 #include "pkv_device.h"
@@ -18,10 +19,10 @@
 namespace pkv {
 namespace {
 
-template <class DT, int D>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
+template <class DT, int D, int T>
+__global__ __launch_bounds__(T) void reduce_kernel(DecodeArgs a) {
   constexpr int TPS = D / 4;           // threads per strand (4 dims each)
-  constexpr int S = kThreads / TPS;    // strands
+  constexpr int S = T / TPS;           // strands
   const int row = blockIdx.x;          // b * num_heads + h
   const int b = row / a.num_heads;
   const int NP = min(a.np_of[b], a.slots);
@@ -35,17 +36,30 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   // strand s: online merge of its items (running max ms, sum ls, vector acc)
   float ms = -INFINITY, ls = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q = s; q < NP; q += S) {
-    const float mq = pm[q], lq = pl[q];
-    const float4 aq = *reinterpret_cast<const float4*>(pacc + (int64_t)q * D);
-    const float mn = fmaxf(ms, mq);
-    const float c = exp2f(ms - mn), w = exp2f(mq - mn);  // ms = -inf at first: c = 0
-    ls = fmaf(ls, c, w * lq);
-    acc.x = fmaf(acc.x, c, w * aq.x);
-    acc.y = fmaf(acc.y, c, w * aq.y);
-    acc.z = fmaf(acc.z, c, w * aq.z);
-    acc.w = fmaf(acc.w, c, w * aq.w);
-    ms = mn;
+  // U of the strand's items loaded at once, then merged in item order
+  constexpr int U = 4;
+  for (int q0 = s; q0 < NP; q0 += U * S) {
+    float mq[U], lq[U];
+    float4 aq[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = min(q0 + u * S, NP - 1);  // past the end: a valid index, its values unused
+      mq[u] = pm[q];
+      lq[u] = pl[q];
+      aq[u] = *reinterpret_cast<const float4*>(pacc + (int64_t)q * D);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q0 + u * S >= NP) break;
+      const float mn = fmaxf(ms, mq[u]);
+      const float c = exp2f(ms - mn), w = exp2f(mq[u] - mn);  // ms = -inf at first: c = 0
+      ls = fmaf(ls, c, w * lq[u]);
+      acc.x = fmaf(acc.x, c, w * aq[u].x);
+      acc.y = fmaf(acc.y, c, w * aq[u].y);
+      acc.z = fmaf(acc.z, c, w * aq[u].z);
+      acc.w = fmaf(acc.w, c, w * aq[u].w);
+      ms = mn;
+    }
   }
   __shared__ float s_m[S], s_l[S];
   __shared__ float4 s_acc[S][TPS];
@@ -80,10 +94,19 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(DecodeArgs a) {
   store_elem(DT(), a.out, o + 3, num.w * inv);
 }
 
+// Workgroup shape by row count: many rows (a large batch, few items each) take one wave per
+// row, so every row is resident in one round; few rows with many partials each keep 256 threads
+// (more strands, more loads in flight per row).
+constexpr int64_t kWaveRowsFrom = 4096;
+
 template <class DT, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_heads)),
-                     dim3(kThreads), 0, stream, a);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
+  if (rows >= kWaveRowsFrom)
+    hipLaunchKernelGGL((reduce_kernel<DT, D, 64>), dim3((unsigned)rows), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<DT, D, kThreads>), dim3((unsigned)rows), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
