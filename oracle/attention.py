@@ -184,40 +184,41 @@ def shared_prefix_length(context_lens: np.ndarray, start: int, stop: int, prefix
     return pre - pre % block_size
 
 
+def check_shared_prefix_groups(block_tables: np.ndarray, context_lens: np.ndarray, group_starts,
+                               prefix_lens, block_size: int) -> None:
+    """Raise ValueError unless the groups satisfy the shared-prefix contract.
+
+    Groups are consecutive runs of sequences [group_starts[g], group_starts[g + 1]) that cover
+    [0, B) once, in order (an empty group is allowed).  Members of a group hold the same physical blocks for their shared tokens
+    [0, pre), pre = shared_prefix_length(...): the block table entries of every member equal
+    the first member's for the pre / block_size logical blocks (PagedAttention's block sharing:
+    beams or samples forked from one prompt point at the prompt's blocks, mlqm.cn explainer,
+    "PagedAttention", and the fork of the AIGC interview book, section 23).  Entries past the
+    rounded prefix may differ (a partial last block is copied on write)."""
+    starts = [int(s) for s in group_starts]
+    B = len(context_lens)
+    if len(starts) != len(prefix_lens) + 1 or starts[0] != 0 or starts[-1] != B or any(
+            b < a for a, b in zip(starts, starts[1:])):
+        raise ValueError("group_starts must be non-decreasing from 0 to num_seqs")
+    for g in range(len(prefix_lens)):
+        s0, s1 = starts[g], starts[g + 1]
+        pre = shared_prefix_length(context_lens, s0, s1, int(prefix_lens[g]), block_size)
+        n = pre // block_size
+        for b in range(s0 + 1, s1):
+            if not np.array_equal(block_tables[b, :n], block_tables[s0, :n]):
+                raise ValueError(f"sequence {b} does not share group {g}'s first {n} blocks")
+
+
 def shared_prefix_decode(query_bits: np.ndarray, key_bits: np.ndarray, value_bits: np.ndarray,
                          dtype: str, block_tables: np.ndarray, context_lens: np.ndarray,
-                         scale: float, group_starts, prefix_lens, partition_size: int) -> np.ndarray:
-    """Decode of sequences grouped by a shared prompt prefix, with the prefix read once.
+                         scale: float, group_starts, prefix_lens) -> np.ndarray:
+    """Decode of sequences grouped by a shared prompt prefix.
 
-    Group g is the sequences [group_starts[g], group_starts[g + 1]).  Its shared tokens
-    [0, pre) are gathered from the first member's block table only and cut into partitions
-    [p P, min((p + 1) P, pre)); each member's own tokens [pre, L) are gathered from its own
-    table and cut into [pre + j P, ...).  Every member's partition statistics are combined
-    with the log-sum-exp rule (split-K, "Vllm" page, "Prefill vs decoding" item 5).  When the
-    members' tables really hold the same blocks for the prefix, this equals paged_decode.
-    """
-    B, Hq, D = query_bits.shape
-    Hkv = key_bits.shape[1]
-    group = Hq // Hkv
-    bs = key_bits.shape[3]
-    sc = as_scale(scale)
-    P = partition_size
-    out = np.zeros((B, Hq, D))
-    for g in range(len(prefix_lens)):
-        s0, s1 = int(group_starts[g]), int(group_starts[g + 1])
-        pre = shared_prefix_length(context_lens, s0, s1, int(prefix_lens[g]), bs)
-        for kvh in range(Hkv):
-            Kp, Vp = gather_kv(key_bits, value_bits, dtype, block_tables[s0], pre, kvh)
-            for b in range(s0, s1):
-                L = int(context_lens[b])
-                if L == 0:
-                    continue
-                K, V = gather_kv(key_bits, value_bits, dtype, block_tables[b], L, kvh)
-                for h in range(kvh * group, (kvh + 1) * group):
-                    q = widen(query_bits[b, h], dtype)
-                    stats = [partition_stats(q, Kp, Vp, sc, t0, min(t0 + P, pre))
-                             for t0 in range(0, pre, P)]
-                    stats += [partition_stats(q, K, V, sc, t0, min(t0 + P, L))
-                              for t0 in range(pre, L, P)]
-                    out[b, h] = combine_partitions(stats)
-    return out
+    Reading the shared blocks once per group is a change of memory traffic, not of the result:
+    inside the contract (check_shared_prefix_groups, which raises outside it) every member's
+    output is the plain paged decode of its own table and length.  So the oracle checks the
+    contract and then computes that definition."""
+    check_shared_prefix_groups(block_tables, context_lens, group_starts, prefix_lens,
+                               key_bits.shape[3])
+    return paged_decode(query_bits, key_bits, value_bits, dtype, block_tables, context_lens,
+                        scale)

@@ -59,6 +59,25 @@ def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB) -> str:
     return lib_path
 
 
+# Host-only test helper: runs the kernels' address functions (csrc/pkv_tile_addr.h) on the CPU.
+TILECHECK_SRC = os.path.join(os.path.dirname(HERE), "tests", "native", "tile_check.hip")
+TILECHECK_LIB = os.path.join(os.path.dirname(HERE), "tests", "native", "libpkv_tilecheck.so")
+
+
+def build_tilecheck(verbose: bool = False) -> str:
+    cmd = [HIPCC, "--offload-host-only", "-x", "hip", "-O2", "-std=c++17", "-shared", "-fPIC",
+           "-Wall", "-Wno-unused-function", f"-I{CSRC}", f"-I{INCLUDE}", TILECHECK_SRC, "-o",
+           TILECHECK_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {TILECHECK_SRC}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(TILECHECK_LIB + ".tmp", TILECHECK_LIB)
+    if verbose:
+        print(f"built {TILECHECK_LIB}")
+    return TILECHECK_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_tilecheck(verbose=True)
     sys.exit(0)

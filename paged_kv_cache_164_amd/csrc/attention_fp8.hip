@@ -23,6 +23,7 @@
 #include "pkv_device.h"
 #include "pkv_kv8.h"
 #include "pkv_internal.h"
+#include "pkv_tile_addr.h"
 #include "pkv_kv8_host.h"
 
 namespace pkv {
@@ -70,8 +71,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   const int lane = threadIdx.x & 63;
   // The item's block ids (at most 256) go to four lane registers.
   const int32_t* bt = a.block_tables + (int64_t)b0 * a.max_blocks + tok0 / BS;
-  const int row_left = a.max_blocks - tok0 / BS;
-  const int nmax = min(P / BS, row_left);
+  const int nmax = item_id_count(P, BS, a.max_blocks, tok0);
   const int ids0 = (lane < nmax) ? bt[lane] : 0;
   const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
   const int ids2 = (128 + lane < nmax) ? bt[128 + lane] : 0;
@@ -132,33 +132,26 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
 #pragma unroll
     for (int k = 0; k < NBT; ++k) cand[k] = int(block_of(j0 + k));
     // A lane whose token lies past the item's last block (a tile can reach beyond it) reads
-    // block 0 instead: table entries there are not block ids; its data is masked.  The block
-    // of tile token t is chosen by a select tree on t / BS (a compare chain over four
-    // candidates was turned into an indexed scratch array).
-    auto pick = [&](int t) -> int64_t {
-      int r = cand[0];
-      if constexpr (NBT == 2) {
-        r = (t >= BS) ? cand[1] : cand[0];
-      } else if constexpr (NBT == 4) {
-        const int j = t / BS;
-        const int lo = (j & 1) ? cand[1] : cand[0], hi = (j & 1) ? cand[3] : cand[2];
-        r = (j & 2) ? hi : lo;
-      }
-      return (t0 + t < nslots) ? int64_t(r) : int64_t(0);
+    // block 0 instead: table entries there are not block ids; its data is masked (kv8_pick,
+    // pkv_tile_addr.h).  The block of tile token t is chosen by a select tree on t / BS (a
+    // compare chain over four candidates was turned into an indexed scratch array).
+    auto pick = [&](int t) {
+      return kv8_pick<BS>(cand[0], cand[NBT > 1 ? 1 : 0], cand[NBT > 2 ? 2 : 0],
+                          cand[NBT > 3 ? 3 : 0], t0, t, nslots);
     };
-    const bool pad = t0 > last * TT;
-    const char* kp0 = (pad ? a.prefetch_pad : kbase + pick(ktok0) * block_bytes) + (ktok0 % BS) * 16;
-    const char* kp1 = (pad ? a.prefetch_pad : kbase + pick(ktok1) * block_bytes) + (ktok1 % BS) * 16;
-    const char* vp = (pad ? a.prefetch_pad : vbase + pick(vtok) * block_bytes) + (vtok % BS);
+    const bool pad = kv8_pad(t0, last);
+    const char* kp0 = (pad ? a.prefetch_pad : kbase + pick(ktok0) * block_bytes) + kv8_key_row<BS>(ktok0);
+    const char* kp1 = (pad ? a.prefetch_pad : kbase + pick(ktok1) * block_bytes) + kv8_key_row<BS>(ktok1);
+    const char* vp = (pad ? a.prefetch_pad : vbase + pick(vtok) * block_bytes) + kv8_value_run<BS>(vtok);
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
       const int64_t c = quad + 4 * j;
-      tl.k[0][j] = kv_load<true>(reinterpret_cast<const uint4*>(kp0 + c * BS * 16));
-      tl.k[1][j] = kv_load<true>(reinterpret_cast<const uint4*>(kp1 + c * BS * 16));
+      tl.k[0][j] = kv_load<true>(reinterpret_cast<const uint4*>(kp0 + kv8_key_chunk<BS>(c)));
+      tl.k[1][j] = kv_load<true>(reinterpret_cast<const uint4*>(kp1 + kv8_key_chunk<BS>(c)));
     }
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
-      tl.v[i] = kv_load<true>(reinterpret_cast<const uint2*>(vp + (int64_t)(i * 16 + col) * BS));
+      tl.v[i] = kv_load<true>(reinterpret_cast<const uint2*>(vp + kv8_value_row<BS>(i * 16 + col)));
   };
 
   Tile T0, T1, T2, T3;

@@ -30,6 +30,7 @@
 // Column c is query head (c % G) of KV head kh in sequence b0 + c / G.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_tile_addr.h"
 
 #include <algorithm>
 
@@ -95,8 +96,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
   const int32_t* bt = a.block_tables + (int64_t)b0 * a.max_blocks + tok0 / BS;
   // The item's block ids (at most 128) go to two lane registers (entries past the row's end
   // are never read; entries past the context are unused).
-  const int row_left = a.max_blocks - tok0 / BS;
-  const int nmax = min(P / BS, row_left);
+  const int nmax = item_id_count(P, BS, a.max_blocks, tok0);
   const int ids0 = (lane < nmax) ? bt[lane] : 0;
   const int ids1 = (64 + lane < nmax) ? bt[64 + lane] : 0;
   const int h0 = kh * G;
@@ -133,38 +133,24 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
   // Loads are issued without branches (a load under a branch makes the compiler wait for every
   // outstanding load at the next use, which would serialise the double buffering).  With
   // block_size >= 16 every lane of a tile below ntok lies inside the partition's blocks; with
-  // block_size 8 a lane past the last block reads block 0 and masks the data to zero.
+  // block_size 8 a lane past the last block reads block 0 and masks the data to zero
+  // (gqa_lane, pkv_tile_addr.h).
   auto load_tile = [&](int t0, Tile& tl) {
-    int64_t kblk, vblk;
-    int koff, voff;
-    bool kvalid = true, vvalid = true;
-    if constexpr (BS >= 16) {
-      kblk = vblk = block_of(t0 / BS);
-      koff = t0 % BS + col;
-      voff = t0 % BS + quad * 4;
-    } else {
-      const int64_t lo = block_of(t0 / BS), hi = block_of(t0 / BS + 1);
-      kvalid = t0 + col < nslots;
-      vvalid = t0 + quad * 4 < nslots;
-      kblk = !kvalid ? 0 : (col < BS) ? lo : hi;
-      vblk = !vvalid ? 0 : (quad * 4 < BS) ? lo : hi;
-      koff = col % BS;
-      voff = (quad * 4) % BS;
-    }
+    const GqaLane ln = gqa_lane<BS>(t0, col, quad, nslots, last, block_of(t0 / BS),
+                                    BS < 16 ? block_of(t0 / BS + 1) : 0);
     // Tiles past the last one (the ring's prefetches at the end of the item) read the small
     // shared prefetch pad of the workspace instead, which stays in L2: no branch, no HBM re-read.
-    const bool pad = t0 > last * 16;
-    const char* kp = (pad ? a.prefetch_pad : kbase + kblk * block_bytes) + koff * 16;
-    const char* vp = (pad ? a.prefetch_pad : vbase + vblk * block_bytes) + voff * 2;
-    const uint32_t km = kvalid ? ~0u : 0u, vm = vvalid ? ~0u : 0u;
+    const char* kp = (ln.pad ? a.prefetch_pad : kbase + ln.kblk * block_bytes) + ln.koff * 16;
+    const char* vp = (ln.pad ? a.prefetch_pad : vbase + ln.vblk * block_bytes) + ln.voff * 2;
+    const uint32_t km = ln.kvalid ? ~0u : 0u, vm = ln.vvalid ? ~0u : 0u;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      tl.k[kc] = kv_load<kStream>(reinterpret_cast<const uint4*>(kp + (int64_t)(kc * 4 + quad) * BS * 16));
+      tl.k[kc] = kv_load<kStream>(reinterpret_cast<const uint4*>(kp + gqa_key_chunk<BS>(kc, quad)));
       if constexpr (BS < 16) tl.k[kc] = make_uint4(tl.k[kc].x & km, tl.k[kc].y & km, tl.k[kc].z & km, tl.k[kc].w & km);
     }
 #pragma unroll
     for (int i = 0; i < NDT; ++i) {
-      tl.v[i] = kv_load<kStream>(reinterpret_cast<const uint2*>(vp + (int64_t)(i * 16 + col) * BS * 2));
+      tl.v[i] = kv_load<kStream>(reinterpret_cast<const uint2*>(vp + gqa_value_row<BS>(i, col)));
       if constexpr (BS < 16) tl.v[i] = make_uint2(tl.v[i].x & vm, tl.v[i].y & vm);
     }
   };

@@ -28,6 +28,7 @@
 // items[i] = (b0, nseq | slot << 8, begin, end).
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_tile_addr.h"
 
 #include <algorithm>
 
@@ -116,10 +117,8 @@ __device__ __forceinline__ GroupSpan group_span(const DecodeArgs& a, int g, int 
   return r;
 }
 
-// Items of a token range of length n: whole partitions, then remainder chunks of at most Q.
-__device__ __forceinline__ int whole_parts(int n, int P) { return n / P; }
-// Size class of a chunk of n (1 <= n <= Q) tokens: 1 (longest) .. 8 (shortest).
-__device__ __forceinline__ int chunk_class(int n, int Q) { return 1 + min(7, (Q - n) * 8 / Q); }
+// Items of a token range: whole partitions, then remainder chunks of at most Q
+// (whole_parts, chunk_end, chunk_class: pkv_tile_addr.h).
 
 // Per-thread counters (or next positions) of the item classes.  Classes are selected with
 // unrolled compare-and-add, never by a run-time array index, so the counters stay in registers.
@@ -167,7 +166,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
   auto count_range = [&](int s, int e, int mult) {
     const int F = whole_parts(e - s, P);
     c.add(0, F * mult);
-    for (int t0 = s + F * P; t0 < e; t0 += Q) c.add(chunk_class(min(Q, e - t0), Q), mult);
+    for (int t0 = s + F * P; t0 < e; t0 += Q) c.add(chunk_class(chunk_end(t0, e, Q) - t0, Q), mult);
   };
   for (int g = g0; g < g1; ++g) {
     const GroupSpan sp = group_span(a, g, bs);
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
       }
     }
     for (int t0 = s + F * P; t0 < e; t0 += Q, ++slot) {
-      const int t1 = min(t0 + Q, e);
+      const int t1 = chunk_end(t0, e, Q);
       put(chunk_class(t1 - t0, Q), b0, nseq, slot, t0, t1);
     }
     return slot;

@@ -65,6 +65,60 @@ def test_oracle_watermark_closed_form():
     assert bm.can_allocate(0) == OK
 
 
+def _check_can_append(bm, free):
+    """`free` is the hand-counted number of free GPU blocks."""
+    assert bm.can_append(free - 1) is True
+    assert bm.can_append(free) is True          # a step may use every free block
+    assert bm.can_append(free + 1) is False
+
+
+def test_oracle_can_append_closed_form():
+    """can_append_slots of the interview book (section 23, running / swapped queues): each
+    running sequence may need one new block in a decode step, so the step may go ahead while
+    the number of sequences is at most the number of free GPU blocks.  Free blocks counted by
+    hand after allocate, fork, a copy-on-write append and a swap out and back."""
+    bm = OracleBlockManager(4, 10, 10)
+    _check_can_append(bm, 10)
+    bm.allocate(1, 9)            # 3 blocks (0, 1, 2)
+    _check_can_append(bm, 7)
+    bm.fork(1, 2)                # shares all three
+    _check_can_append(bm, 7)
+    slot, cow = bm.append(1)     # token 9 lands in shared block 2: copy on write into block 3
+    assert cow == (2, 3) and slot == 3 * 4 + 1
+    _check_can_append(bm, 6)
+    bm.append(2)                 # block 2 is now only sequence 2's: written in place
+    _check_can_append(bm, 6)
+    bm.append(1)
+    bm.append(1)
+    bm.append(1)                 # token 12 opens a fourth logical block: block 4
+    _check_can_append(bm, 5)
+    pairs = bm.swap_out([1, 2])  # distinct blocks 0, 1, 3, 4 (sequence 1), 2 (sequence 2)
+    assert [b for b, _ in pairs] == [0, 1, 3, 4, 2]
+    _check_can_append(bm, 10)
+    bm.swap_in([1, 2])
+    _check_can_append(bm, 5)
+    bm.free(1)                   # blocks 0 and 1 stay held by sequence 2; 3 and 4 come free
+    _check_can_append(bm, 7)
+
+
+@pytest.mark.parametrize("n", range(1, 9))
+def test_oracle_can_append_matches_worst_case_appends(n):
+    """Brute force of the worst case the check guards: n sequences whose last blocks are full
+    each need a new block for their next token.  With 5 blocks free, can_append(n) holds exactly
+    when all n appends succeed."""
+    bm = OracleBlockManager(4, n + 5)
+    for sid in range(n):
+        bm.allocate(sid, 4)
+    ok = bm.can_append(n)
+    try:
+        for sid in range(n):
+            bm.append(sid)
+        done = True
+    except BlockError:
+        done = False
+    assert ok == done == (n <= 5)
+
+
 class _Memory:
     """Token-level content of both pools: physical slots hold token values.  Replays the
     cache operations the manager plans (writes at slots, copy-on-write block copies, swap

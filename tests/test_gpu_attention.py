@@ -1,9 +1,9 @@
 """GPU parity of paged decode attention (reshape_and_cache of the step's new tokens, then
 decode) against the fp64 oracle, through the C ABI.
 
-Sizes: every workload at a size the oracle covers completely (several partitions, a
-ragged last block), and every workload at its full size with sampled (sequence, head)
-outputs, in the launch configuration the benchmark times (auto partition size).
+Sizes: every workload at a size the oracle covers in a few seconds (several partitions, a
+ragged last block), and every workload at its full size with every (sequence, head) output
+compared, in the launch configuration the benchmark times (auto partition size).
 """
 import dataclasses
 
@@ -12,9 +12,10 @@ import pytest
 import torch
 
 import paged_kv_cache_164_amd as pkv
-from gpu_cases import (DEV, GpuDecode, log, oracle_after_write, oracle_decode, sample_pairs,
+from gpu_cases import (DEV, GpuDecode, log, oracle_after_write, oracle_decode,
                        within_tolerance)
-from workloads import make_decode_case
+import tilecheck as TC
+from workloads import DTYPES, decode_layout, make_decode_case
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +63,8 @@ def test_c4_long_splitk_bf16_small(P):
 
 @pytest.mark.parametrize("P", [16, 48, 80, 256, 512, 1024, 2048])
 def test_partition_sizes(P):
-    """Whole partitions of P tokens and remainder chunks of ceil(P / 4) rounded up to blocks
-    (48 -> chunks of 16, 80 -> chunks of 32: three per remainder)."""
+    """Whole partitions of P tokens and remainder chunks of at most ceil(P / 2) rounded up to
+    whole blocks (48 -> chunks of 32, 80 -> chunks of 48: two per remainder)."""
     _run_and_check(make_decode_case("c3", num_seqs=6, len_cap=5000), P, tag=f"c3 P={P}")
 
 
@@ -90,12 +91,39 @@ def test_shape_variants(dtype, D, bs, heads):
     _run_and_check(case, tag=f"variant {dtype} D{D} bs{bs} {heads}")
 
 
-# ---------------------------------------------------------------- full size, sampled outputs
+# ---------------------------------------------------------------- full size, every output
+
+# One full-size case and its oracle output at a time: c4's two partition sizes share them.
+# The oracle's cache write lands in the CPU case tensors; a second GPU step on the same case
+# writes the same new tokens to the same slots again, so it sees the same cache.
+_FULL = {}
+
+
+def _full_case_and_oracle(key):
+    if key not in _FULL:
+        _FULL.clear()
+        case = make_decode_case(key)
+        log(f"[{key} full] oracle over all {case.num_seqs} x {case.query.shape[1]} outputs")
+        kb, vb = oracle_after_write(case)
+        _FULL[key] = (case, oracle_decode(case, kb, vb))
+    return _FULL[key]
+
 
 @pytest.mark.parametrize("key,P", [("c2", 0), ("c3", 0), ("c4", 0), ("c4", 512)])
-def test_full_size_sampled(key, P):
-    case = make_decode_case(key)
-    _run_and_check(case, P, pairs=sample_pairs(case, 48, seed=1), tag=f"{key} full P={P}")
+def test_full_size_all_outputs(key, P):
+    """Each workload at its full size, every (sequence, head) output against the oracle, in the
+    launch configuration the benchmark times (auto partitions) and, for the long-context
+    workload, the 512-token partitions it states."""
+    case, ref = _full_case_and_oracle(key)
+    log(f"[{key} full P={P}] B={case.num_seqs} Lmax={case.max_context_len}")
+    out = GpuDecode(case, P).step()
+    torch.cuda.synchronize()
+    got = out.cpu().to(torch.float64).numpy()
+    ok, err, ratio = within_tolerance(got, ref, case.cfg.dtype)
+    log(f"[{key} full P={P}] max|err|={err:.3e} worst err/bound={ratio:.3f} over {got.size} elements")
+    assert ok, f"{key} full P={P}: max|err| {err} exceeds tolerance (ratio {ratio})"
+    if key == "c4" and P == 512:
+        _FULL.clear()
 
 
 # ---------------------------------------------------------------- properties on the GPU
@@ -198,3 +226,52 @@ def test_gqa_matches_mha_with_repeated_kv_on_gpu():
     diff = (gqa - mha.to(torch.float64)).abs().max().item()
     log(f"GQA vs repeated-KV MHA: max diff {diff:.3e}")
     assert torch.equal(gqa.to(torch.bfloat16).view(torch.int16), mha.view(torch.int16))
+
+
+@pytest.mark.parametrize("key,over,P,groups", [
+    ("c3", {}, 0, None), ("c4", {}, 512, None), ("c4", {}, 0, None), ("c2", {}, 0, None),
+    ("c3", dict(num_seqs=6, len_cap=5000), 80, None),
+    ("c3", dict(lens=[0, 1, 15, 16, 17, 2047, 2048, 2049, 4095], block_size=8), 0, None),
+    ("c3", dict(lens=[300, 300, 290, 500, 40, 40, 2100, 2200, 2300, 0]), 256,
+     ([0, 3, 4, 6, 9, 10], [288, 0, 32, 2048, 0])),
+])
+def test_device_plan_matches_host_planner(key, over, P, groups):
+    """The plan kernel's work list equals, as a set, the host planner's that the address check
+    (tests/test_tile_addresses.py) runs over; the per-sequence item counts agree too."""
+    lay = decode_layout(key, **over)
+    cfg = lay.cfg
+    B, Hq, Hkv, D, bs = len(lay.lens), cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.block_size
+    lens = lay.lens.astype(np.int32)
+    Lmax = int(lens.max())
+    dt = DTYPES[cfg.dtype]
+    x = cfg.x
+    q = torch.zeros((B, Hq, D), dtype=dt, device=DEV)
+    kc = torch.zeros((1, Hkv, D // x, bs, x), dtype=dt, device=DEV)   # the plan reads no cache
+    vc = torch.zeros((1, Hkv, D, bs), dtype=dt, device=DEV)
+    bt = torch.from_numpy(lay.tables).to(DEV)
+    cl = torch.from_numpy(lens).to(DEV)
+    need = pkv.paged_attention_workspace_size(B, Hq, D, Lmax, P)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    log(f"plan {key} {over} P={P} groups={groups is not None}: B={B} Lmax={Lmax}")
+    per_item = 1
+    if groups is None:
+        pkv.paged_attention_plan(torch.empty_like(q), q, kc, vc, bt, cl, 1.0, Lmax, P, ws)
+        gs = pl = None
+    else:
+        gs, pl = groups
+        per_item = 16 // (Hq // Hkv)
+        pkv.paged_attention_plan_shared(torch.empty_like(q), q, kc, vc, bt, cl,
+                                        torch.tensor(gs, dtype=torch.int32, device=DEV),
+                                        torch.tensor(pl, dtype=torch.int32, device=DEV), 1.0, Lmax,
+                                        P, ws)
+    torch.cuda.synchronize()
+    host = ws.cpu().numpy()
+    n = int(host[4:8].view(np.uint32)[0])
+    off = TC.items_offset(B, Hq, D, Lmax, P)
+    dev_items = host[off:off + 16 * n].view(np.uint32).reshape(n, 4)
+    coff = TC.counts_offset(B, Hq, D, Lmax, P)
+    dev_counts = host[coff:coff + 4 * B].view(np.int32)
+    P_eff = TC.partition(False, bs, Lmax, P)
+    items, counts = TC.plan(lens, bs, P_eff, min(Lmax, lay.tables.shape[1] * bs), gs, pl, per_item)
+    assert sorted(map(tuple, dev_items.tolist())) == sorted(map(tuple, items.tolist()))
+    assert dev_counts.tolist() == counts.tolist()

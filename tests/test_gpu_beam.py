@@ -122,5 +122,6 @@ def test_beam_small_all_outputs():
     _beam_run(num_prompts=4)
 
 
-def test_beam_full_size_sampled():
-    _beam_run(num_prompts=32, n_pairs=64)
+def test_beam_full_size_all_outputs():
+    """32 prompts x 4 beams at full size: every (sequence, head) output against the oracle."""
+    _beam_run(num_prompts=32)

@@ -122,7 +122,7 @@ def test_full_chunked_prefill_workload_sampled(P):
     U[0, 7168] cached ones, 32 / 8 heads, head 128, block 16, bf16): sampled (row, head)
     pairs against the oracle, including each request's first and last rows."""
     reqs = draw_prefill_requests()
-    case = make_prefill_case(reqs, poison=False)
+    case = make_prefill_case(reqs)
     log(f"chunked prefill workload: {case.num_tokens} rows, max context {case.max_context_len}, P={P}")
     out, _, _ = _gpu_step(case, P)
     torch.cuda.synchronize()

@@ -308,10 +308,11 @@ def _random_shared(seed, sizes=(3, 1, 2), prefixes=(8, 0, 12), Hq=4, Hkv=2, D=16
                 prefixes=np.asarray(prefixes, dtype=np.int32))
 
 
-def _shared(c, P, prefixes=None):
+def _shared(c, prefixes=None, starts=None):
     return OA.shared_prefix_decode(_bits(c["q"]), _bits(c["kc"]), _bits(c["vc"]), c["dtype"],
-                                   c["tables"], c["lens"], c["scale"], c["starts"],
-                                   c["prefixes"] if prefixes is None else prefixes, P)
+                                   c["tables"], c["lens"], c["scale"],
+                                   c["starts"] if starts is None else starts,
+                                   c["prefixes"] if prefixes is None else prefixes)
 
 
 def test_shared_prefix_length_rule():
@@ -323,38 +324,46 @@ def test_shared_prefix_length_rule():
     assert OA.shared_prefix_length(lens, 2, 4, 8, 4) == 4     # capped by L = 5, rounded down
 
 
-@pytest.mark.parametrize("P", [4, 8, 12, 512])
-def test_shared_prefix_equals_monolithic(P):
-    """Prefix read once from the first member's table + own tokens == plain attention."""
+def test_shared_prefix_decode_is_the_plain_decode():
+    """Inside the contract the grouped call has the plain decode's result (prefix lengths that
+    end inside a block are cut back to whole blocks and still qualify)."""
     c = _random_shared(21)
     mono = _oracle(c)
-    assert np.max(np.abs(_shared(c, P) - mono)) <= 1e-12
-    # prefix lengths that end inside a block are cut back to whole blocks
-    assert np.max(np.abs(_shared(c, P, np.array([10, 3, 15], dtype=np.int32)) - mono)) <= 1e-12
+    assert np.array_equal(_shared(c), mono)
+    assert np.array_equal(_shared(c, np.array([10, 3, 15], dtype=np.int32)), mono)
 
 
-def test_shared_prefix_without_sharing_is_the_partitioned_decode():
-    c = _random_shared(22, sizes=(1, 1, 1, 1), prefixes=(8, 4, 0, 12))
-    part = OA.partitioned_decode(_bits(c["q"]), _bits(c["kc"]), _bits(c["vc"]), "bf16",
-                                 c["tables"], c["lens"], c["scale"], 8)
-    assert np.array_equal(_shared(c, 8), part)
-
-
-def test_shared_prefix_reads_the_first_members_blocks():
-    """The prefix comes from the group's first table row only: a member whose table points
-    elsewhere for the prefix still sees the first member's prefix blocks."""
+def test_shared_prefix_contract_refuses_diverging_tables():
+    """A member whose table points elsewhere below the rounded prefix breaks the contract: the
+    oracle refuses it (what the kernel does with such input is unspecified)."""
     c = _random_shared(23, sizes=(2,), prefixes=(8,), max_priv=6)
     bs = c["kc"].shape[3]
-    alt = c["tables"].copy()
-    # move member 1's prefix to fresh copies holding different keys
-    NB = c["kc"].shape[0]
-    kc = torch.cat([c["kc"], -c["kc"][alt[1, :2]]])
-    vc = torch.cat([c["vc"], c["vc"][alt[1, :2]]])
-    alt[1, :2] = [NB, NB + 1]
-    c2 = dict(c, kc=kc, vc=vc, tables=alt)
-    got = _shared(c2, 512)
-    same = _oracle(dict(c2, tables=c["tables"]))  # member 1 reading member 0's prefix blocks
-    own = _oracle(c2)                             # member 1 reading its own (negated) keys
-    assert np.max(np.abs(got - same)) <= 1e-12
-    assert np.max(np.abs(got[1] - own[1])) > 1e-3
     assert 2 * bs == 8
+    # member 1's second prefix block moved to a fresh copy holding other keys
+    alt = c["tables"].copy()
+    NB = c["kc"].shape[0]
+    c2 = dict(c, kc=torch.cat([c["kc"], -c["kc"][alt[1, 1:2]]]),
+              vc=torch.cat([c["vc"], c["vc"][alt[1, 1:2]]]), tables=alt)
+    alt[1, 1] = NB
+    with pytest.raises(ValueError, match="does not share"):
+        _shared(c2)
+    # a divergence at or past the rounded prefix is allowed: with prefix 7 only block 0 is
+    # shared (7 rounds down to 4 tokens), so member 1 may own block 1
+    got = _shared(c2, np.array([7], dtype=np.int32))
+    assert np.all(np.isfinite(got)) and np.array_equal(got, _oracle(c2))
+
+
+@pytest.mark.parametrize("starts", [[0, 1], [1, 2], [0, 2, 1, 2], [0, 3]])
+def test_shared_prefix_contract_refuses_bad_groups(starts):
+    """Groups must cover the sequences once, in order."""
+    c = _random_shared(24, sizes=(2,), prefixes=(8,), max_priv=6)
+    prefixes = np.zeros(len(starts) - 1, dtype=np.int32)
+    with pytest.raises(ValueError, match="group_starts"):
+        _shared(c, prefixes, np.asarray(starts, dtype=np.int32))
+
+
+def test_shared_prefix_contract_allows_empty_groups_and_singletons():
+    c = _random_shared(25, sizes=(1, 2, 1), prefixes=(0, 8, 4), max_priv=6)
+    starts = np.array([0, 1, 1, 3, 4], dtype=np.int32)   # an empty group between 0 and 1
+    prefixes = np.array([0, 64, 8, 4], dtype=np.int32)
+    assert np.array_equal(_shared(c, prefixes, starts), _oracle(c))

@@ -199,16 +199,20 @@ def poison_slots(key_cache: torch.Tensor, value_cache: torch.Tensor, block_id: i
     value_cache[block_id, :, :, first_off:last_off] = float("nan")
 
 
-def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optional[int] = None,
-                     lens: Optional[Sequence[int]] = None, poison: bool = True,
-                     **overrides) -> DecodeCase:
-    """Build one decode step of config ``key`` (c1..c4).
+@dataclasses.dataclass
+class DecodeLayout:
+    """Lengths and block tables of a decode step, without any cache contents."""
+    cfg: DecodeConfig
+    lens: np.ndarray        # int64 [B]
+    tables: np.ndarray      # int32 [B, max_blocks], -1 past each sequence's blocks
+    num_blocks: int         # pool size
+    used: np.ndarray        # physical ids in use, in assignment order
+    free: np.ndarray        # physical ids not referenced by any table
 
-    ``num_seqs`` keeps the first sequences of the full draw (same lengths);
-    ``len_cap`` clips lengths, for oracle-sized parity cases; ``lens`` replaces
-    the drawn lengths outright; ``overrides`` replace config fields (shapes,
-    dtype, pool) for variants outside the five workloads.
-    """
+
+def decode_layout(key: str, *, num_seqs: Optional[int] = None, len_cap: Optional[int] = None,
+                  lens: Optional[Sequence[int]] = None, **overrides) -> DecodeLayout:
+    """The lengths and block tables make_decode_case draws (same arguments, same streams)."""
     cfg = dataclasses.replace(CONFIGS[key], **overrides) if overrides else CONFIGS[key]
     if lens is not None:
         lens = np.asarray(lens, dtype=np.int64)
@@ -219,7 +223,7 @@ def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optio
     if len_cap is not None:
         lens = np.minimum(lens, len_cap)
     B = len(lens)
-    bs, Hq, Hkv, D, x = cfg.block_size, cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.x
+    bs = cfg.block_size
     nblk = (lens + bs - 1) // bs
     n_used = int(nblk.sum())
     NB = _pool_size(cfg, n_used)
@@ -232,6 +236,23 @@ def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optio
     for b in range(B):
         tables[b, :nblk[b]] = used[off:off + nblk[b]]
         off += nblk[b]
+    return DecodeLayout(cfg, lens, tables, NB, used, free)
+
+
+def make_decode_case(key: str, *, num_seqs: Optional[int] = None, len_cap: Optional[int] = None,
+                     lens: Optional[Sequence[int]] = None, poison: bool = True,
+                     **overrides) -> DecodeCase:
+    """Build one decode step of config ``key`` (c1..c4).
+
+    ``num_seqs`` keeps the first sequences of the full draw (same lengths);
+    ``len_cap`` clips lengths, for oracle-sized parity cases; ``lens`` replaces
+    the drawn lengths outright; ``overrides`` replace config fields (shapes,
+    dtype, pool) for variants outside the five workloads.
+    """
+    lay = decode_layout(key, num_seqs=num_seqs, len_cap=len_cap, lens=lens, **overrides)
+    cfg, lens, tables, NB, used, free = lay.cfg, lay.lens, lay.tables, lay.num_blocks, lay.used, lay.free
+    B = len(lens)
+    bs, Hq, Hkv, D, x = cfg.block_size, cfg.num_heads, cfg.num_kv_heads, cfg.head_size, cfg.x
 
     tdt = DTYPES[cfg.dtype]
     fill = float("nan") if poison else 0.0
