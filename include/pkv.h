@@ -67,7 +67,7 @@ enum pkv_swap_direction { PKV_SWAP_IN = 0 /* host -> device */, PKV_SWAP_OUT = 1
  * Long contexts are split (split-K decoding, the "Vllm" page, "Prefill vs
  * decoding" item 5 on FlashDecoding): each sequence into whole partitions of P
  * = partition_size tokens, and the tokens after its last whole partition into
- * chunks of Q = ceil(P / 4) tokens rounded up to whole blocks (short work
+ * chunks of at most Q = ceil(P / 2) tokens rounded up to whole blocks (short work
  * items for the end of the call).  Each piece is handled by its own
  * workgroup per KV head; a sequence with several pieces gets its output from
  * a second kernel that merges them in token order with the log-sum-exp rule.

@@ -139,6 +139,16 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream):
+    """The torch stream object of `stream` (None: torch's current stream; a raw handle is wrapped
+    as an external stream)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
 def _on_gpu(*ts: torch.Tensor) -> None:
     for t in ts:
         if not t.is_cuda:
@@ -497,14 +507,22 @@ def copy_blocks(key_caches: Sequence[torch.Tensor], value_caches: Sequence[torch
             raise PKVError("all caches must be contiguous with equal block counts and block bytes")
     if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise PKVError("block_mapping must be int64 [num_pairs, 2]")
-    if _ptr_buffers is None:
-        kp = torch.tensor([c.data_ptr() for c in key_caches], dtype=torch.int64, device=ref.device)
-        vp = torch.tensor([c.data_ptr() for c in value_caches], dtype=torch.int64, device=ref.device)
-    else:
-        kp, vp = _ptr_buffers
-    bm = block_mapping.contiguous()
+    # The pointer tables (and a contiguous copy of the mapping) are made on the launch stream, so
+    # the kernel sees them written; when that is not torch's current stream, the allocator is told
+    # they are in use there until the kernel has run.
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if _ptr_buffers is None:
+            kp = torch.tensor([c.data_ptr() for c in key_caches], dtype=torch.int64, device=ref.device)
+            vp = torch.tensor([c.data_ptr() for c in value_caches], dtype=torch.int64, device=ref.device)
+        else:
+            kp, vp = _ptr_buffers
+        bm = block_mapping.contiguous()
+    if ts != torch.cuda.current_stream():
+        for t in (kp, vp, bm):
+            t.record_stream(ts)
     _check(library().pkv_copy_blocks(kp.data_ptr(), vp.data_ptr(), len(key_caches), bm.data_ptr(),
-                                     bm.shape[0], block_bytes, nb, _stream(stream)),
+                                     bm.shape[0], block_bytes, nb, ts.cuda_stream),
            "pkv_copy_blocks")
     return kp, vp
 

@@ -16,8 +16,8 @@
 // part of a sequence there).
 //
 // Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
-// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (three stage buffers;
-// the loads run two stages ahead), and every wave reads them from there: the stage is fetched
+// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (four stage buffers;
+// the loads run two stages ahead, and waves 4-7 run one stage behind waves 0-3), and every wave reads them from there: the stage is fetched
 // once for all 256 columns.
 //   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
 //           rows, 16 columns per product);

@@ -128,6 +128,29 @@ def test_copy_blocks_multi_layer(layers):
         assert _bits_equal(kd[l], kb) and _bits_equal(vd[l], vb)
 
 
+def test_copy_blocks_on_a_side_stream():
+    """copy_blocks launched on a stream other than torch's current one: its pointer tables and
+    mapping copy are made on that stream, so the copies land even when the current stream is
+    kept busy; bit-exact against the oracle."""
+    NB, H, D, bs = 48, 4, 128, 16
+    kc = draw_normal((NB, H, D // 8, bs, 8), "bf16", 71, 0)
+    vc = draw_normal((NB, H, D, bs), "bf16", 71, 1)
+    pairs = np.stack([np.arange(0, 16), np.arange(16, 32)], axis=1).astype(np.int64)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    mapping = torch.from_numpy(pairs).to(DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    busy = torch.empty(1 << 24, device=DEV)
+    for _ in range(20):
+        busy.mul_(1.0001)   # keeps the current stream busy while the side stream runs
+    pkv.copy_blocks([kd], [vd], mapping, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    kb, vb = storage_bits(kc).copy(), storage_bits(vc).copy()
+    OC.copy_blocks([kb, vb], pairs)
+    assert _bits_equal(kd, kb) and _bits_equal(vd, vb)
+
+
 def test_swap_out_and_in_through_pinned_host():
     NB_dev, NB_host, H, D, bs = 64, 24, 4, 128, 16
     dev_k = draw_normal((NB_dev, H, D // 8, bs, 8), "bf16", 60, 0).to(DEV)
