@@ -122,6 +122,37 @@ int pkv_paged_attention_decode(void* out, const void* query, const void* key_cac
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_size,
                                           int32_t max_context_len, int32_t partition_size);
 
+/*
+ * pkv_paged_attention_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It takes no workspace: the work list and the split-K partials
+ * live in a static device array of PKV_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every device it runs on until the process ends.  The call
+ * itself allocates and frees nothing.
+ *
+ * Arguments, result and error codes as for pkv_paged_attention_decode (the same
+ * kernels run; the output is bit-identical to it), without workspace and
+ * workspace_bytes.  Sizes whose pkv_paged_attention_workspace_size exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES are refused with PKV_ERR_WORKSPACE before anything
+ * is enqueued.  The first call on a device looks the array's device address up
+ * (hipGetSymbolAddress; a failure returns PKV_ERR_HIP).  Every call on one
+ * device shares that device's array: calls that can overlap on one device (on
+ * different streams, or from several threads) race and must be serialised by
+ * the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_num_blocks_per_seq,
+                                       int32_t max_context_len, int32_t dtype,
+                                       int32_t partition_size, void* stream);
+
+/* Bytes of the static scratch of pkv_paged_attention_decode_noalloc
+ * (PKV_NOALLOC_SCRATCH_BYTES). */
+size_t pkv_paged_attention_noalloc_scratch_bytes(void);
+
 /* The first phase of pkv_paged_attention_decode, alone: the work-list kernel
  * and then one workgroup per (work item, KV head).  Sequences handled by one
  * item get their final output in `out`; the others leave per-item partial

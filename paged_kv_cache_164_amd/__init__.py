@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     library,
     library_path,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
+    noalloc_scratch_bytes,
     paged_attention_decode_shared,
     paged_attention_partitions_planned_shared,
     paged_attention_partitions_planned_fp8,

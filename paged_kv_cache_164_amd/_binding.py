@@ -37,6 +37,8 @@ _SIGNATURES = {
     "pkv_paged_attention_reduce": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int, _c_p, _c_sz, _c_p]),
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "pkv_paged_attention_decode_noalloc": (_c_int, _DECODE_ARGTYPES[:16] + [_c_p]),
+    "pkv_paged_attention_noalloc_scratch_bytes": (_c_sz, []),
     "pkv_paged_attention_decode_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
                                           + _DECODE_ARGTYPES[6:]),
     "pkv_paged_attention_plan_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
@@ -212,6 +214,44 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                             max_context_len, partition_size, workspace, stream)
     _check(library().pkv_paged_attention_decode(*args), "pkv_paged_attention_decode")
     return out
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, scale, max_context_len, partition_size=0,
+                                   stream=None):
+    """paged_attention_decode with the library's static scratch instead of a workspace (no
+    device allocation anywhere in the call)."""
+    need = paged_attention_workspace_size(query.shape[0], query.shape[1], query.shape[2],
+                                          max_context_len, partition_size)
+    if need > noalloc_scratch_bytes():
+        raise PKVError(f"allocation-free decode: these sizes need {need} bytes of scratch, "
+                       f"more than the {noalloc_scratch_bytes()} it holds")
+    # a zero-size stand-in for the workspace keeps the checks shared without allocating
+    args, _ = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                           max_context_len, partition_size, _NO_WORKSPACE, stream)
+    _check(library().pkv_paged_attention_decode_noalloc(*args[:16], args[18]),
+           "pkv_paged_attention_decode_noalloc")
+    return out
+
+
+class _NoWorkspace:
+    """Stands in for a workspace tensor: no device memory behind it."""
+
+    def data_ptr(self):
+        return None
+
+    def numel(self):
+        return 0
+
+    def element_size(self):
+        return 1
+
+
+_NO_WORKSPACE = _NoWorkspace()
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(library().pkv_paged_attention_noalloc_scratch_bytes())
 
 
 def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tables, context_lens,

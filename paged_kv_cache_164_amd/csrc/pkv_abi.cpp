@@ -347,6 +347,45 @@ int pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   }
 }
 
+size_t pkv_paged_attention_noalloc_scratch_bytes(void) { return PKV_NOALLOC_SCRATCH_BYTES; }
+
+// The decode with the library's static scratch as its workspace (no allocation in the call).
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_num_blocks_per_seq,
+                                       int32_t max_context_len, int32_t dtype,
+                                       int32_t partition_size, void* stream) {
+  try {
+    const size_t need = workspace_bytes_for(num_seqs, num_heads, head_size, max_context_len,
+                                            partition_size);
+    if (need > PKV_NOALLOC_SCRATCH_BYTES)
+      return fail(PKV_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
+                                         " bytes of scratch; the allocation-free decode holds " +
+                                         std::to_string(PKV_NOALLOC_SCRATCH_BYTES));
+    // Every argument is checked before the scratch's address is looked up: a stand-in address
+    // (256-byte aligned, never dereferenced) takes its place for that check.
+    Resolved r;
+    void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+    int rc = resolve_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                            max_num_blocks_per_seq, max_context_len, dtype, partition_size,
+                            stand_in, PKV_NOALLOC_SCRATCH_BYTES, &r);
+    if (rc != PKV_OK || r.ws_needed == 0) return rc;
+    void* ws = nullptr;
+    rc = pkv::noalloc_scratch_address(&ws);
+    if (rc != PKV_OK) return rc;
+    return pkv_paged_attention_decode(out, query, key_cache, value_cache, block_tables,
+                                      context_lens, scale, num_seqs, num_heads, num_kv_heads,
+                                      head_size, block_size, max_num_blocks_per_seq,
+                                      max_context_len, dtype, partition_size, ws,
+                                      PKV_NOALLOC_SCRATCH_BYTES, stream);
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 #define PKV_SHARED_PARAMS                                                                     \
   void *out, const void *query, const void *key_cache, const void *value_cache,               \
       const int32_t *block_tables, const int32_t *context_lens, const int32_t *group_starts,  \

@@ -143,6 +143,9 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int block_size, int64_t num_blocks, int64_t key_stride,
                                         int64_t value_stride, int dtype, float k_scale,
                                         float v_scale, hipStream_t stream);
+// Device address of the static scratch of the allocation-free decode on the current device
+// (PKV_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned); PKV_OK or an error code.
+int noalloc_scratch_address(void** out);
 // Records msg as the calling thread's pkv_last_error() and returns code (host code).
 int record_error(int code, const char* msg);
 inline int record_error(int code, const std::string& msg) { return record_error(code, msg.c_str()); }

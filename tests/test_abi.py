@@ -25,7 +25,7 @@ def test_exports_every_header_symbol():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         declared |= set(re.findall(r"\b(pkv_\w+)\s*\(", open(h).read()))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 41
+    assert len(declared) == 43
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -52,6 +52,21 @@ def test_workspace_size():
     assert pkv.paged_attention_workspace_size(0, 8, 64, 100, 0) == 0
     assert pkv.paged_attention_workspace_size(4, 8, 64, 100, 8192) == 0   # partition too large
     assert pkv.paged_attention_workspace_size(4, 8, 64, 100, -1) == 0
+
+
+def test_noalloc_refuses_oversized_calls_on_the_host():
+    """The allocation-free decode checks its sizes against its static scratch before any HIP
+    call: 256 sequences x 32 heads at 512-token partitions of a 10236-token context need more
+    than 64 MiB."""
+    lib = _lib()
+    assert lib.pkv_paged_attention_noalloc_scratch_bytes() == 64 << 20
+    rc = lib.pkv_paged_attention_decode_noalloc(1, 1, 1, 1, 1, 1, 0.125, 256, 32, 8, 128, 16, 640,
+                                                10236, 2, 512, None)
+    assert rc == -4 and b"scratch" in lib.pkv_last_error()
+    # invalid sizes are reported as for the workspace call
+    rc = lib.pkv_paged_attention_decode_noalloc(1, 1, 1, 1, 1, 1, 0.125, 2, 8, 3, 64, 16, 4, 64,
+                                                1, 0, None)
+    assert rc == -1
 
 
 def _shared(lib, entry="pkv_paged_attention_decode_shared", **over):
