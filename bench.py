@@ -1,7 +1,8 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
 A step is the whole hot path over one batch: reshape_and_cache of each sequence's newest
-token into its slot, then paged decode attention (partition kernel + split-K reduce).
+token into its slot and the decode work-list plan (one launch: the two are independent), then
+paged decode attention (partition kernel + split-K reduce).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (every context token's K
@@ -58,7 +59,37 @@ WORKLOADS = {
 }
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 KERNEL_SOURCES = ["attention_valu.hip", "attention_gqa.hip", "work_plan.hip", "pkv_device.h",
-                  "pkv_internal.h"]
+                  "pkv_internal.h", "pkv_tile_addr.h"]
+
+
+class _Roctx:
+    """roctx ranges around the phases of a step (visible with rocprofv3 --marker-trace); no-ops
+    when no roctx library is present."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "libroctx64.so.4", "libroctx64.so"):
+            try:
+                lib = ctypes.CDLL(name)
+                lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+                lib.roctxRangePushA.restype = ctypes.c_int
+                lib.roctxRangePop.restype = ctypes.c_int
+                self.lib = lib
+                break
+            except (OSError, AttributeError):
+                continue
+
+    def push(self, name: str) -> None:
+        if self.lib is not None:
+            self.lib.roctxRangePushA(name.encode())
+
+    def pop(self) -> None:
+        if self.lib is not None:
+            self.lib.roctxRangePop()
+
+
+ROCTX = _Roctx()
 
 
 def kernel_source_hash() -> str:
@@ -228,11 +259,13 @@ def beam_setup(dev):
 
 
 def time_steps(step, steps: int, warmup: int, graph: bool):
-    """W warm-up steps; then the K steps of the dominant kernel's HIP events (an eager pass,
-    events recorded on the launch stream by step(ev)); then the K timed steps of the whole step,
-    between synchronisations: graph replays of one captured step when `graph`, else eager
-    steps.  step(ev=None, st=None) launches on `st` when given (the capture stream), else on
-    the stream it was set up with.  Returns (ms per step, per-step event times in ms)."""
+    """W warm-up steps; then K steps with the dominant kernel bracketed by HIP events (recorded
+    on the launch stream by step(ev)), for its time alone; then the K timed steps of the whole
+    step, between synchronisations and without events (an event record between two kernels
+    holds the second back by ~6 us on this GPU, which is measurement, not the path): graph
+    replays of one captured step when `graph`, else eager steps.  step(ev=None, st=None)
+    launches on `st` when given (the capture stream), else on the stream it was set up with.
+    Returns (ms per step, per-step event times in ms)."""
     import torch
 
     for _ in range(warmup):
@@ -240,12 +273,15 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
     events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / steps
     k_ms = [a.elapsed_time(b) for a, b in events]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
     if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -553,18 +589,24 @@ def run_prefill(args) -> int:
 
     def step(ev=None, st=None):
         st = stream if st is None else st
+        ROCTX.push("step")
+        ROCTX.push("reshape_and_cache")
         if kv8:
             pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale, stream=st,
                                       code=code)
         else:
             pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+        ROCTX.pop()
         if ev is not None:
             ev[0].record(st)
+        ROCTX.push("multi-query attention")
         pkv.paged_attention_prefill(out, q, kc, vc, bt, cl, qsl, case.scale, lmax, P, ws,
                                     stream=st, k_scale=case.k_scale if kv8 else None,
                                     v_scale=case.v_scale if kv8 else None, code=code or "e4m3")
         if ev is not None:
             ev[1].record(st)
+        ROCTX.pop()
+        ROCTX.pop()
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))
@@ -694,24 +736,37 @@ def main() -> int:
 
     def step(ev=None, st=None):
         st = stream if st is None else st
+        ROCTX.push("step")
         # the work list depends on tables, lengths (and groups) only: built before the write
-        if kv8:
-            pkv.paged_attention_plan_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale, case.v_scale,
-                                         lmax, P, ws, stream=st, code=code)
-        elif beam:
-            pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale, lmax,
-                                            P, ws, stream=st)
+        if kv8 or beam:
+            ROCTX.push("plan")
+            if kv8:
+                pkv.paged_attention_plan_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
+                                             case.v_scale, lmax, P, ws, stream=st, code=code)
+            else:
+                pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale,
+                                                lmax, P, ws, stream=st)
+            ROCTX.pop()
+            if beam:  # device pointer table made once, outside any graph capture
+                ROCTX.push("copy_blocks")
+                pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
+                ROCTX.pop()
+            ROCTX.push("reshape_and_cache")
+            if kv8:
+                pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
+                                          stream=st, code=code)
+            else:
+                pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+            ROCTX.pop()
         else:
-            pkv.paged_attention_plan(out, q, kc, vc, bt, cl, scale, lmax, P, ws, stream=st)
-        if beam:  # device pointer table made once, outside any graph capture
-            pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
-        if kv8:
-            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
-                                      stream=st, code=code)
-        else:
-            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+            # the plan and the new tokens' cache write are independent: one launch
+            ROCTX.push("plan and reshape_and_cache")
+            pkv.paged_attention_plan_and_cache(out, q, kc, vc, bt, cl, scale, lmax, nk, nv, slots,
+                                               P, ws, stream=st)
+            ROCTX.pop()
         if ev is not None:
             ev[0].record(st)
+        ROCTX.push("partition kernel")
         if kv8:
             pkv.paged_attention_partitions_planned_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
                                                        case.v_scale, lmax, P, ws, stream=st,
@@ -724,7 +779,11 @@ def main() -> int:
                                                    stream=st)
         if ev is not None:
             ev[1].record(st)
+        ROCTX.pop()
+        ROCTX.push("reduce")
         pkv.paged_attention_reduce(out, cl, lmax, ws, P, stream=st)
+        ROCTX.pop()
+        ROCTX.pop()
 
     ms_step, k_ms = time_steps(step, args.steps, args.warmup, args.graph)
     k_avg = float(np.mean(k_ms))

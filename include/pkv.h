@@ -200,6 +200,34 @@ int pkv_paged_attention_partitions_planned(void* out, const void* query, const v
                                            int32_t partition_size, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
+/* The first calls of a decode step in one launch: pkv_reshape_and_cache of the
+ * step's new tokens and pkv_paged_attention_plan.  The two are independent (the
+ * plan reads block_tables and context_lens only; the write reads key, value and
+ * slot_mapping and writes the caches), so one launch runs the plan in one
+ * workgroup and the write in the others, and the short write no longer waits
+ * behind the plan (the "Vllm" page, "transformer" decoding paragraph: the new
+ * token's K/V are appended, then attended to).  The caches and the workspace
+ * end exactly as after pkv_reshape_and_cache followed by
+ * pkv_paged_attention_plan; pkv_paged_attention_partitions_planned and
+ * pkv_paged_attention_reduce complete the step.
+ *   arguments up to workspace_bytes: as for pkv_paged_attention_plan (16- and
+ *     32-bit caches; out and query are not read)
+ *   key, value, slot_mapping, num_tokens, num_blocks, key_stride, value_stride:
+ *     as for pkv_reshape_and_cache, into the same key_cache and value_cache, with
+ *     the decode's dtype, num_kv_heads, head_size and block_size
+ * Errors as for those two calls; nothing is enqueued when any argument fails. */
+int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_num_blocks_per_seq,
+                                       int32_t max_context_len, int32_t dtype,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, const void* key, const void* value,
+                                       const int64_t* slot_mapping, int32_t num_tokens,
+                                       int64_t num_blocks, int64_t key_stride,
+                                       int64_t value_stride, void* stream);
+
 /* The second kernel alone: for each sequence with more than one work item,
  * out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p with M = max_p m_p,
  * over its items p in token order.  Sequences with one item are left

@@ -38,6 +38,8 @@ _SIGNATURES = {
                                             _c_int, _c_p, _c_sz, _c_p]),
     "pkv_paged_attention_workspace_size": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "pkv_paged_attention_decode_noalloc": (_c_int, _DECODE_ARGTYPES[:16] + [_c_p]),
+    "pkv_paged_attention_plan_and_cache": (_c_int, _DECODE_ARGTYPES[:18] + [_c_p, _c_p, _c_p, _c_int,
+                                                                           _c_i64, _c_i64, _c_i64, _c_p]),
     "pkv_paged_attention_noalloc_scratch_bytes": (_c_sz, []),
     "pkv_paged_attention_decode_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
                                           + _DECODE_ARGTYPES[6:]),
@@ -472,6 +474,43 @@ def paged_attention_reduce(out, context_lens, max_context_len, workspace, partit
                                                 _stream(stream)),
            "pkv_paged_attention_reduce")
     return out
+
+
+def _cache_write_checks(key, value, key_cache, value_cache, slot_mapping):
+    _on_gpu(key, value, key_cache, value_cache, slot_mapping)
+    N, Hkv, D = key.shape
+    NB, Hkv2, Dx, bs, x = key_cache.shape
+    if Hkv2 != Hkv or Dx * x != D or tuple(value.shape) != (N, Hkv, D):
+        raise PKVError("key/value [N, Hkv, D] must match the cache layout")
+    if tuple(value_cache.shape) != (NB, Hkv, D, bs):
+        raise PKVError("value_cache must be [num_blocks, Hkv, D, bs]")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise PKVError("key, value and caches must share one dtype")
+    for t in (key, value):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise PKVError("key/value need stride(-1) == 1 and stride(1) == head_size")
+    if not (key_cache.is_contiguous() and value_cache.is_contiguous()):
+        raise PKVError("caches must be contiguous")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N or not slot_mapping.is_contiguous():
+        raise PKVError("slot_mapping must be contiguous int64 with one entry per token")
+    return N, NB
+
+
+def paged_attention_plan_and_cache(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, scale, max_context_len, key, value,
+                                   slot_mapping, partition_size=0, workspace=None, stream=None):
+    """reshape_and_cache of the step's new tokens and the decode work-list plan in one launch;
+    returns the workspace holding the list (paged_attention_partitions_planned and
+    paged_attention_reduce complete the step)."""
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream)
+    N, NB = _cache_write_checks(key, value, key_cache, value_cache, slot_mapping)
+    if key.dtype != query.dtype:
+        raise PKVError("key and value must have the query's dtype")
+    _check(library().pkv_paged_attention_plan_and_cache(
+        *args[:18], key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), N, NB,
+        key.stride(0), value.stride(0), args[18]), "pkv_paged_attention_plan_and_cache")
+    return ws
 
 
 def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):

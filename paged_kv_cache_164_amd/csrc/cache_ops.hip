@@ -8,6 +8,7 @@
 //
 // copy_blocks: CacheEngine "copy" -- whole key and value blocks, every layer,
 // for each (src, dst) copy-on-write pair.
+#include "pkv_cache_write.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_kv8.h"
@@ -17,76 +18,15 @@
 namespace pkv {
 namespace {
 
-// A valid (non-negative) slot's block and offset: shift and mask for a power-of-two block size
-// (every size the attention kernels take), a 64-bit division otherwise.
-__device__ inline int64_t slot_block(int64_t slot, int block_size) {
-  if ((block_size & (block_size - 1)) == 0)
-    return slot >> __builtin_ctz(static_cast<unsigned>(block_size));
-  return slot / block_size;
-}
-__device__ inline int slot_offset(int64_t slot, int block_size) {
-  if ((block_size & (block_size - 1)) == 0) return static_cast<int>(slot & (block_size - 1));
-  return static_cast<int>(slot % block_size);
-}
-
-// One workgroup per new token.  VEC (16-byte aligned rows and key cache): a thread takes 16-byte
-// chunks of the key row and of the value row, all its loads in flight together; a key chunk is
-// one 16-byte store, a value chunk X element stores down the value rows.  Otherwise element by
-// element.
+// One workgroup per new token: cache_write_token (pkv_cache_write.h).
 template <typename E, bool VEC>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ key_cache,
     E* __restrict__ value_cache, const int64_t* __restrict__ slot_mapping, int num_kv_heads,
     int head_size, int block_size, int64_t num_blocks, int64_t key_stride, int64_t value_stride) {
-  constexpr int X = 16 / sizeof(E);
-  const int64_t i = blockIdx.x;
-  const int D = head_size;
-  const int n = num_kv_heads * D;
-  const int64_t tile = (int64_t)D * block_size;  // elements of one (block, head) tile
-  const E* krow = key + i * key_stride;
-  const E* vrow = value + i * value_stride;
-  if constexpr (VEC) {
-    const int nc = n / X, cph = D / X;
-    const uint4* k4 = reinterpret_cast<const uint4*>(krow);
-    const uint4* v4 = reinterpret_cast<const uint4*>(vrow);
-    // the first two chunks per thread (all of a row up to 512 chunks) without a branch: indices
-    // past the row are clamped to its last chunk and their values dropped
-    const int c0 = threadIdx.x, c1 = c0 + blockDim.x;
-    const int l0 = min(c0, nc - 1), l1 = min(c1, nc - 1);
-    const uint4 ka = k4[l0], va = v4[l0], kb = k4[l1], vb = v4[l1];
-    const int64_t slot = slot_mapping[i];
-    if (slot < 0 || slot >= num_blocks * block_size) return;
-    const int64_t blk = slot_block(slot, block_size);
-    const int off = slot_offset(slot, block_size);
-    E* kdst = key_cache + blk * num_kv_heads * tile;
-    E* vdst = value_cache + blk * num_kv_heads * tile;
-    auto put = [&](int c, const uint4& kq, const uint4& vq) {
-      const int h = c / cph, cc = c % cph;
-      *reinterpret_cast<uint4*>(kdst + h * tile + ((int64_t)cc * block_size + off) * X) = kq;
-      const E* ve = reinterpret_cast<const E*>(&vq);
-      E* vd = vdst + h * tile + (int64_t)(cc * X) * block_size + off;
-#pragma unroll
-      for (int e = 0; e < X; ++e) vd[(int64_t)e * block_size] = ve[e];
-    };
-    if (c0 < nc) put(c0, ka, va);
-    if (c1 < nc) put(c1, kb, vb);
-    for (int c = c0 + 2 * blockDim.x; c < nc; c += blockDim.x) put(c, k4[c], v4[c]);
-  } else {
-    const int64_t slot = slot_mapping[i];
-    if (slot < 0 || slot >= num_blocks * block_size) return;
-    const int64_t blk = slot_block(slot, block_size);
-    const int off = slot_offset(slot, block_size);
-    E* kdst = key_cache + blk * num_kv_heads * tile;
-    E* vdst = value_cache + blk * num_kv_heads * tile;
-    for (int e = threadIdx.x; e < n; e += blockDim.x) {
-      const int h = e / D, d = e % D;
-      kdst[h * tile + ((int64_t)(d / X) * block_size + off) * X + d % X] = krow[e];
-    }
-    for (int e = threadIdx.x; e < n; e += blockDim.x) {
-      const int h = e / D, d = e % D;
-      vdst[h * tile + (int64_t)d * block_size + off] = vrow[e];
-    }
-  }
+  cache_write_token<E, VEC>(blockIdx.x, key, value, key_cache, value_cache, slot_mapping,
+                            num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                            value_stride);
 }
 
 // The same scatter for many tokens (a prefill chunk), 16-bit elements: one workgroup per run

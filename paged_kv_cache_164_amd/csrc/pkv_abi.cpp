@@ -521,6 +521,46 @@ int pkv_paged_attention_partitions_planned(PKV_DECODE_PARAMS) {
   return phase1_mode(PKV_DECODE_ARGS, stream, 2);
 }
 
+int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_num_blocks_per_seq,
+                                       int32_t max_context_len, int32_t dtype,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, const void* key, const void* value,
+                                       const int64_t* slot_mapping, int32_t num_tokens,
+                                       int64_t num_blocks, int64_t key_stride,
+                                       int64_t value_stride, void* stream) {
+  try {
+    Resolved r;
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r);
+    if (rc != PKV_OK) return rc;
+    const int eb = elem_bytes(dtype);
+    if (num_tokens < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+    if (key_stride < (int64_t)num_kv_heads * head_size || value_stride < (int64_t)num_kv_heads * head_size)
+      return fail(PKV_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_size");
+    if (num_tokens > 0 && (!key || !value || !slot_mapping || !key_cache || !value_cache))
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    if ((int64_t)num_tokens + 1 >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const pkv::CacheWriteArgs w{key, value, const_cast<void*>(key_cache),
+                                const_cast<void*>(value_cache), slot_mapping, num_tokens,
+                                num_kv_heads, head_size, block_size, num_blocks, key_stride,
+                                value_stride};
+    hipError_t e;
+    if (num_seqs == 0)  // no plan: the write alone
+      e = pkv::launch_reshape_and_cache(key, value, w.key_cache, w.value_cache, slot_mapping,
+                                        num_tokens, num_kv_heads, head_size, block_size,
+                                        num_blocks, key_stride, value_stride, eb, s);
+    else
+      e = pkv::launch_plan_and_cache(r.args, block_size, r.use_mfma ? 16 / r.group : 1, w, eb, s);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "plan and cache write launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t head_size, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size, const void* workspace,

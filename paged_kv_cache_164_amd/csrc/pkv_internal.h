@@ -121,6 +121,24 @@ constexpr size_t kMaxDynamicLds = 65536;
 // The plan kernel lists the work items; the attention kernels run one workgroup per (item,
 // KV head); the reduce kernel merges each sequence's partial results.
 hipError_t launch_plan(const DecodeArgs& a, int block_size, int seqs_per_item, hipStream_t stream);
+// A decode step's new tokens, written by reshape_and_cache's per-token scatter.
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  int num_kv_heads;
+  int head_size;
+  int block_size;
+  int64_t num_blocks;
+  int64_t key_stride;  // elements between token rows
+  int64_t value_stride;
+};
+// The plan kernel and the cache write of w in one launch (16- and 32-bit caches).
+hipError_t launch_plan_and_cache(const DecodeArgs& a, int block_size, int seqs_per_item,
+                                 const CacheWriteArgs& w, int elem_bytes, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
                               int group, hipStream_t stream);
 bool valu_supported(int dtype, int head_size, int block_size, int group);

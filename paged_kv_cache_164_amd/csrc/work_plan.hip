@@ -26,6 +26,7 @@
 //
 // Layout in the caller's workspace (see workspace_layout): header[1] = number of items;
 // items[i] = (b0, nseq | slot << 8, begin, end).
+#include "pkv_cache_write.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_tile_addr.h"
@@ -144,8 +145,8 @@ struct ClassCounters {
   }
 };
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs, int per_item,
-                                                            int64_t capacity) {
+__device__ __forceinline__ void plan_body(const DecodeArgs& a, int bs, int per_item,
+                                          int64_t capacity) {
   __shared__ int s_wave[kWavesPerPlan][kClasses];
   __shared__ int s_base[kClasses + 1];
   const int P = a.partition_size, Q = a.tail_chunk;
@@ -244,15 +245,64 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a, int bs, int per_item,
+                                                            int64_t capacity) {
+  plan_body(a, bs, per_item, capacity);
+}
+
+// The plan and a decode step's cache write in one launch: workgroup 0 lists the work items,
+// workgroup 1 + i writes new token i (cache_write_token).  The two are independent -- the plan
+// reads block tables and lengths, the write reads new keys and values and slots -- so the short
+// write no longer waits behind the plan, and one launch gap is saved.
+template <typename E, bool VEC>
+__global__ __launch_bounds__(kPlanThreads) void plan_and_cache_kernel(DecodeArgs a, int bs,
+                                                                      int per_item,
+                                                                      int64_t capacity,
+                                                                      CacheWriteArgs w) {
+  if (blockIdx.x == 0) {
+    plan_body(a, bs, per_item, capacity);
+  } else {
+    cache_write_token<E, VEC>(blockIdx.x - 1, static_cast<const E*>(w.key),
+                              static_cast<const E*>(w.value), static_cast<E*>(w.key_cache),
+                              static_cast<E*>(w.value_cache), w.slot_mapping, w.num_kv_heads,
+                              w.head_size, w.block_size, w.num_blocks, w.key_stride,
+                              w.value_stride);
+  }
+}
+
+int plan_threads(const DecodeArgs& a) {
+  // one thread per group up to 1024 threads, in whole waves
+  const int groups = a.group_starts ? a.num_groups : a.num_seqs;
+  return (int)std::min<int64_t>(kPlanThreads, std::max<int64_t>(64, (groups + 63) / 64 * 64));
+}
+
 }  // namespace
 
 hipError_t launch_plan(const DecodeArgs& a, int block_size, int seqs_per_item, hipStream_t stream) {
   const int64_t capacity = (int64_t)a.num_seqs * a.slots;
-  // one thread per group up to 1024 threads, in whole waves
-  const int groups = a.group_starts ? a.num_groups : a.num_seqs;
-  const int threads = (int)std::min<int64_t>(kPlanThreads, std::max<int64_t>(64, (groups + 63) / 64 * 64));
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(threads), 0, stream, a, block_size,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(plan_threads(a)), 0, stream, a, block_size,
                      seqs_per_item, capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_and_cache(const DecodeArgs& a, int block_size, int seqs_per_item,
+                                 const CacheWriteArgs& w, int elem_bytes, hipStream_t stream) {
+  const int64_t capacity = (int64_t)a.num_seqs * a.slots;
+  const bool vec = (reinterpret_cast<uintptr_t>(w.key) % 16 == 0) &&
+                   ((w.key_stride * elem_bytes) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(w.key_cache) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(w.value) % 16 == 0) &&
+                   ((w.value_stride * elem_bytes) % 16 == 0);
+  const dim3 grid((unsigned)(1 + w.num_tokens)), block(plan_threads(a));
+#define PKV_PC(E, V)                                                                           \
+  hipLaunchKernelGGL((plan_and_cache_kernel<E, V>), grid, block, 0, stream, a, block_size,     \
+                     seqs_per_item, capacity, w)
+  if (elem_bytes == 2) {
+    if (vec) PKV_PC(uint16_t, true); else PKV_PC(uint16_t, false);
+  } else {
+    if (vec) PKV_PC(uint32_t, true); else PKV_PC(uint32_t, false);
+  }
+#undef PKV_PC
   return hipGetLastError();
 }
 

@@ -275,3 +275,30 @@ def test_device_plan_matches_host_planner(key, over, P, groups):
     items, counts = TC.plan(lens, bs, P_eff, min(Lmax, lay.tables.shape[1] * bs), gs, pl, per_item)
     assert sorted(map(tuple, dev_items.tolist())) == sorted(map(tuple, items.tolist()))
     assert dev_counts.tolist() == counts.tolist()
+
+
+@pytest.mark.parametrize("key,over,P", [
+    ("c3", dict(num_seqs=64, len_cap=6000), 0), ("c1", {}, 0), ("c2", dict(num_seqs=12), 512),
+    ("c3", dict(lens=[0, 1, 15, 16, 17, 2047, 2048, 2049, 4095], block_size=8), 0),
+])
+def test_plan_and_cache_equals_write_then_plan(key, over, P):
+    """The fused launch (cache write + work-list plan) then the planned kernel and the reduce:
+    caches and output bit-identical to reshape_and_cache followed by the one-call decode."""
+    case = make_decode_case(key, **over)
+    ref = GpuDecode(case, P)
+    base = ref.step().clone()
+    g = GpuDecode(case, P)
+    out = torch.full_like(g.out, float("nan"))
+    ws = pkv.paged_attention_plan_and_cache(out, g.q, g.kc, g.vc, g.bt, g.cl, case.scale,
+                                            case.max_context_len, g.nk, g.nv, g.slots, P, g.ws)
+    pkv.paged_attention_partitions_planned(out, g.q, g.kc, g.vc, g.bt, g.cl, case.scale,
+                                           case.max_context_len, P, ws)
+    pkv.paged_attention_reduce(out, g.cl, case.max_context_len, ws, P)
+    torch.cuda.synchronize()
+    iv = torch.int16 if out.element_size() == 2 else torch.int32
+    assert torch.equal(ref.kc.view(iv), g.kc.view(iv)) and torch.equal(ref.vc.view(iv), g.vc.view(iv))
+    assert torch.equal(base.view(iv), out.view(iv))
+    kb, vb = oracle_after_write(case)
+    ok, err, _ = within_tolerance(out.cpu().to(torch.float64).numpy(), oracle_decode(case, kb, vb),
+                                  case.cfg.dtype)
+    assert ok, err
