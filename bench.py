@@ -60,6 +60,8 @@ WORKLOADS = {
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 KERNEL_SOURCES = ["attention_valu.hip", "attention_gqa.hip", "work_plan.hip", "pkv_device.h",
                   "pkv_internal.h", "pkv_tile_addr.h"]
+KERNEL_SOURCES_KV8 = ["attention_fp8.hip", "pkv_kv8.h", "work_plan.hip", "pkv_device.h",
+                      "pkv_internal.h", "pkv_tile_addr.h"]
 
 
 class _Roctx:
@@ -92,28 +94,32 @@ class _Roctx:
 ROCTX = _Roctx()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kv: str = "native") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if kv == "native" else KERNEL_SOURCES_KV8):
         p = os.path.join(ROOT, "paged_kv_cache_164_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
+def traffic_name(workload: str, kv: str = "native") -> str:
+    return f"partition_kernel_{workload}{'' if kv == 'native' else '_' + kv}_traffic.json"
+
+
+def traffic_from_profile(workload: str, kv: str = "native"):
     """HBM bytes per launch of the partition kernel from committed rocprofv3 counter runs, or
     None when absent or taken on different kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"partition_kernel_{workload}_traffic.json")
+    p = os.path.join(ROOT, "profiles", traffic_name(workload, kv))
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kv):
         return None
     return d.get("hbm_bytes_per_launch")
 
 
-PARTITION_KERNELS = ("gqa_grid_kernel", "decode_valu_kernel")
+PARTITION_KERNELS = ("gqa_grid_kernel", "decode_valu_kernel", "fp8_grid_kernel")
 
 
 def _counter_means(path: str):
@@ -126,7 +132,7 @@ def _counter_means(path: str):
 
 
 def derive_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv: str,
-                   cal_write_csv: str, cal_mib: int) -> dict:
+                   cal_write_csv: str, cal_mib: int, kv: str = "native") -> dict:
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the partition kernel by what the same
     counters read for one copy_blocks launch that moves cal_mib one-MiB blocks in each of its two
     caches (2 * cal_mib MiB read, 2 * cal_mib MiB written)."""
@@ -142,11 +148,12 @@ def derive_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv:
     w_cal = pick(_counter_means(cal_write_csv), ("copy_blocks_kernel",)) * 1024
     f_k = pick(_counter_means(fetch_csv), PARTITION_KERNELS) * 1024
     w_k = pick(_counter_means(write_csv), PARTITION_KERNELS) * 1024
-    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    rec = {"workload": workload if kv == "native" else f"{workload}-{kv}",
+           "kernel_source_hash": kernel_source_hash(kv),
            "fetch_scale": known / f_cal, "write_scale": known / w_cal,
            "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
            "hbm_bytes_per_launch": round(f_k * known / f_cal + w_k * known / w_cal)}
-    out = os.path.join(ROOT, "profiles", f"partition_kernel_{workload}_traffic.json")
+    out = os.path.join(ROOT, "profiles", traffic_name(workload, kv))
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
@@ -674,7 +681,7 @@ def main() -> int:
                     help="print reference rates (streaming read, block copy, host-link swap) instead")
     args = ap.parse_args()
     if args.derive_traffic:
-        derive_traffic(args.workload, *args.derive_traffic, args.calibration_mib)
+        derive_traffic(args.workload, *args.derive_traffic, args.calibration_mib, args.kv)
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path has no multi-GPU mode "
@@ -803,8 +810,7 @@ def main() -> int:
     step_bytes = dec_bytes + write_bytes
     gbs = step_bytes / (ms_step / 1e3) / 1e9
     kernel_gbs = dec_bytes / (k_avg / 1e3) / 1e9
-    # the stored counters were taken on the 16-bit cache's partition kernel
-    traffic = None if kv8 else traffic_from_profile(args.workload)
+    traffic = None if beam else traffic_from_profile(args.workload, args.kv)
     rec = {
         "metric": "paged decode attention achieved HBM GB/s (% of peak) and KV-tokens/s, 1 GPU",
         "value": round(gbs, 2),

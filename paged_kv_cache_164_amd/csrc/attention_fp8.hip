@@ -43,15 +43,6 @@ __device__ __forceinline__ f32x4 mma(F16, const uint4& a, const uint4& b, f32x4 
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t to_bits(BF16, float v) { return f32_to_bf16_rne(v); }
-__device__ __forceinline__ float from_bits(BF16, uint32_t h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ uint32_t to_bits(F16, float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-__device__ __forceinline__ float from_bits(F16, uint32_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
-}
-
 // Byte mask keeping the bytes of tokens base + e < limit (e = 0..3) of one dword.
 __device__ __forceinline__ uint32_t keep4(int base, int limit) {
   return ((base + 0 < limit) ? 0x000000ffu : 0u) | ((base + 1 < limit) ? 0x0000ff00u : 0u) |
@@ -162,8 +153,10 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
   f32x4 oacc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // reference maximum of column col (base-2 units), lazily moved
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // column col's sum of weights (all four rows)
+  const uint32_t one2 = one_bits(DT());
+  const uint4 ones = make_uint4(one2, one2, one2, one2);
 
   auto compute_tile = [&](int t0, Tile& tl) {
     f32x4 s[2];
@@ -187,26 +180,27 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // the first tile holds a token; a tile past the end leaves m, l and acc unchanged
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    // lazy maximum (as in attention_gqa.hip): the first tile holds a token; a tile past the end
+    // leaves m, the sums and acc unchanged
+    const bool need = tmax > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      lacc *= alpha;
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
-    uint32_t hw[8];
+      for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+    }
+    float p[8];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hw[4 * r + e] = to_bits(DT(), exp2f(s[r][e] - m_new));
-        l_run += from_bits(DT(), hw[4 * r + e]);
-      }
+      for (int e = 0; e < 4; ++e) p[4 * r + e] = __builtin_amdgcn_exp2f(s[r][e] - m_run);
     // weights of tokens 4 quad .. + 4 (w0) and 16 + 4 quad .. + 4 (w1), two per dword; after
     // the swaps lane (col, quad) holds tokens 8 quad .. + 8: rows (16 lanes) 2-3 of w0 trade
     // with rows 0-1 of w1, then odd rows of the first with even rows of the second
-    const uint32_t w0x = hw[0] | (hw[1] << 16), w0y = hw[2] | (hw[3] << 16);
-    const uint32_t w1x = hw[4] | (hw[5] << 16), w1y = hw[6] | (hw[7] << 16);
+    const uint32_t w0x = pack2(DT(), p[0], p[1]), w0y = pack2(DT(), p[2], p[3]);
+    const uint32_t w1x = pack2(DT(), p[4], p[5]), w1y = pack2(DT(), p[6], p[7]);
     const auto sx = __builtin_amdgcn_permlane32_swap(w0x, w1x, false, false);
     const auto sy = __builtin_amdgcn_permlane32_swap(w0y, w1y, false, false);
     const auto tx = __builtin_amdgcn_permlane16_swap(sx[0], sx[1], false, false);
@@ -220,6 +214,7 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
     }
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = mma(DT(), widen8<DT, CODE>(tl.v[i].x, tl.v[i].y), pop, oacc[i]);
+    lacc = mma(DT(), ones, pop, lacc);
   };
 
   // Computes of tiles past the end are not skipped (see attention_gqa.hip).
@@ -234,9 +229,9 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
     compute_tile((i + 3) * TT, T3);
   }
 
-  // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r], the value scale applied here
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r] and its column's sum of weights; the
+  // value scale is applied here
+  const float l_tot = lacc[0];
   if (col < ncols) {
     if (np_col <= 1) {
       const float f = a.v_scale / l_tot;

@@ -13,7 +13,8 @@
 //   key tile [D/8][bs][8]: lane (token l%16, dims 8*(l/16)..) = one 16-byte load;
 //   value tile [D][bs]: lane (dim l%16, tokens 4*(l/16)..+4) = one 8-byte load, and the 64
 //   lanes of one load cover 16 whole value rows (512 contiguous bytes at bs 16).
-// Weights are rounded to the element type once; l accumulates the rounded weights.
+// Weights are rounded to the element type once; their sum comes from the matrix cores (a ones
+// row times the same rounded weights).  The running maximum is lazy (kLazyRescale).
 // Tokens past the context: logit -inf, weight 0, value entries zeroed before the product.
 //
 // Scheduling: workgroup t takes ticket t of the list that the plan kernel (work_plan.hip)
@@ -59,15 +60,6 @@ __device__ __forceinline__ f32x4 mma_k16(BF16, const uint2& a, const uint2& b, f
 __device__ __forceinline__ f32x4 mma_k16(F16, const uint2& a, const uint2& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t to_bits(BF16, float v) { return f32_to_bf16_rne(v); }
-__device__ __forceinline__ float from_bits(BF16, uint32_t h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ uint32_t to_bits(F16, float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
-}
-__device__ __forceinline__ float from_bits(F16, uint32_t h) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
 // Zero the 16-bit elements of an 8-byte value chunk whose token base + e is >= limit.
@@ -179,8 +171,9 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
   f32x4 oacc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of column col (base-2 units)
-  float l_run = 0.f;        // this lane's share of the running sum (its tokens only)
+  float m_run = -INFINITY;  // reference maximum of column col (base-2 units), lazily moved
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};  // column col's sum of weights (all four rows)
+  const uint2 ones = make_uint2(one_bits(DT()), one_bits(DT()));
 
   auto compute_tile = [&](int t0, Tile& tl) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -194,22 +187,25 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // The first tile holds a token, so m_run is finite from then on; a tile past the end has
-    // only -inf logits: m stays, alpha is exactly 1 and every weight is 0.
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    // Lazy maximum: a column moves its reference (and rescales) only when the tile's maximum
+    // exceeds it by more than kLazyRescale; the wave branches if any column needs it, and the
+    // other columns' alpha is exactly 1.  The first tile holds a token, so every column moves
+    // (alpha 0 from m = -inf); a tile past the end has only -inf logits and changes nothing.
+    const bool need = tmax > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      lacc *= alpha;
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
-    // weights rounded once to the element type; the same values feed l and P.V
-    uint32_t h[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      h[r] = to_bits(DT(), exp2f(s[r] - m_new));
-      l_run += from_bits(DT(), h[r]);
+      for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
     }
-    const uint2 pop = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    // weights (at most 2^8; v_exp_f32 flushes those below 2^-126 to 0) rounded once to the
+    // element type; the same values feed the sum (a ones row on the matrix cores) and P.V
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
+    const uint2 pop = make_uint2(pack2(DT(), p[0], p[1]), pack2(DT(), p[2], p[3]));
     const int tv = t0 + quad * 4;
     if (tv + 4 > ntok) {
 #pragma unroll
@@ -217,6 +213,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     }
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = mma_k16(DT(), tl.v[i], pop, oacc[i]);
+    lacc = mma_k16(DT(), ones, pop, lacc);
   };
 
   // Computes of tiles past the end (at most three) are not skipped: a branch around them would
@@ -232,9 +229,8 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     compute_tile((i + 3) * 16, T3);
   }
 
-  // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r]
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  // ---- epilogue: lane holds O[col][d = 16 i + 4 quad + r] and its column's sum of weights
+  const float l_tot = lacc[0];
   if (col < ncols) {
     if (np_col <= 1) {  // the column's sequence has no other item: final output
       const float inv = 1.f / l_tot;
@@ -259,7 +255,7 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
 // One workgroup per ticket of the plan's list (the grid is an upper bound: workgroups past the
 // list's end exit at once, after every real item has been dispatched).
 template <class DT, int D, int BS>
-__global__ __launch_bounds__(64) void gqa_grid_kernel(DecodeArgs a, int G) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void gqa_grid_kernel(DecodeArgs a, int G) {
   const int Hkv = a.num_kv_heads;
   const int t = blockIdx.x;
   if (t >= int(a.queue[1]) * Hkv) return;

@@ -46,7 +46,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kLazyRescale = 8.f;  // log2 units: weights stay below 2^8 between rescales
 
 __device__ __forceinline__ f32x4 mma(BF16, const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -56,15 +55,7 @@ __device__ __forceinline__ f32x4 mma(F16, const uint4& a, const uint4& b, f32x4 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
-// Two floats to two packed elements, round to nearest even (one v_cvt_pk_* on gfx950).
-__device__ __forceinline__ uint32_t pack2(BF16, float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), bf16x2));
-}
-__device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), f16x2));
-}
-__device__ __forceinline__ uint32_t one_bits(BF16) { return 0x3f803f80u; }
-__device__ __forceinline__ uint32_t one_bits(F16) { return 0x3c003c00u; }
+// pack2 / one_bits (pkv_device.h): two floats to two packed elements (RNE), and packed ones.
 
 // Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA column): gfx950's lane-swap
 // instructions (VALU), not an LDS permute.

@@ -54,6 +54,25 @@ __device__ __forceinline__ void unpack(BF16, const uint4& v, float* f) {
   unpack2_bf16(v.w, f + 6);
 }
 
+// Two floats to two packed 16-bit elements, round to nearest even (one v_cvt_pk_* on gfx950).
+typedef float pkv_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pkv_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pkv_f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(BF16, float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((pkv_f32x2{x, y}), pkv_bf16x2));
+}
+__device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((pkv_f32x2{x, y}), pkv_f16x2));
+}
+// Two packed ones of the element type (an all-ones MFMA operand turns a product into row sums).
+__device__ __forceinline__ uint32_t one_bits(BF16) { return 0x3f803f80u; }
+__device__ __forceinline__ uint32_t one_bits(F16) { return 0x3c003c00u; }
+
+// Online softmax with a lazy maximum (log2 units): a column's running maximum moves, and its
+// accumulators are rescaled, only when a tile's maximum exceeds it by more than this margin, so
+// weights stay below 2^8 and most tiles skip the rescale.
+constexpr float kLazyRescale = 8.f;
+
 // Round-to-nearest-even narrowing stores.
 __device__ __forceinline__ void store_elem(F32, void* base, int64_t i, float v) {
   static_cast<float*>(base)[i] = v;
