@@ -169,15 +169,22 @@ __device__ __forceinline__ void fp8_item(const DecodeArgs& a, int G, int kh, int
         s[r] = mma(DT(), widen8<DT, CODE>(tl.k[r][j].z, tl.k[r][j].w), qop[j][1], s[r]);
       }
     }
-    // lane: logits of tokens t0 + 16 r + 4 quad + e (e < 4) of its column
+    // lane: logits of tokens t0 + 16 r + 4 quad + e (e < 4) of its column; tokens past the
+    // item (only in a tile that reaches past its end) get -inf
+#pragma unroll
+    for (int r = 0; r < 2; ++r) s[r] *= a.scale_log2;
+    if (t0 + TT > ntok) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (t0 + (r ? stok1 : stok0) + e >= ntok) s[r][e] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[r][e] = (t0 + (r ? stok1 : stok0) + e < ntok) ? s[r][e] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, s[r][e]);
-      }
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s[r][e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     // lazy maximum (as in attention_gqa.hip): the first tile holds a token; a tile past the end

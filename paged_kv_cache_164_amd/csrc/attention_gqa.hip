@@ -179,12 +179,13 @@ __device__ __forceinline__ void gqa_item(const DecodeArgs& a, int G, int kh, int
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) s = mma_k32(DT(), tl.k[kc], qop[kc], s);
-    float tmax = -INFINITY;
+    s *= a.scale_log2;
+    if (t0 + 16 > ntok) {  // tokens past the item (only in its last tile): -inf
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r] = (t0 + quad * 4 + r < ntok) ? s[r] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, s[r]);
+      for (int r = 0; r < 4; ++r)
+        if (t0 + quad * 4 + r >= ntok) s[r] = -INFINITY;
     }
+    float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     // Lazy maximum: a column moves its reference (and rescales) only when the tile's maximum
