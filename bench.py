@@ -745,25 +745,23 @@ def main() -> int:
         st = stream if st is None else st
         ROCTX.push("step")
         # the work list depends on tables, lengths (and groups) only: built before the write
-        if kv8 or beam:
+        if beam:
             ROCTX.push("plan")
-            if kv8:
-                pkv.paged_attention_plan_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
-                                             case.v_scale, lmax, P, ws, stream=st, code=code)
-            else:
-                pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale,
-                                                lmax, P, ws, stream=st)
+            pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale,
+                                            lmax, P, ws, stream=st)
             ROCTX.pop()
-            if beam:  # device pointer table made once, outside any graph capture
-                ROCTX.push("copy_blocks")
-                pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
-                ROCTX.pop()
+            # device pointer table made once, outside any graph capture
+            ROCTX.push("copy_blocks")
+            pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
+            ROCTX.pop()
             ROCTX.push("reshape_and_cache")
-            if kv8:
-                pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, case.k_scale, case.v_scale,
-                                          stream=st, code=code)
-            else:
-                pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+            ROCTX.pop()
+        elif kv8:
+            ROCTX.push("plan and reshape_and_cache")
+            pkv.paged_attention_plan_and_cache_fp8(out, q, kc, vc, bt, cl, scale, case.k_scale,
+                                                   case.v_scale, lmax, nk, nv, slots, P, ws,
+                                                   stream=st, code=code)
             ROCTX.pop()
         else:
             # the plan and the new tokens' cache write are independent: one launch

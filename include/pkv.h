@@ -402,6 +402,35 @@ int pkv_paged_attention_partitions_planned_int8(
     int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_plan_and_cache over an 8-bit cache: the write of the
+ * step's new tokens (pkv_reshape_and_cache_fp8 / _int8, with the cache's k_scale
+ * and v_scale) and pkv_paged_attention_plan_fp8 / _int8 in one launch.  The
+ * caches and the workspace end exactly as after those two calls in that order;
+ * pkv_paged_attention_partitions_planned_fp8 / _int8 and
+ * pkv_paged_attention_reduce complete the step.
+ *   arguments up to workspace_bytes: as for pkv_paged_attention_plan_fp8
+ *   key, value, slot_mapping, num_tokens, num_blocks, key_stride, value_stride:
+ *     as for pkv_reshape_and_cache_fp8, into the same key_cache and value_cache,
+ *     fp16 / bf16 keys and values of the decode's dtype, num_kv_heads, head_size
+ *     and block_size
+ * Errors as for those two calls; nothing is enqueued when any argument fails. */
+int pkv_paged_attention_plan_and_cache_fp8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, const void* key,
+    const void* value, const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+    int64_t key_stride, int64_t value_stride, void* stream);
+int pkv_paged_attention_plan_and_cache_int8(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+    float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, const void* key,
+    const void* value, const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+    int64_t key_stride, int64_t value_stride, void* stream);
+
 /*
  * Multi-query paged attention: chunked prefill and mixed prefill / decode
  * batches.  The query rows of num_seqs requests are flattened; request b owns

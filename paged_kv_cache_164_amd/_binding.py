@@ -60,6 +60,14 @@ _SIGNATURES = {
                                         + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_partitions_planned_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                         + _DECODE_ARGTYPES[7:]),
+    "pkv_paged_attention_plan_and_cache_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                               + _DECODE_ARGTYPES[7:18]
+                                               + [_c_p, _c_p, _c_p, _c_int, _c_i64, _c_i64,
+                                                  _c_i64, _c_p]),
+    "pkv_paged_attention_plan_and_cache_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
+                                                + _DECODE_ARGTYPES[7:18]
+                                                + [_c_p, _c_p, _c_p, _c_int, _c_i64, _c_i64,
+                                                   _c_i64, _c_p]),
     "pkv_paged_attention_prefill_workspace_size": (_c_sz, [_c_int] * 7),
     "pkv_paged_attention_prefill": (_c_int, [_c_p] * 7 + [_c_f] + [_c_int] * 10
                                     + [_c_p, _c_sz, _c_p]),
@@ -510,6 +518,35 @@ def paged_attention_plan_and_cache(out, query, key_cache, value_cache, block_tab
     _check(library().pkv_paged_attention_plan_and_cache(
         *args[:18], key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), N, NB,
         key.stride(0), value.stride(0), args[18]), "pkv_paged_attention_plan_and_cache")
+    return ws
+
+
+def paged_attention_plan_and_cache_fp8(out, query, key_cache, value_cache, block_tables,
+                                       context_lens, scale, k_scale, v_scale, max_context_len,
+                                       key, value, slot_mapping, partition_size=0,
+                                       workspace=None, stream=None, code="e4m3"):
+    """paged_attention_plan_and_cache over an 8-bit cache: reshape_and_cache_fp8 of the step's
+    new fp16 / bf16 tokens and the work-list plan in one launch; returns the workspace holding
+    the list (paged_attention_partitions_planned_fp8 and paged_attention_reduce complete the
+    step)."""
+    name = "pkv_paged_attention_plan_and_cache_" + _kv8_entry(code)
+    args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                            max_context_len, partition_size, workspace, stream, kv8=True)
+    N, Hkv, D = key.shape
+    NB = key_cache.shape[0]
+    _on_gpu(key, value, slot_mapping)
+    if tuple(value.shape) != (N, Hkv, D) or key.dtype != query.dtype or value.dtype != query.dtype:
+        raise PKVError("key and value must be [N, Hkv, D] of the query's dtype")
+    if Hkv != key_cache.shape[1] or D != key_cache.shape[2] * key_cache.shape[4]:
+        raise PKVError("key/value [N, Hkv, D] must match the cache layout")
+    for t in (key, value):
+        if t.stride(2) != 1 or t.stride(1) != D:
+            raise PKVError("key/value need stride(-1) == 1 and stride(1) == head_size")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N or not slot_mapping.is_contiguous():
+        raise PKVError("slot_mapping must be contiguous int64 with one entry per token")
+    _check(getattr(library(), name)(
+        *args[:7], float(k_scale), float(v_scale), *args[7:18], key.data_ptr(), value.data_ptr(),
+        slot_mapping.data_ptr(), N, NB, key.stride(0), value.stride(0), args[18]), name)
     return ws
 
 

@@ -561,6 +561,75 @@ int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void*
   }
 }
 
+// The plan and the write of the new tokens into an 8-bit cache, in one launch.
+static int plan_and_cache_kv8(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, const Kv8& kv8,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_size, int32_t block_size,
+                              int32_t max_num_blocks_per_seq, int32_t max_context_len,
+                              int32_t dtype, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, const void* key, const void* value,
+                              const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                              int64_t key_stride, int64_t value_stride, void* stream) {
+  try {
+    Resolved r;
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r, nullptr, &kv8);
+    if (rc != PKV_OK) return rc;
+    if (num_tokens < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+    if (key_stride < (int64_t)num_kv_heads * head_size || value_stride < (int64_t)num_kv_heads * head_size)
+      return fail(PKV_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_size");
+    if (num_tokens > 0 && (!key || !value || !slot_mapping || !key_cache || !value_cache))
+      return fail(PKV_ERR_NULL_POINTER, "null tensor pointer");
+    if (num_tokens > 0 && reinterpret_cast<uintptr_t>(key_cache) % 16 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "key_cache must be 16-byte aligned");
+    if ((int64_t)num_tokens + 1 >= (int64_t(1) << 31)) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* kc = const_cast<void*>(key_cache);
+    void* vc = const_cast<void*>(value_cache);
+    hipError_t e;
+    if (num_seqs == 0) {  // no plan: the write alone
+      if (num_tokens == 0) return PKV_OK;
+      auto* launch = kv8.code == pkv::kCodeE4M3 ? pkv::launch_reshape_and_cache_fp8
+                                                : pkv::launch_reshape_and_cache_i8;
+      e = launch(key, value, kc, vc, slot_mapping, num_tokens, num_kv_heads, head_size, block_size,
+                 num_blocks, key_stride, value_stride, dtype, kv8.k_scale, kv8.v_scale, s);
+    } else {
+      const pkv::CacheWriteArgs w{key, value, kc, vc, slot_mapping, num_tokens, num_kv_heads,
+                                  head_size, block_size, num_blocks, key_stride, value_stride};
+      e = pkv::launch_plan_and_cache_kv8(r.args, block_size, 16 / r.group, w, dtype, kv8.code,
+                                         kv8.k_scale, kv8.v_scale, s);
+    }
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "plan and 8-bit cache write launch");
+  } catch (...) {
+    return fail(PKV_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+#define PKV_PLAN_AND_CACHE_KV8_PARAMS                                                            \
+  void *out, const void *query, const void *key_cache, const void *value_cache,                 \
+      const int32_t *block_tables, const int32_t *context_lens, float scale, float k_scale,     \
+      float v_scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,                 \
+      int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,                    \
+      int32_t max_context_len, int32_t dtype, int32_t partition_size, void *workspace,          \
+      size_t workspace_bytes, const void *key, const void *value, const int64_t *slot_mapping,  \
+      int32_t num_tokens, int64_t num_blocks, int64_t key_stride, int64_t value_stride,         \
+      void *stream
+#define PKV_PLAN_AND_CACHE_KV8_CALL(CODE)                                                        \
+  plan_and_cache_kv8(out, query, key_cache, value_cache, block_tables, context_lens, scale,      \
+                     Kv8{k_scale, v_scale, CODE}, num_seqs, num_heads, num_kv_heads, head_size, \
+                     block_size, max_num_blocks_per_seq, max_context_len, dtype, partition_size, \
+                     workspace, workspace_bytes, key, value, slot_mapping, num_tokens,           \
+                     num_blocks, key_stride, value_stride, stream)
+
+int pkv_paged_attention_plan_and_cache_fp8(PKV_PLAN_AND_CACHE_KV8_PARAMS) {
+  return PKV_PLAN_AND_CACHE_KV8_CALL(pkv::kCodeE4M3);
+}
+
+int pkv_paged_attention_plan_and_cache_int8(PKV_PLAN_AND_CACHE_KV8_PARAMS) {
+  return PKV_PLAN_AND_CACHE_KV8_CALL(pkv::kCodeI8);
+}
+
 int pkv_paged_attention_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                                int32_t num_heads, int32_t head_size, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size, const void* workspace,

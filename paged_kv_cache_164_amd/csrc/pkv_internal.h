@@ -139,6 +139,11 @@ struct CacheWriteArgs {
 // The plan kernel and the cache write of w in one launch (16- and 32-bit caches).
 hipError_t launch_plan_and_cache(const DecodeArgs& a, int block_size, int seqs_per_item,
                                  const CacheWriteArgs& w, int elem_bytes, hipStream_t stream);
+// The same with the write into an 8-bit cache (code kCodeE4M3 / kCodeI8; dtype 1 / 2 = fp16 /
+// bf16 new keys and values).
+hipError_t launch_plan_and_cache_kv8(const DecodeArgs& a, int block_size, int seqs_per_item,
+                                     const CacheWriteArgs& w, int dtype, int code, float k_scale,
+                                     float v_scale, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_size, int block_size,
                               int group, hipStream_t stream);
 bool valu_supported(int dtype, int head_size, int block_size, int group);

@@ -270,6 +270,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_and_cache_kernel(DecodeArgs
   }
 }
 
+// The same with the write into an 8-bit cache (cache_write_token_kv8): the new fp16 / bf16 keys
+// and values quantised with the cache's scales.
+template <class IN, int CODE>
+__global__ __launch_bounds__(kPlanThreads) void plan_and_cache_kv8_kernel(
+    DecodeArgs a, int bs, int per_item, int64_t capacity, CacheWriteArgs w, float k_scale,
+    float v_scale) {
+  if (blockIdx.x == 0) {
+    plan_body(a, bs, per_item, capacity);
+  } else {
+    cache_write_token_kv8<IN, CODE>(blockIdx.x - 1, static_cast<const uint16_t*>(w.key),
+                                    static_cast<const uint16_t*>(w.value),
+                                    static_cast<uint8_t*>(w.key_cache),
+                                    static_cast<uint8_t*>(w.value_cache), w.slot_mapping,
+                                    w.num_kv_heads, w.head_size, w.block_size, w.num_blocks,
+                                    w.key_stride, w.value_stride, k_scale, v_scale);
+  }
+}
+
 int plan_threads(const DecodeArgs& a) {
   // one thread per group up to 1024 threads, in whole waves
   const int groups = a.group_starts ? a.num_groups : a.num_seqs;
@@ -303,6 +321,23 @@ hipError_t launch_plan_and_cache(const DecodeArgs& a, int block_size, int seqs_p
     if (vec) PKV_PC(uint32_t, true); else PKV_PC(uint32_t, false);
   }
 #undef PKV_PC
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_and_cache_kv8(const DecodeArgs& a, int block_size, int seqs_per_item,
+                                     const CacheWriteArgs& w, int dtype, int code, float k_scale,
+                                     float v_scale, hipStream_t stream) {
+  const int64_t capacity = (int64_t)a.num_seqs * a.slots;
+  const dim3 grid((unsigned)(1 + w.num_tokens)), block(plan_threads(a));
+#define PKV_PC8(IN, CODE)                                                                      \
+  hipLaunchKernelGGL((plan_and_cache_kv8_kernel<IN, CODE>), grid, block, 0, stream, a,         \
+                     block_size, seqs_per_item, capacity, w, k_scale, v_scale)
+  if (code == kCodeE4M3) {
+    if (dtype == 1) PKV_PC8(F16, kCodeE4M3); else PKV_PC8(BF16, kCodeE4M3);
+  } else {
+    if (dtype == 1) PKV_PC8(F16, kCodeI8); else PKV_PC8(BF16, kCodeI8);
+  }
+#undef PKV_PC8
   return hipGetLastError();
 }
 

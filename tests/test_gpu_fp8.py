@@ -204,3 +204,35 @@ def test_kv8_plan_reused_across_layers(code, P):
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"layer {i}"
         if i == 0:
             _check(case, got, _oracle(case), f"{code} planned layer 0")
+
+
+@pytest.mark.parametrize("code", CODES)
+@pytest.mark.parametrize("key,over,P", [
+    ("c3", dict(num_seqs=64, len_cap=6000), 0), ("c2", dict(num_seqs=12, dtype="f16"), 512),
+    ("c3", dict(lens=[0, 1, 15, 16, 17, 2047, 2048, 2049, 4095], block_size=8), 0),
+])
+def test_kv8_plan_and_cache_equals_write_then_plan(code, key, over, P):
+    """The fused launch (8-bit cache write + work-list plan), then the planned kernel and the
+    reduce: caches and output bit-identical to reshape_and_cache_fp8 followed by the one-call
+    8-bit decode; the output matches the oracle."""
+    case = with_8bit_cache(make_decode_case(key, **over), code)
+    ref = _decode(case, P)
+    q = case.query.to(DEV)
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+    L, ks, vs = case.max_context_len, case.k_scale, case.v_scale
+    ref_kc, ref_vc = kc.clone(), vc.clone()
+    pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), ref_kc, ref_vc,
+                              case.slot_mapping.to(DEV), ks, vs, code=code)
+    out = torch.full_like(q, float("nan"))
+    log(f"{code} plan+cache {key} P={P}")
+    ws = pkv.paged_attention_plan_and_cache_fp8(out, q, kc, vc, bt, cl, case.scale, ks, vs, L,
+                                                case.new_key.to(DEV), case.new_value.to(DEV),
+                                                case.slot_mapping.to(DEV), P, code=code)
+    pkv.paged_attention_partitions_planned_fp8(out, q, kc, vc, bt, cl, case.scale, ks, vs, L, P,
+                                               ws, code=code)
+    pkv.paged_attention_reduce(out, cl, L, ws, P)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, ref_kc) and torch.equal(vc, ref_vc)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    _check(case, out, _oracle(case), f"{code} plan+cache {key}")
