@@ -16,15 +16,17 @@
 // part of a sequence there).
 //
 // Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
-// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (four stage buffers;
-// the loads run two stages ahead, and waves 4-7 run one stage behind waves 0-3), and every wave reads them from there: the stage is fetched
-// once for all 256 columns.
+// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (three stage buffers;
+// the loads run two stages ahead), and every wave reads them from there: the stage is fetched
+// once for all 256 columns.  A wave computes the logits of the next stage while its VALU
+// turns the current stage's logits into weights.
 //   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
-//           rows, 16 columns per product);
-//   values: LDS rows of 32 tokens (96-byte stride), stored in the order
-//           (4q..4q+3, 16+4q..16+4q+3) for q = 0..3, so that a lane's 16-byte read is the A
-//           operand of O^T += V^T P^T with 32 keys per product and the lane's own softmax
-//           weights (two 16x16 logit tiles) are its B operand without any data movement.
+//           rows, 16 columns per product), the 32 tokens stored in the row order
+//           (8q..8q+3 for q = 0..3, then 8q+4..8q+7), so that lane quad q of the two 16x16
+//           logit tiles holds the logits of keys 8q..8q+7;
+//   values: LDS rows of 32 tokens in their natural order (96-byte stride): a lane's 16-byte
+//           read is the A operand of O^T += V^T P^T with 32 keys per product, and the lane's
+//           own 8 softmax weights are its B operand without any data movement.
 // Online softmax per column in base 2 with a lazy maximum: the running maximum is only moved
 // (and the accumulators rescaled) when a stage's maximum exceeds it by more than 2^8, so most
 // stages skip the rescale; weights are rounded once to the element type, and the row sums
@@ -75,11 +77,15 @@ __device__ __forceinline__ uint4 mask8(uint4 v, int base, int limit) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Plan: one workgroup lists the work items, longest first (32 length classes, the longest
-// class first; the order inside a class is arbitrary, which changes no result: every item
-// writes its own outputs or partial slot).  Requests whose metadata is inconsistent (negative
-// or decreasing offsets, rows past num_tokens, a chunk longer than its context, a context
-// longer than max_context_len) get no items: their rows are left unwritten.
+// Plan: one workgroup lists the work items.  A request's items are listed together (its
+// tiles, longest first), so that the workgroups of one request and one KV head run side by
+// side on one XCD (workgroup t runs on XCD t mod 8 and takes KV head t mod num_kv_heads) and
+// read the request's keys and values through that XCD's L2 once, not once per tile.
+// Requests go longest first (32 classes by their longest item, the longest class first; the
+// order inside a class is arbitrary, which changes no result: every item writes its own
+// outputs or partial slot).  Requests whose metadata is inconsistent (negative or decreasing
+// offsets, rows past num_tokens, a chunk longer than its context, a context longer than
+// max_context_len) get no items: their rows are left unwritten.
 // ---------------------------------------------------------------------------------------
 constexpr int kPlanClasses = 32;
 
@@ -119,8 +125,21 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
   auto cls = [&](int len) {
     return kPlanClasses - 1 - min(kPlanClasses - 1, int((int64_t)len * kPlanClasses / span));
   };
-  for (int b = tid; b < a.num_seqs; b += 1024)
-    for_each_item(a, b, [&](int, int k0, int k1) { atomicAdd(&s_count[cls(k1 - k0)], 1); });
+  // a request's item count and its longest item
+  auto count = [&](int b, int& longest) {
+    int n_items = 0;
+    longest = 0;
+    for_each_item(a, b, [&](int, int k0, int k1) {
+      ++n_items;
+      longest = max(longest, k1 - k0);
+    });
+    return n_items;
+  };
+  for (int b = tid; b < a.num_seqs; b += 1024) {
+    int longest;
+    const int n_items = count(b, longest);
+    if (n_items > 0) atomicAdd(&s_count[cls(longest)], n_items);
+  }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
@@ -132,12 +151,17 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
     a.queue[1] = uint32_t(min<int64_t>(run, a.capacity));
   }
   __syncthreads();
-  for (int b = tid; b < a.num_seqs; b += 1024)
+  for (int b = tid; b < a.num_seqs; b += 1024) {
+    int longest;
+    const int n_items = count(b, longest);
+    if (n_items == 0) continue;
+    int idx = atomicAdd(&s_count[cls(longest)], n_items);
     for_each_item(a, b, [&](int j, int k0, int k1) {
-      const int idx = atomicAdd(&s_count[cls(k1 - k0)], 1);
       if (idx < a.capacity)
         a.items[idx] = make_uint4(uint32_t(b), uint32_t(j), uint32_t(k0), uint32_t(k1));
+      ++idx;
     });
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -157,8 +181,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int VSTAGE = D * VRS;
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
-  // stage s - 1 (values, late waves), s (read), s + 1 (ready), s + 2 (being written)
-  constexpr int NBUF = 4;
+  // stage s (values read), s + 1 (keys read), s + 2 (being written)
+  constexpr int NBUF = 3;
+  // register sets of stage copies in flight: a stage is loaded R steps before it is stored.
+  // Three (loads about 3 us ahead of their use at c6's pace; deeper measured no faster), a
+  // multiple of NBUF, so that the buffer of every step of the unrolled loop is a constant.
+  constexpr int R = 3;
+  static_assert(R >= 2 && R % NBUF == 0, "stages 0 and 1 are staged through two sets");
   __shared__ __align__(16) char s_k[NBUF][KSTAGE];
   __shared__ __align__(16) char s_v[NBUF][VSTAGE];
   __shared__ int s_ids[kPrefillMaxIds];
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // Raw pieces as loaded (8 codes of an 8-bit cache take 8 bytes); they are widened to the
   // 16-bit type only when stored to LDS, so no load has to be waited for early.
   using Raw = typename std::conditional<KV8, uint2, uint4>::type;
-  Raw kA[PPT], vA[PPT], kB[PPT], vB[PPT];
+  Raw kR[R][PPT], vR[R][PPT];  // register sets: stage u sits in set u mod R
   auto widen = [&](const Raw& r) -> uint4 {
     if constexpr (KV8) return widen8<DT, KVC>(r.x, r.y);
     else return r;
@@ -268,14 +297,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
       if (KPIECES % NT == 0 || p < KPIECES) {
-        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + (p & 31)) * 16]) = widen(kst[i]);
+        const int tok = p & 31;
+        const int krow = ((tok >> 2) & 1) * 16 + (tok >> 3) * 4 + (tok & 3);
+        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + krow) * 16]) = widen(kst[i]);
         const int d = p >> 2, t8 = (p & 3) * 8;
         uint4 v = widen(vst[i]);
         if (k0 + 32 * (s + 1) > k1) v = mask8(v, k0 + 32 * s + t8, k1);  // the last stage only
-        const int q = (t8 & 15) >> 2, half = t8 >> 4;
-        char* row = &s_v[buf][d * VRS + half * 8];
-        *reinterpret_cast<uint2*>(row + q * 16) = make_uint2(v.x, v.y);
-        *reinterpret_cast<uint2*>(row + (q + 1) * 16) = make_uint2(v.z, v.w);
+        *reinterpret_cast<uint4*>(&s_v[buf][d * VRS + t8 * 2]) = v;
       }
     }
   };
@@ -310,41 +338,40 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         for (int cb = 0; cb < CB; ++cb) S[tt][cb] = mma(DT(), ka, qop[cb][kc], S[tt][cb]);
       }
   };
-  // per column: the stage's largest logit, in base-2 units (the scale is positive, so the
-  // maximum commutes with it)
+  // per column and lane: the largest of the lane's 8 logits of the stage (raw units)
   auto stage_max = [&](const f32x4 (&S)[2][CB], float (&mc)[CB]) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      float mx = fmaxf(fmaxf(fmaxf(S[0][cb][0], S[0][cb][1]), fmaxf(S[0][cb][2], S[0][cb][3])),
-                       fmaxf(fmaxf(S[1][cb][0], S[1][cb][1]), fmaxf(S[1][cb][2], S[1][cb][3])));
-      mc[cb] = column_max(mx) * sl2;
-    }
+    for (int cb = 0; cb < CB; ++cb)
+      mc[cb] = fmaxf(fmaxf(fmaxf(S[0][cb][0], S[0][cb][1]), fmaxf(S[0][cb][2], S[0][cb][3])),
+                     fmaxf(fmaxf(S[1][cb][0], S[1][cb][1]), fmaxf(S[1][cb][2], S[1][cb][3])));
   };
-  // keys a column must not see (causal, or past the item): logit -inf
+  // keys a column must not see (causal, or past the item): logit -inf.  Element r of logit
+  // tile tt of lane quad q is the key 8 q + 4 tt + r of the stage.
   auto mask_stage = [&](int t0, f32x4 (&S)[2][CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int lim = end_c[cb] - (t0 + quad * 4);
+      const int lim = end_c[cb] - (t0 + quad * 8);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (tt * 16 + r >= lim) S[tt][cb][r] = -INFINITY;
+          if (tt * 4 + r >= lim) S[tt][cb][r] = -INFINITY;
     }
   };
-  // lazy maximum: move it (and rescale) only when a column's stage maximum exceeds it by more
-  // than the margin; the wave takes the branch if any of its columns needs it
-  auto rescale = [&](const float (&mc)[CB]) {
-    bool need[CB], any = false;
+  // lazy maximum: move it (and rescale) only when a column's stage maximum, in base-2 units,
+  // exceeds it by more than the margin; the wave takes the branch if any of its columns needs
+  // it.  The test runs on each lane's own maximum first: rounding x * scale is monotonic for a
+  // positive scale, so some lane of a column passes it exactly when the column's maximum does,
+  // and the column maximum (a cross-lane exchange) is only formed inside the rare branch.
+  auto rescale = [&](const float (&lm)[CB]) {
+    bool any = false;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      need[cb] = mc[cb] > m_run[cb] + kLazyRescale;
-      any |= need[cb];
-    }
+    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] * sl2 > m_run[cb] + kLazyRescale;
     if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float m_new = need[cb] ? mc[cb] : m_run[cb];
+        const float mc = column_max(lm[cb]) * sl2;
+        const float m_new = mc > m_run[cb] + kLazyRescale ? mc : m_run[cb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 at first (m = -inf)
         m_run[cb] = m_new;
         lacc[cb] *= alpha;
@@ -371,81 +398,74 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // a stage with a key some column of the wave must not see
   auto needs_mask = [&](int s) { return k0 + 32 * s + 32 > wave_full; };
 
-  // One stage per step.  Stages past a wave's last column are computed too: their keys are
-  // all masked (zero weights).  The block written in step s is the one stage s - 2 used.
+  // Software pipeline, one stage per step.  Step s starts from the logits of stage s (their
+  // products were issued in step s - 1): it masks them where needed and tests the lazy maximum,
+  // then issues the logit products of stage s + 1 -- independent work for the matrix cores
+  // while the VALU turns stage s's logits into weights -- and last the P.V products of stage s.
+  // Stages past a wave's last column are computed too: their keys are all masked (zero
+  // weights).  The logits of stage nst, past the end, come from a block holding a copy of the
+  // last stage and are never used.
   f32x4 S[2][CB];
-  float mc[CB];
-  // Two schedules, so that the two waves sharing a SIMD (w and w + 4) are out of phase: early
-  // waves (w < 4) do stage s's logits, softmax and P.V in step s; late waves do stage s - 1's
-  // P.V first, then stage s's logits and softmax, keeping its weights for the next step.  A
-  // late wave's products then overlap its partner's softmax, and the reverse, though the
-  // barrier of each stage keeps the two in step.
-  const bool late = w >= NW / 2;
-  uint4 pop_prev[CB];
-  auto pv = [&](int s, const uint4 (&pop)[CB]) {
+  auto step = [&](int s) {
+    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
+    float lm[CB];
+    stage_max(S, lm);
+    rescale(lm);  // before the stage's weights and its P.V
     uint4 vop[NDT];
     const char* sv = s_v[s % NBUF];
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
       vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
+    f32x4 Sn[2][CB];
+    qk((s + 1) % NBUF, Sn);
+    uint4 pop[CB];
+    weights(S, pop);
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
-  };
-  auto softmax = [&](int s, uint4 (&pop)[CB]) {
-    qk(s % NBUF, S);
-    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
-    stage_max(S, mc);
-    rescale(mc);  // before the stage's weights: o holds stages < s (late waves: P.V of s - 1 done)
-    weights(S, pop);
-  };
-  auto step = [&](int s) {
-    if (!late) {
-      // value operands first: their LDS latency hides behind the logits and the softmax
-      uint4 vop[NDT];
-      const char* sv = s_v[s % NBUF];
 #pragma unroll
-      for (int i = 0; i < NDT; ++i)
-        vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
-      uint4 pop[CB];
-      softmax(s, pop);
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int i = 0; i < NDT; ++i)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
-    } else {
-      if (s > 0) pv(s - 1, pop_prev);
-      softmax(s, pop_prev);
-    }
+      for (int cb = 0; cb < CB; ++cb) S[tt][cb] = Sn[tt][cb];
   };
 
   __syncthreads();  // s_ids
-  load_stage(0, kA, vA);
-  load_stage(1, kB, vB);
-  store_stage(0, 0, kA, vA);
-  store_stage(1, 1, kB, vB);
-  load_stage(2, kA, vA);
-  load_stage(3, kB, vB);
+  load_stage(0, kR[0], vR[0]);
+  load_stage(1, kR[1], vR[1]);
+  store_stage(0, 0, kR[0], vR[0]);
+  store_stage(1, 1, kR[1], vR[1]);
+#pragma unroll
+  for (int u = 2; u < R + 2; ++u) load_stage(u, kR[u % R], vR[u % R]);
   __syncthreads();
+  if (active) qk(0, S);
 
-  // Steps in pairs: the only way back to the loop head is the end of a pair, so the wait
-  // counters there know exactly which loads are in flight.  Registers A carry the even
-  // stages, B the odd ones, each loaded two steps before it is stored; stores and loads are
-  // not skipped past the end (the blocks they fill are free, and unread after the loop).
+  // Steps in groups of R: the only way back to the loop head is the end of a group, so the
+  // wait counters there know exactly which loads are in flight.  Step s stores stage s + 2 to
+  // LDS from its register set, loaded R steps before, and loads stage s + 2 + R into it;
+  // stores and loads are not skipped past the end (the blocks they fill are free, and unread
+  // after the loop but for stage nst's discarded logits).
   int s = 0;
-  for (; s + 1 < nst; s += 2) {
-    store_stage((s + 2) % NBUF, s + 2, kA, vA);
-    load_stage(s + 4, kA, vA);
-    if (active) step(s);
-    __syncthreads();
-    store_stage((s + 3) % NBUF, s + 3, kB, vB);
-    load_stage(s + 5, kB, vB);
-    if (active) step(s + 1);
+  for (; s + R - 1 < nst; s += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int set = (u + 2) % R;
+      store_stage((s + u + 2) % NBUF, s + u + 2, kR[set], vR[set]);
+      load_stage(s + u + 2 + R, kR[set], vR[set]);
+      if (active) step(s + u);
+      __syncthreads();
+    }
+  }
+  // fewer than R stages left: stage s + u + 1 is in LDS before step s + u, s + u + 2 in its
+  // register set
+#pragma unroll
+  for (int u = 0; u < R - 1; ++u) {
+    if (s + u >= nst) break;
+    const int set = (u + 2) % R;
+    store_stage((s + u + 2) % NBUF, s + u + 2, kR[set], vR[set]);
+    if (active) step(s + u);
     __syncthreads();
   }
-  if (s < nst && active) step(s);  // an odd count: the last stage
-  if (active && late) pv(nst - 1, pop_prev);  // the block is intact: no store since the last step
   if (!active) return;
 
   // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column
