@@ -94,9 +94,15 @@ class _Roctx:
 ROCTX = _Roctx()
 
 
-def kernel_source_hash(kv: str = "native") -> str:
+PREFILL_SOURCES = ["attention_prefill.hip", "pkv_prefill.h", "pkv_kv8.h", "pkv_device.h",
+                   "pkv_internal.h"]
+
+
+def kernel_source_hash(kv: str = "native", workload: str = "c3") -> str:
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES if kv == "native" else KERNEL_SOURCES_KV8):
+    srcs = (PREFILL_SOURCES if workload == "c6"
+            else KERNEL_SOURCES if kv == "native" else KERNEL_SOURCES_KV8)
+    for f in srcs:
         p = os.path.join(ROOT, "paged_kv_cache_164_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
@@ -104,7 +110,8 @@ def kernel_source_hash(kv: str = "native") -> str:
 
 
 def traffic_name(workload: str, kv: str = "native") -> str:
-    return f"partition_kernel_{workload}{'' if kv == 'native' else '_' + kv}_traffic.json"
+    kind = "multi_query_kernel" if workload == "c6" else "partition_kernel"
+    return f"{kind}_{workload}{'' if kv == 'native' else '_' + kv}_traffic.json"
 
 
 def traffic_from_profile(workload: str, kv: str = "native"):
@@ -114,12 +121,13 @@ def traffic_from_profile(workload: str, kv: str = "native"):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_source_hash") != kernel_source_hash(kv):
+    if d.get("kernel_source_hash") != kernel_source_hash(kv, workload):
         return None
     return d.get("hbm_bytes_per_launch")
 
 
 PARTITION_KERNELS = ("gqa_grid_kernel", "decode_valu_kernel", "fp8_grid_kernel")
+MULTI_QUERY_KERNELS = ("prefill_kernel<",)
 
 
 def _counter_means(path: str):
@@ -146,10 +154,11 @@ def derive_traffic(workload: str, fetch_csv: str, write_csv: str, cal_fetch_csv:
 
     f_cal = pick(_counter_means(cal_fetch_csv), ("copy_blocks_kernel",)) * 1024
     w_cal = pick(_counter_means(cal_write_csv), ("copy_blocks_kernel",)) * 1024
-    f_k = pick(_counter_means(fetch_csv), PARTITION_KERNELS) * 1024
-    w_k = pick(_counter_means(write_csv), PARTITION_KERNELS) * 1024
+    names = MULTI_QUERY_KERNELS if workload == "c6" else PARTITION_KERNELS
+    f_k = pick(_counter_means(fetch_csv), names) * 1024
+    w_k = pick(_counter_means(write_csv), names) * 1024
     rec = {"workload": workload if kv == "native" else f"{workload}-{kv}",
-           "kernel_source_hash": kernel_source_hash(kv),
+           "kernel_source_hash": kernel_source_hash(kv, workload),
            "fetch_scale": known / f_cal, "write_scale": known / w_cal,
            "fetch_bytes_raw": f_k, "write_bytes_raw": w_k,
            "hbm_bytes_per_launch": round(f_k * known / f_cal + w_k * known / w_cal)}
@@ -644,7 +653,8 @@ def run_prefill(args) -> int:
                    "attention_flops": flops, "timing": "graph replay" if args.graph else "eager"},
         "query_tokens_per_s": round(T / (ms_step / 1e3), 1),
         "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(k_tflops / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(k_tflops / peak, 4),
+                     "traffic": traffic_from_profile(args.workload, args.kv),
                      "kernel": "multi-query attention: plan + attention kernel",
                      "kernel_ms": round(k_avg, 5), "kernel_ms_median": round(float(np.median(k_ms)), 5),
                      "kernel_ms_p10_p90":
