@@ -252,15 +252,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // the last one, from L2): a load under a branch would make every wait conservative.
   // Per-thread constants of the copies (a stage starts at a multiple of 32 >= k0, which is
   // itself a multiple of 32, so a thread's pieces sit at fixed offsets inside their blocks):
-  //   key piece p: dims 8 (p / 32) .. +8 of stage token p % 32
-  //   value piece p: dim p / 4, stage tokens 8 (p % 4) .. +8 (inside one block)
+  //   key piece: dims 8 c8 .. +8 of stage token tok
+  //   value piece: dim d, stage tokens t8 .. t8 + 8 (inside one block)
+  // Which piece a thread copies: key piece p fills LDS row krow = p mod 32 of dim chunk
+  // c8 = p / 32 (token tok of that row, in the row order above); among the value pieces, 16
+  // neighbouring ones are one 8-token chunk of 16 dims, so that 16 lanes store to 16 rows in
+  // the pattern the P.V operand reads use.
+  auto key_piece = [](int p, int& c8, int& krow, int& tok) {
+    c8 = p >> 5;
+    krow = p & 31;
+    tok = 8 * ((krow >> 2) & 3) + 4 * (krow >> 4) + (krow & 3);
+  };
+  auto value_piece = [](int p, int& d, int& t8) {
+    d = ((p >> 6) << 4) + (p & 15);
+    t8 = ((p >> 4) & 3) * 8;
+  };
   constexpr int IDS_PER_STAGE = 32 / BS;
   int kid[PPT], vid[PPT];
   uint32_t koff[PPT], voff[PPT];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const int p = min(tid + i * NT, KPIECES - 1);
-    const int c8 = p >> 5, tt = p & 31, d = p >> 2, t8 = (p & 3) * 8;
+    int c8, krow, tt, d, t8;
+    key_piece(p, c8, krow, tt);
+    value_piece(p, d, t8);
     kid[i] = tt / BS;
     vid[i] = t8 / BS;
     if constexpr (KV8) {  // 8-bit cache: keys [D/16][bs][16], values [D][bs], one byte each
@@ -297,10 +312,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int i = 0; i < PPT; ++i) {
       const int p = tid + i * NT;
       if (KPIECES % NT == 0 || p < KPIECES) {
-        const int tok = p & 31;
-        const int krow = ((tok >> 2) & 1) * 16 + (tok >> 3) * 4 + (tok & 3);
-        *reinterpret_cast<uint4*>(&s_k[buf][((p >> 5) * 32 + krow) * 16]) = widen(kst[i]);
-        const int d = p >> 2, t8 = (p & 3) * 8;
+        int c8, krow, tok, d, t8;
+        key_piece(p, c8, krow, tok);
+        value_piece(p, d, t8);
+        *reinterpret_cast<uint4*>(&s_k[buf][(c8 * 32 + krow) * 16]) = widen(kst[i]);
         uint4 v = widen(vst[i]);
         if (k0 + 32 * (s + 1) > k1) v = mask8(v, k0 + 32 * s + t8, k1);  // the last stage only
         *reinterpret_cast<uint4*>(&s_v[buf][d * VRS + t8 * 2]) = v;
