@@ -754,18 +754,17 @@ def main() -> int:
     def step(ev=None, st=None):
         st = stream if st is None else st
         ROCTX.push("step")
-        # the work list depends on tables, lengths (and groups) only: built before the write
+        # the work list depends on tables, lengths (and groups) only: one launch builds it and
+        # writes the new tokens
         if beam:
-            ROCTX.push("plan")
-            pkv.paged_attention_plan_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"], scale,
-                                            lmax, P, ws, stream=st)
-            ROCTX.pop()
-            # device pointer table made once, outside any graph capture
+            # copy-on-write first: new tokens land in the copied blocks.  Device pointer table
+            # made once, outside any graph capture.
             ROCTX.push("copy_blocks")
             pkv.copy_blocks([kc], [vc], t["mapping"], stream=st, _ptr_buffers=ptrs)
             ROCTX.pop()
-            ROCTX.push("reshape_and_cache")
-            pkv.reshape_and_cache(nk, nv, kc, vc, slots, stream=st)
+            ROCTX.push("plan and reshape_and_cache")
+            pkv.paged_attention_plan_and_cache_shared(out, q, kc, vc, bt, cl, t["gs"], t["pl"],
+                                                      scale, lmax, nk, nv, slots, P, ws, stream=st)
             ROCTX.pop()
         elif kv8:
             ROCTX.push("plan and reshape_and_cache")

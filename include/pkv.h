@@ -318,6 +318,27 @@ int pkv_paged_attention_partitions_planned_shared(
     int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_paged_attention_plan_and_cache for the shared-prefix decode: the write of
+ * the step's new tokens (pkv_reshape_and_cache) and pkv_paged_attention_plan_shared
+ * in one launch.  The caches and the workspace end exactly as after those two
+ * calls; pkv_paged_attention_partitions_planned_shared and
+ * pkv_paged_attention_reduce complete the step.  A beam step's copy-on-write
+ * (pkv_copy_blocks) must be ordered before this call when a new token lands in
+ * a copied block.
+ *   arguments up to workspace_bytes: as for pkv_paged_attention_plan_shared
+ *   key, value, slot_mapping, num_tokens, num_blocks, key_stride, value_stride:
+ *     as for pkv_reshape_and_cache, into the same key_cache and value_cache
+ * Errors as for those two calls; nothing is enqueued when any argument fails. */
+int pkv_paged_attention_plan_and_cache_shared(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, const void* key,
+    const void* value, const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+    int64_t key_stride, int64_t value_stride, void* stream);
+
 /*
  * Decode attention over an 8-bit KV cache: keys and values stored as OCP FP8
  * E4M3 codes with one float scale per cache (key = code * k_scale, value =

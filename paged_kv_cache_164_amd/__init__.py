@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     paged_attention_plan,
     paged_attention_plan_and_cache,
     paged_attention_plan_and_cache_fp8,
+    paged_attention_plan_and_cache_shared,
     paged_attention_plan_fp8,
     paged_attention_plan_shared,
     paged_attention_reduce,

@@ -48,6 +48,10 @@ _SIGNATURES = {
     "pkv_paged_attention_partitions_planned_shared": (_c_int, _DECODE_ARGTYPES[:6]
                                                       + [_c_p, _c_p, _c_int]
                                                       + _DECODE_ARGTYPES[6:]),
+    "pkv_paged_attention_plan_and_cache_shared": (_c_int, _DECODE_ARGTYPES[:6] + [_c_p, _c_p, _c_int]
+                                                  + _DECODE_ARGTYPES[6:18]
+                                                  + [_c_p, _c_p, _c_p, _c_int, _c_i64, _c_i64,
+                                                     _c_i64, _c_p]),
     "pkv_paged_attention_decode_fp8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
                                        + _DECODE_ARGTYPES[7:]),
     "pkv_paged_attention_decode_int8": (_c_int, _DECODE_ARGTYPES[:7] + [_c_f, _c_f]
@@ -277,7 +281,7 @@ def paged_attention_decode_shared(out, query, key_cache, value_cache, block_tabl
 
 def _shared_call(name, out, query, key_cache, value_cache, block_tables, context_lens,
                  group_starts, prefix_lens, scale, max_context_len, partition_size, workspace,
-                 stream):
+                 stream, tail=()):
     args, ws = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                             max_context_len, partition_size, workspace, stream)
     _on_gpu(group_starts, prefix_lens)
@@ -287,6 +291,7 @@ def _shared_call(name, out, query, key_cache, value_cache, block_tables, context
             or not (group_starts.is_contiguous() and prefix_lens.is_contiguous())):
         raise PKVError("group_starts must be int32 [num_groups + 1], prefix_lens int32 [num_groups]")
     args = args[:6] + (group_starts.data_ptr(), prefix_lens.data_ptr(), ng) + args[6:]
+    args = args[:-1] + tuple(tail) + args[-1:]  # arguments before the stream
     _check(getattr(library(), name)(*args), name)
     return ws
 
@@ -299,6 +304,23 @@ def paged_attention_plan_shared(out, query, key_cache, value_cache, block_tables
     return _shared_call("pkv_paged_attention_plan_shared", out, query, key_cache, value_cache,
                         block_tables, context_lens, group_starts, prefix_lens, scale,
                         max_context_len, partition_size, workspace, stream)
+
+
+def paged_attention_plan_and_cache_shared(out, query, key_cache, value_cache, block_tables,
+                                          context_lens, group_starts, prefix_lens, scale,
+                                          max_context_len, key, value, slot_mapping,
+                                          partition_size=0, workspace=None, stream=None):
+    """reshape_and_cache of the step's new tokens and the shared-prefix work-list plan in one
+    launch; returns the workspace holding the list (paged_attention_partitions_planned_shared
+    and paged_attention_reduce complete the step)."""
+    N, NB = _cache_write_checks(key, value, key_cache, value_cache, slot_mapping)
+    if key.dtype != query.dtype:
+        raise PKVError("key and value must have the query's dtype")
+    return _shared_call("pkv_paged_attention_plan_and_cache_shared", out, query, key_cache,
+                        value_cache, block_tables, context_lens, group_starts, prefix_lens, scale,
+                        max_context_len, partition_size, workspace, stream,
+                        tail=(key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), N, NB,
+                              key.stride(0), value.stride(0)))
 
 
 def paged_attention_partitions_planned_shared(out, query, key_cache, value_cache, block_tables,

@@ -386,13 +386,14 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void*
   }
 }
 
-#define PKV_SHARED_PARAMS                                                                     \
+#define PKV_SHARED_PARAMS_NO_STREAM                                                           \
   void *out, const void *query, const void *key_cache, const void *value_cache,               \
       const int32_t *block_tables, const int32_t *context_lens, const int32_t *group_starts,  \
       const int32_t *prefix_lens, int32_t num_groups, float scale, int32_t num_seqs,          \
       int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,         \
       int32_t max_num_blocks_per_seq, int32_t max_context_len, int32_t dtype,                 \
-      int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream
+      int32_t partition_size, void *workspace, size_t workspace_bytes
+#define PKV_SHARED_PARAMS PKV_SHARED_PARAMS_NO_STREAM, void *stream
 
 // The shared-prefix decode, whole (mode 0: plan, attention kernel, reduce), the plan alone
 // (mode 1) or the attention kernel on the plan already in the workspace (mode 2).
@@ -521,20 +522,21 @@ int pkv_paged_attention_partitions_planned(PKV_DECODE_PARAMS) {
   return phase1_mode(PKV_DECODE_ARGS, stream, 2);
 }
 
-int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void* key_cache,
-                                       const void* value_cache, const int32_t* block_tables,
-                                       const int32_t* context_lens, float scale, int32_t num_seqs,
-                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                                       int32_t block_size, int32_t max_num_blocks_per_seq,
-                                       int32_t max_context_len, int32_t dtype,
-                                       int32_t partition_size, void* workspace,
-                                       size_t workspace_bytes, const void* key, const void* value,
-                                       const int64_t* slot_mapping, int32_t num_tokens,
-                                       int64_t num_blocks, int64_t key_stride,
-                                       int64_t value_stride, void* stream) {
+// The plan and the new tokens' cache write (16- and 32-bit caches) in one launch; groups: the
+// shared-prefix plan, or null for the plain one.
+static int plan_and_cache_16(void* out, const void* query, const void* key_cache,
+                             const void* value_cache, const int32_t* block_tables,
+                             const int32_t* context_lens, float scale, int32_t num_seqs,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                             int32_t block_size, int32_t max_num_blocks_per_seq,
+                             int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, const Groups* groups,
+                             const void* key, const void* value, const int64_t* slot_mapping,
+                             int32_t num_tokens, int64_t num_blocks, int64_t key_stride,
+                             int64_t value_stride, void* stream) {
   try {
     Resolved r;
-    int rc = resolve_decode(PKV_DECODE_ARGS, &r);
+    int rc = resolve_decode(PKV_DECODE_ARGS, &r, groups);
     if (rc != PKV_OK) return rc;
     const int eb = elem_bytes(dtype);
     if (num_tokens < 0 || num_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
@@ -559,6 +561,31 @@ int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void*
   } catch (...) {
     return fail(PKV_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+int pkv_paged_attention_plan_and_cache(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, float scale, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_num_blocks_per_seq,
+                                       int32_t max_context_len, int32_t dtype,
+                                       int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, const void* key, const void* value,
+                                       const int64_t* slot_mapping, int32_t num_tokens,
+                                       int64_t num_blocks, int64_t key_stride,
+                                       int64_t value_stride, void* stream) {
+  return plan_and_cache_16(PKV_DECODE_ARGS, nullptr, key, value, slot_mapping, num_tokens,
+                           num_blocks, key_stride, value_stride, stream);
+}
+
+int pkv_paged_attention_plan_and_cache_shared(PKV_SHARED_PARAMS_NO_STREAM, const void* key,
+                                              const void* value, const int64_t* slot_mapping,
+                                              int32_t num_tokens, int64_t num_blocks,
+                                              int64_t key_stride, int64_t value_stride,
+                                              void* stream) {
+  const Groups groups{group_starts, prefix_lens, num_groups};
+  return plan_and_cache_16(PKV_DECODE_ARGS, &groups, key, value, slot_mapping, num_tokens,
+                           num_blocks, key_stride, value_stride, stream);
 }
 
 // The plan and the write of the new tokens into an 8-bit cache, in one launch.

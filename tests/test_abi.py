@@ -25,7 +25,7 @@ def test_exports_every_header_symbol():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         declared |= set(re.findall(r"\b(pkv_\w+)\s*\(", open(h).read()))
     assert declared == set(pkv.EXPORTED_SYMBOLS)
-    assert len(declared) == 46
+    assert len(declared) == 47
     for name in declared:
         assert hasattr(lib, name), name
 

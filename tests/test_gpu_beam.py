@@ -38,17 +38,14 @@ def _decode_shared(q, kc, vc, tables, lens, scale, beams, prompt_len):
     return out
 
 
-def _beam_run(num_prompts, n_pairs=None):
-    bc = make_beam_case(num_prompts=num_prompts)
+def _cow_step(bc):
+    """One beam step's bookkeeping: copy-on-write of each beam's partial last block into a
+    free block, and the slot of its next token there.  Returns the new tables and lengths,
+    the copy pairs, the slots, the new keys and values and the remaining free list."""
     bs = bc.cfg.block_size
     B, H, D = bc.query.shape
-    log(f"beam: {num_prompts} prompts x {bc.beams} beams, H={H}, pool={bc.key_cache.shape[0]}")
-    kc, vc = bc.key_cache.to(DEV), bc.value_cache.to(DEV)
-    q = bc.query.to(DEV)
     tables, lens = bc.block_tables.copy(), bc.context_lens.copy()
     free, ref = list(bc.free_blocks), bc.ref_count.copy()
-
-    # (i) copy-on-write of each beam's partial last block, then its next token
     pairs, slots = [], np.full(B, -1, dtype=np.int64)
     for b in range(B):
         L = int(lens[b])
@@ -64,6 +61,17 @@ def _beam_run(num_prompts, n_pairs=None):
     nk = draw_normal((B, H, D), "f16", bc.cfg.seed, S_COW)
     nv = draw_normal((B, H, D), "f16", bc.cfg.seed, S_COW + 100)
     mapping = np.array(pairs, dtype=np.int64).reshape(-1, 2)
+    return tables, lens, pairs, mapping, slots, nk, nv, free
+
+
+def _beam_run(num_prompts, n_pairs=None):
+    bc = make_beam_case(num_prompts=num_prompts)
+    B, H, D = bc.query.shape
+    log(f"beam: {num_prompts} prompts x {bc.beams} beams, H={H}, pool={bc.key_cache.shape[0]}")
+    kc, vc = bc.key_cache.to(DEV), bc.value_cache.to(DEV)
+    q = bc.query.to(DEV)
+    # (i) copy-on-write of each beam's partial last block, then its next token
+    tables, lens, pairs, mapping, slots, nk, nv, free = _cow_step(bc)
     pkv.copy_blocks([kc], [vc], torch.from_numpy(mapping).to(DEV))
     pkv.reshape_and_cache(nk.to(DEV), nv.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV))
     out1 = _decode(q, kc, vc, tables, lens, bc.scale)
@@ -125,3 +133,38 @@ def test_beam_small_all_outputs():
 def test_beam_full_size_all_outputs():
     """32 prompts x 4 beams at full size: every (sequence, head) output against the oracle."""
     _beam_run(num_prompts=32)
+
+
+@pytest.mark.parametrize("num_prompts,P", [(8, 0), (32, 512)])
+def test_beam_step_with_fused_plan_and_cache(num_prompts, P):
+    """The beam step as bench.py runs it: copy-on-write, then the new tokens' cache write and the
+    shared-prefix plan in one launch, the planned kernel and the reduce.  Caches and output
+    bit-identical to copy_blocks + reshape_and_cache + the one-call shared-prefix decode."""
+    bc = make_beam_case(num_prompts=num_prompts)
+    B = bc.query.shape[0]
+    tables, lens, pairs, mapping, slots, nk, nv, _ = _cow_step(bc)
+    q = bc.query.to(DEV)
+    bt, cl = torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV)
+    gs = torch.arange(0, B + 1, bc.beams, dtype=torch.int32, device=DEV)
+    pl = torch.full((B // bc.beams,), bc.prompt_len, dtype=torch.int32, device=DEV)
+    mp, sl = torch.from_numpy(mapping).to(DEV), torch.from_numpy(slots).to(DEV)
+    nkd, nvd = nk.to(DEV), nv.to(DEV)
+    L = int(lens.max())
+    log(f"beam fused step: {num_prompts} prompts, {len(pairs)} copy-on-write pairs, P={P}")
+    kc1, vc1 = bc.key_cache.to(DEV), bc.value_cache.to(DEV)
+    pkv.copy_blocks([kc1], [vc1], mp)
+    pkv.reshape_and_cache(nkd, nvd, kc1, vc1, sl)
+    ref = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode_shared(ref, q, kc1, vc1, bt, cl, gs, pl, bc.scale, L, P)
+    kc2, vc2 = bc.key_cache.to(DEV), bc.value_cache.to(DEV)
+    pkv.copy_blocks([kc2], [vc2], mp)
+    out = torch.full_like(q, float("nan"))
+    ws = pkv.paged_attention_plan_and_cache_shared(out, q, kc2, vc2, bt, cl, gs, pl, bc.scale, L,
+                                                   nkd, nvd, sl, P)
+    pkv.paged_attention_partitions_planned_shared(out, q, kc2, vc2, bt, cl, gs, pl, bc.scale, L,
+                                                  P, ws)
+    pkv.paged_attention_reduce(out, cl, L, ws, P)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
