@@ -39,7 +39,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 constexpr int kRunTokens = 16;
 constexpr int kRunMinTokens = 512;  // below it, one workgroup per token spreads the work wider
 
-template <bool VEC_KEY>
+// Values of a run staged through LDS: kValChunk elements of the 16 token rows at a time, read
+// with 16-byte loads (rows padded by 8 elements, so that rows 8 apart sit in other banks).
+constexpr int kValChunk = 512;
+constexpr int kValPitch = kValChunk + 8;
+
+template <bool VEC_KEY, bool VEC_VAL>
 __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint16_t* __restrict__ key_cache, uint16_t* __restrict__ value_cache,
@@ -84,17 +89,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
   }
   // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2), so consecutive
   // threads write consecutive 16-byte pieces: a wave's stores cover whole value rows
-  for (int t = tid; t < 2 * n; t += blockDim.x) {
-    const int e = t >> 1, half = t & 1;
+  auto store_values = [&](int e, int half, const uint32_t (&v)[4]) {
     const int h = e / D, d = e % D;
     const int kb = 8 * half;
-    uint32_t v[4];
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      const uint32_t lo = (kb + k < ntok) ? value[(i0 + kb + k) * value_stride + e] : 0u;
-      const uint32_t hi = (kb + k + 1 < ntok) ? value[(i0 + kb + k + 1) * value_stride + e] : 0u;
-      v[k / 2] = lo | (hi << 16);
-    }
     if (s_vec[half]) {
       const int64_t sl = s_slot[kb];
       uint16_t* dst = value_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
@@ -108,6 +105,42 @@ __global__ __launch_bounds__(256) void reshape_and_cache_runs_kernel(
         value_cache[(slot_block(sl, block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
                     slot_offset(sl, block_size)] = uint16_t(v[k / 2] >> (16 * (k & 1)));
       }
+    }
+  };
+  if constexpr (VEC_VAL) {
+    __shared__ __align__(16) uint16_t s_val[kRunTokens * kValPitch];
+    for (int c0 = 0; c0 < n; c0 += kValChunk) {
+      const int pieces = min(kValChunk, n - c0) / 8;
+      for (int t = tid; t < kRunTokens * pieces; t += blockDim.x) {
+        const int j = t / pieces, q = t % pieces;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (j < ntok) v = *reinterpret_cast<const uint4*>(value + (i0 + j) * value_stride + c0 + q * 8);
+        *reinterpret_cast<uint4*>(&s_val[j * kValPitch + q * 8]) = v;
+      }
+      __syncthreads();
+      for (int t = tid; t < 16 * pieces; t += blockDim.x) {
+        const int el = t >> 1, half = t & 1;
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          v[k] = uint32_t(s_val[(8 * half + 2 * k) * kValPitch + el]) |
+                 (uint32_t(s_val[(8 * half + 2 * k + 1) * kValPitch + el]) << 16);
+        store_values(c0 + el, half, v);
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int t = tid; t < 2 * n; t += blockDim.x) {
+      const int e = t >> 1, half = t & 1;
+      const int kb = 8 * half;
+      uint32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) {
+        const uint32_t lo = (kb + k < ntok) ? value[(i0 + kb + k) * value_stride + e] : 0u;
+        const uint32_t hi = (kb + k + 1 < ntok) ? value[(i0 + kb + k + 1) * value_stride + e] : 0u;
+        v[k / 2] = lo | (hi << 16);
+      }
+      store_values(e, half, v);
     }
   }
 }
@@ -128,7 +161,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 // A run of 8 consecutive tokens landing in 8 consecutive, 8-aligned slots of one block writes
 // its codes of a value row as one 8-byte store; other runs fall back to byte stores.  Keys are
 // 16-byte chunks (16 codes) either way.
-template <class IN, int CODE>
+// VEC: key and value rows 16-byte aligned (16-byte loads of the new elements).
+template <class IN, int CODE, bool VEC>
 __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
@@ -157,36 +191,45 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
   const int D = head_size;
   const int n = num_kv_heads * D;
   const int64_t tile = (int64_t)D * block_size;  // bytes of one (block, head) tile
-  // keys: one 16-byte chunk (16 dims) of one token per thread, token index fastest
+  // keys: one 16-byte chunk (16 dims) of one token per thread, token index fastest; with
+  // aligned rows the 16 elements come in as two 16-byte loads
   for (int t = tid; t < kRunTokens * (n / 16); t += blockDim.x) {
     const int j = t % kRunTokens, c = t / kRunTokens;
     const int64_t sl = s_slot[j];
     if (sl < 0) continue;
     const int h = c / (D / 16), cc = c % (D / 16);
     const uint16_t* e = key + (i0 + j) * key_stride + (int64_t)c * 16;
+    uint16_t el[16];
+    if constexpr (VEC) {
+      const uint4 a = reinterpret_cast<const uint4*>(e)[0], b = reinterpret_cast<const uint4*>(e)[1];
+      const uint32_t wds[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        el[2 * k] = uint16_t(wds[k] & 0xffffu);
+        el[2 * k + 1] = uint16_t(wds[k] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) el[k] = e[k];
+    }
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      w[k] = quant2<CODE>(widen16(IN(), e[4 * k]), widen16(IN(), e[4 * k + 1]), k_scale) |
-             (quant2<CODE>(widen16(IN(), e[4 * k + 2]), widen16(IN(), e[4 * k + 3]), k_scale) << 16);
+      w[k] = quant2<CODE>(widen16(IN(), el[4 * k]), widen16(IN(), el[4 * k + 1]), k_scale) |
+             (quant2<CODE>(widen16(IN(), el[4 * k + 2]), widen16(IN(), el[4 * k + 3]), k_scale) << 16);
     *reinterpret_cast<uint4*>(key_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
                               ((int64_t)cc * block_size + slot_offset(sl, block_size)) * 16) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
-  // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2)
-  for (int t = tid; t < 2 * n; t += blockDim.x) {
-    const int e = t >> 1, half = t & 1;
+  // values: a thread takes one (head, dim) row and 8 tokens (half = t % 2); x holds the 8
+  // elements of the row, tokens past the run 0
+  auto store_values = [&](int e, int half, const float (&x)[8]) {
     const int h = e / D, d = e % D;
     const int kb = 8 * half;
     uint32_t v[2];
 #pragma unroll
-    for (int k = 0; k < 8; k += 4) {
-      float x[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        x[q] = (kb + k + q < ntok) ? widen16(IN(), value[(i0 + kb + k + q) * value_stride + e]) : 0.f;
-      v[k / 4] = quant2<CODE>(x[0], x[1], v_scale) | (quant2<CODE>(x[2], x[3], v_scale) << 16);
-    }
+    for (int k = 0; k < 8; k += 4)
+      v[k / 4] = quant2<CODE>(x[k], x[k + 1], v_scale) | (quant2<CODE>(x[k + 2], x[k + 3], v_scale) << 16);
     if (s_vec[half]) {
       const int64_t sl = s_slot[kb];
       *reinterpret_cast<uint2*>(value_cache + (slot_block(sl, block_size) * num_kv_heads + h) * tile +
@@ -199,6 +242,37 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(
         value_cache[(slot_block(sl, block_size) * num_kv_heads + h) * tile + (int64_t)d * block_size +
                     slot_offset(sl, block_size)] = uint8_t(v[k / 4] >> (8 * (k & 3)));
       }
+    }
+  };
+  if constexpr (VEC) {
+    __shared__ __align__(16) uint16_t s_val[kRunTokens * kValPitch];
+    for (int c0 = 0; c0 < n; c0 += kValChunk) {
+      const int pieces = min(kValChunk, n - c0) / 8;
+      for (int t = tid; t < kRunTokens * pieces; t += blockDim.x) {
+        const int j = t / pieces, q = t % pieces;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (j < ntok) v = *reinterpret_cast<const uint4*>(value + (i0 + j) * value_stride + c0 + q * 8);
+        *reinterpret_cast<uint4*>(&s_val[j * kValPitch + q * 8]) = v;
+      }
+      __syncthreads();
+      for (int t = tid; t < 16 * pieces; t += blockDim.x) {
+        const int el = t >> 1, half = t & 1;
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = widen16(IN(), s_val[(8 * half + k) * kValPitch + el]);
+        store_values(c0 + el, half, x);
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int t = tid; t < 2 * n; t += blockDim.x) {
+      const int e = t >> 1, half = t & 1;
+      const int kb = 8 * half;
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        x[k] = (kb + k < ntok) ? widen16(IN(), value[(i0 + kb + k) * value_stride + e]) : 0.f;
+      store_values(e, half, x);
     }
   }
 }
@@ -286,13 +360,18 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
   if (elem_bytes == 2 && num_tokens >= kRunMinTokens &&
       reinterpret_cast<uintptr_t>(value_cache) % 16 == 0) {
     const dim3 rgrid((unsigned)((num_tokens + kRunTokens - 1) / kRunTokens));
-#define PKV_RUNS(V)                                                                             \
-  hipLaunchKernelGGL((reshape_and_cache_runs_kernel<V>), rgrid, dim3(256), 0, stream,           \
+    const bool vec_val = (reinterpret_cast<uintptr_t>(value) % 16 == 0) && (value_stride % 8 == 0);
+#define PKV_RUNS(V, W)                                                                          \
+  hipLaunchKernelGGL((reshape_and_cache_runs_kernel<V, W>), rgrid, dim3(256), 0, stream,        \
                      static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),    \
                      static_cast<uint16_t*>(key_cache), static_cast<uint16_t*>(value_cache),    \
                      slot_mapping, num_tokens, num_kv_heads, head_size, block_size, num_blocks, \
                      key_stride, value_stride)
-    if (vec) PKV_RUNS(true); else PKV_RUNS(false);
+    if (vec) {
+      if (vec_val) PKV_RUNS(true, true); else PKV_RUNS(true, false);
+    } else {
+      if (vec_val) PKV_RUNS(false, true); else PKV_RUNS(false, false);
+    }
 #undef PKV_RUNS
     return hipGetLastError();
   }
@@ -322,13 +401,20 @@ hipError_t launch_rc8(const void* key, const void* value, void* key_cache, void*
   // many tokens: the run kernel (its 8-byte value stores need an 8-byte aligned cache)
   if (num_tokens >= kRunMinTokens && reinterpret_cast<uintptr_t>(value_cache) % 8 == 0) {
     const dim3 rgrid((unsigned)((num_tokens + kRunTokens - 1) / kRunTokens));
-#define PKV_RUNS8(IN)                                                                           \
-  hipLaunchKernelGGL((reshape_and_cache_kv8_runs_kernel<IN, CODE>), rgrid, dim3(256), 0, stream, \
-                     static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),    \
-                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),      \
-                     slot_mapping, num_tokens, num_kv_heads, head_size, block_size, num_blocks, \
-                     key_stride, value_stride, k_scale, v_scale)
-    if (dtype == 1) PKV_RUNS8(F16); else PKV_RUNS8(BF16);
+    const bool vec_rows = (reinterpret_cast<uintptr_t>(value) % 16 == 0) && (value_stride % 8 == 0) &&
+                          (reinterpret_cast<uintptr_t>(key) % 16 == 0) && (key_stride % 8 == 0);
+#define PKV_RUNS8(IN, W)                                                                        \
+  hipLaunchKernelGGL((reshape_and_cache_kv8_runs_kernel<IN, CODE, W>), rgrid, dim3(256), 0,     \
+                     stream, static_cast<const uint16_t*>(key),                                 \
+                     static_cast<const uint16_t*>(value), static_cast<uint8_t*>(key_cache),     \
+                     static_cast<uint8_t*>(value_cache), slot_mapping, num_tokens,              \
+                     num_kv_heads, head_size, block_size, num_blocks, key_stride,               \
+                     value_stride, k_scale, v_scale)
+    if (vec_rows) {
+      if (dtype == 1) PKV_RUNS8(F16, true); else PKV_RUNS8(BF16, true);
+    } else {
+      if (dtype == 1) PKV_RUNS8(F16, false); else PKV_RUNS8(BF16, false);
+    }
 #undef PKV_RUNS8
     return hipGetLastError();
   }
