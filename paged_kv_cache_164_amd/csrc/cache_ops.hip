@@ -30,12 +30,14 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 // The same scatter for many tokens (a prefill chunk), 16-bit elements: one workgroup per run
-// of 16 consecutive tokens.  A thread holds one (head, dim) value element of 8 tokens
-// (loads coalesced across the threads), and 8 tokens whose slots are consecutive, 8-aligned
-// and inside one block -- the usual case for a chunk, whose tokens fill blocks in order -- land
-// as one 16-byte store of the value row instead of eight 2-byte ones.  Other runs fall back to
-// element stores; keys are 16-byte chunks either way (token index fastest across threads, so a
-// block's consecutive tokens are written as one contiguous run).
+// of 16 consecutive tokens.  A thread holds one (head, dim) value element of 8 tokens, and 8
+// tokens whose slots are consecutive, 8-aligned and inside one block -- the usual case for a
+// chunk, whose tokens fill blocks in order -- land as one 16-byte store of the value row
+// instead of eight 2-byte ones.  Other runs fall back to element stores.  With 16-byte aligned
+// value rows (VEC_VAL) the run's values come in through LDS with 16-byte loads and are read
+// back transposed; otherwise each thread loads its 8 elements one by one.  Keys are 16-byte
+// chunks either way (token index fastest across threads, so a block's consecutive tokens are
+// written as one contiguous run).
 constexpr int kRunTokens = 16;
 constexpr int kRunMinTokens = 512;  // below it, one workgroup per token spreads the work wider
 
@@ -160,7 +162,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 // The 8-bit write for many tokens: 16 tokens per workgroup, as reshape_and_cache_runs_kernel.
 // A run of 8 consecutive tokens landing in 8 consecutive, 8-aligned slots of one block writes
 // its codes of a value row as one 8-byte store; other runs fall back to byte stores.  Keys are
-// 16-byte chunks (16 codes) either way.
+// 16-byte chunks (16 codes) either way.  With 16-byte aligned key and value rows (VEC) the new
+// elements come in with 16-byte loads (values through LDS, as in the 16-bit run kernel).
 // VEC: key and value rows 16-byte aligned (16-byte loads of the new elements).
 template <class IN, int CODE, bool VEC>
 __global__ __launch_bounds__(256) void reshape_and_cache_kv8_runs_kernel(

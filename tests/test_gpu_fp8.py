@@ -129,11 +129,14 @@ def test_kv8_run_to_run_bit_determinism(code):
 
 
 @pytest.mark.parametrize("code", CODES)
-@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 8), ("bf16", 32)])
-def test_reshape_and_cache_kv8_many_tokens(dtype, bs, code):
+@pytest.mark.parametrize("dtype,bs,stride_pad", [("bf16", 16, 0), ("f16", 8, 0), ("bf16", 32, 0),
+                                                 ("bf16", 16, 3)])
+def test_reshape_and_cache_kv8_many_tokens(dtype, bs, stride_pad, code):
     """A prefill-sized batch (the 8-bit many-token path): runs of consecutive slots filling
     blocks, runs starting mid-block, a run with a hole, skipped (-1) and out-of-range slots,
-    random singles, and a ragged tail; compared byte for byte with the oracle's write."""
+    random singles, and a ragged tail; compared byte for byte with the oracle's write.  With
+    stride_pad the token rows are strided by a count that is not a multiple of 8 elements (a
+    fused buffer), so the rows are not 16-byte aligned."""
     case = with_8bit_cache(make_decode_case("c3", num_seqs=8, len_cap=1500, dtype=dtype,
                                             block_size=bs, pool=("plus", 160)), code)
     Hkv, D = case.key_cache.shape[1], case.query.shape[2]
@@ -158,11 +161,15 @@ def test_reshape_and_cache_kv8_many_tokens(dtype, bs, code):
     slots = np.array(slots, dtype=np.int64)
     N = len(slots)
     assert N >= 512 and N % 16 != 0
-    key = draw_normal((N, Hkv, D), dtype, 79, 0) * 3
-    val = draw_normal((N, Hkv, D), dtype, 79, 1) * 3
-    log(f"reshape {code} many tokens {dtype} bs{bs} N={N}")
+    row = Hkv * D + stride_pad
+    kbuf = draw_normal((N, row), dtype, 79, 0) * 3
+    vbuf = draw_normal((N, row), dtype, 79, 1) * 3
+    key, val = kbuf[:, :Hkv * D].reshape(N, Hkv, D), vbuf[:, :Hkv * D].reshape(N, Hkv, D)
+    log(f"reshape {code} many tokens {dtype} bs{bs} N={N} row stride {row}")
     kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
-    pkv.reshape_and_cache_fp8(key.to(DEV), val.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV),
+    kd = kbuf.to(DEV)[:, :Hkv * D].view(N, Hkv, D)
+    vd = vbuf.to(DEV)[:, :Hkv * D].view(N, Hkv, D)
+    pkv.reshape_and_cache_fp8(kd, vd, kc, vc, torch.from_numpy(slots).to(DEV),
                               case.k_scale, case.v_scale, code=code)
     torch.cuda.synchronize()
     kb, vb = case.key_cache.numpy().copy(), case.value_cache.numpy().copy()
