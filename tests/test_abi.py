@@ -271,3 +271,45 @@ def test_kv8_cache_write_argument_errors(entry):
     assert f(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 128, 2, 0.0, 0.03, None) == -1    # scale 0
     assert f(1, 1, 1, 1, 1, 4, 2, 64, 16, 10, 128, 100, 2, 0.02, 0.03, None) == -1   # stride
     assert f(None, None, None, None, None, 0, 2, 64, 16, 10, 128, 128, 2, 0.02, 0.03, None) == 0
+
+
+def _plan_and_cache(lib, fmt="", **over):
+    """The fused plan + cache-write entries; fmt '' (16-bit), 'fp8', 'int8' or 'shared'."""
+    args = dict(out=1, query=1, key_cache=1, value_cache=1, block_tables=1, context_lens=1)
+    if fmt == "shared":
+        args.update(group_starts=1, prefix_lens=1, num_groups=1)
+    args.update(scale=0.125)
+    if fmt in ("fp8", "int8"):
+        args.update(k_scale=0.02, v_scale=0.03)
+    args.update(num_seqs=0, num_heads=8, num_kv_heads=2, head_size=128, block_size=16,
+                max_blocks=4, max_context_len=64, dtype=2, partition_size=0, workspace=None,
+                ws_bytes=0, key=1, value=1, slot_mapping=1, num_tokens=0, num_blocks=10,
+                key_stride=256, value_stride=256, stream=None)
+    args.update(over)
+    name = "pkv_paged_attention_plan_and_cache" + (f"_{fmt}" if fmt else "")
+    return getattr(lib, name)(*args.values())
+
+
+@pytest.mark.parametrize("fmt", ["", "fp8", "int8", "shared"])
+def test_plan_and_cache_argument_errors(fmt):
+    """Every fused plan + cache-write entry validates both halves on the host and enqueues
+    nothing on error; with no sequences and no tokens it has nothing to do."""
+    lib = _lib()
+    assert _plan_and_cache(lib, fmt) == 0
+    for over, code in [(dict(num_tokens=-1), -1),
+                       (dict(num_blocks=-5), -1),
+                       (dict(num_tokens=3, key_stride=100), -1),   # stride < Hkv * D
+                       (dict(num_tokens=3, key=None), -3),
+                       (dict(num_tokens=3, slot_mapping=None), -3),
+                       (dict(head_size=96), -2),
+                       (dict(num_seqs=2), -4)]:                    # the plan needs a workspace
+        if fmt == "shared" and over.get("num_seqs") == 2:
+            over = dict(over, num_groups=1)
+        assert _plan_and_cache(lib, fmt, **over) == code, (fmt, over)
+        assert lib.pkv_last_error().decode() != ""
+    if fmt in ("fp8", "int8"):
+        assert _plan_and_cache(lib, fmt, k_scale=0.0) == -1
+        assert _plan_and_cache(lib, fmt, dtype=0) == -2           # 16-bit queries only
+    if fmt == "shared":
+        assert _plan_and_cache(lib, fmt, num_seqs=2, num_groups=3) == -1
+        assert _plan_and_cache(lib, fmt, num_seqs=2, group_starts=None) == -3
