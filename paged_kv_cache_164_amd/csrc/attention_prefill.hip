@@ -184,8 +184,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // stage s (values read), s + 1 (keys read), s + 2 (being written)
   constexpr int NBUF = 3;
   // register sets of stage copies in flight: a stage is loaded R steps before it is stored.
-  // Three (loads about 3 us ahead of their use at c6's pace; deeper measured no faster), a
-  // multiple of NBUF, so that the buffer of every step of the unrolled loop is a constant.
+  // Three (on a 16-request chunked-prefill step the loads then run about 3 us ahead of their
+  // use; deeper measured no faster), a multiple of NBUF, so that the buffer of every step of
+  // the unrolled loop is a constant.
   constexpr int R = 3;
   static_assert(R >= 2 && R % NBUF == 0, "stages 0 and 1 are staged through two sets");
   __shared__ __align__(16) char s_k[NBUF][KSTAGE];
@@ -238,7 +239,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int kc = 0; kc < KC; ++kc) qop[cb][kc] = qv[kc * 4 + quad];
   }
   const int qi_first = (w * CB * 16) / G;
-  const int qi_last = min((w * CB * 16 + CB * 16 - 1) / G, nqt - 1);
   const bool active = qi_first < nqt;                       // the wave has a real column
   const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
 
@@ -247,9 +247,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
 
-  // Stage s's keys and values go from HBM to registers two stages ahead of their use and from
-  // registers to LDS one stage ahead.  Loads are never skipped (a stage past the end reloads
-  // the last one, from L2): a load under a branch would make every wait conservative.
+  // Stage s's keys and values go from HBM to registers R steps before step s - 2 stores them to
+  // LDS (its keys are read in step s - 1, its values in step s).  Loads are never skipped (a
+  // stage past the end reloads the last one, from L2): a load under a branch would make every
+  // wait conservative.
   // Per-thread constants of the copies (a stage starts at a multiple of 32 >= k0, which is
   // itself a multiple of 32, so a thread's pieces sit at fixed offsets inside their blocks):
   //   key piece: dims 8 c8 .. +8 of stage token tok

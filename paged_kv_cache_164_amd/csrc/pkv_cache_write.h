@@ -40,8 +40,8 @@ __device__ __forceinline__ void cache_write_token(
     const int nc = n / X, cph = D / X;
     const uint4* k4 = reinterpret_cast<const uint4*>(krow);
     const uint4* v4 = reinterpret_cast<const uint4*>(vrow);
-    // the first two chunks per thread (all of a row up to 512 chunks) without a branch: indices
-    // past the row are clamped to its last chunk and their values dropped
+    // the first two chunks per thread (a whole row of up to 2 blockDim.x chunks) without a
+    // branch: indices past the row are clamped to its last chunk and their values dropped
     const int c0 = threadIdx.x, c1 = c0 + blockDim.x;
     const int l0 = min(c0, nc - 1), l1 = min(c1, nc - 1);
     const uint4 ka = k4[l0], va = v4[l0], kb = k4[l1], vb = v4[l1];

@@ -141,3 +141,64 @@ def test_8bit_decode_and_multi_query_graph_replays(code):
                                     v_scale=pcase.v_scale, code=code)
 
     _check_replays(pstep, pout)
+
+
+@pytest.mark.parametrize("kind", ["16-bit", "e4m3", "i8", "beam"])
+def test_fused_plan_and_cache_steps_graph_replays(kind):
+    """The steps bench.py times, captured as one graph: the fused plan + cache-write launch
+    (16-bit, 8-bit, or shared-prefix after a beam step's copy-on-write), the planned kernel and
+    the reduce.  Replays must equal the eager step bit for bit."""
+    from workloads import make_beam_case, with_8bit_cache
+    if kind == "beam":
+        from test_gpu_beam import _cow_step
+        bc = make_beam_case(num_prompts=8)
+        B = bc.query.shape[0]
+        tables, lens, pairs, mapping, slots, nk, nv, _ = _cow_step(bc)
+        q, kc, vc = bc.query.to(DEV), bc.key_cache.to(DEV), bc.value_cache.to(DEV)
+        bt, cl = torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV)
+        gs = torch.arange(0, B + 1, bc.beams, dtype=torch.int32, device=DEV)
+        pl = torch.full((B // bc.beams,), bc.prompt_len, dtype=torch.int32, device=DEV)
+        mp, sl = torch.from_numpy(mapping).to(DEV), torch.from_numpy(slots).to(DEV)
+        nkd, nvd = nk.to(DEV), nv.to(DEV)
+        L, scale = int(lens.max()), bc.scale
+        ptrs = pkv.copy_blocks([kc], [vc], mp)  # device pointer tables made outside the capture
+        H, D = q.shape[1], q.shape[2]
+        ws = torch.empty(pkv.paged_attention_workspace_size(B, H, D, L), dtype=torch.uint8,
+                         device=DEV)
+        log(f"graph fused beam step: {B} sequences, {len(pairs)} copy-on-write pairs")
+
+        def step():
+            pkv.copy_blocks([kc], [vc], mp, _ptr_buffers=ptrs)
+            pkv.paged_attention_plan_and_cache_shared(out, q, kc, vc, bt, cl, gs, pl, scale, L,
+                                                      nkd, nvd, sl, 0, ws)
+            pkv.paged_attention_partitions_planned_shared(out, q, kc, vc, bt, cl, gs, pl, scale,
+                                                          L, 0, ws)
+            pkv.paged_attention_reduce(out, cl, L, ws, 0)
+    else:
+        case = make_decode_case("c3", num_seqs=40, len_cap=6000)
+        if kind != "16-bit":
+            case = with_8bit_cache(case, kind)
+        q, kc, vc = case.query.to(DEV), case.key_cache.to(DEV), case.value_cache.to(DEV)
+        bt, cl = case.block_tables.to(DEV), case.context_lens.to(DEV)
+        nk, nv, sl = case.new_key.to(DEV), case.new_value.to(DEV), case.slot_mapping.to(DEV)
+        L = case.max_context_len
+        ws = torch.empty(pkv.paged_attention_workspace_size(case.num_seqs, 32, 128, L),
+                         dtype=torch.uint8, device=DEV)
+        log(f"graph fused {kind} step: {case.num_seqs} sequences")
+
+        def step():
+            if kind == "16-bit":
+                pkv.paged_attention_plan_and_cache(out, q, kc, vc, bt, cl, case.scale, L, nk, nv,
+                                                   sl, 0, ws)
+                pkv.paged_attention_partitions_planned(out, q, kc, vc, bt, cl, case.scale, L, 0,
+                                                       ws)
+            else:
+                pkv.paged_attention_plan_and_cache_fp8(out, q, kc, vc, bt, cl, case.scale,
+                                                       case.k_scale, case.v_scale, L, nk, nv, sl,
+                                                       0, ws, code=kind)
+                pkv.paged_attention_partitions_planned_fp8(out, q, kc, vc, bt, cl, case.scale,
+                                                           case.k_scale, case.v_scale, L, 0, ws,
+                                                           code=kind)
+            pkv.paged_attention_reduce(out, cl, L, ws, 0)
+    out = torch.empty_like(q)
+    _check_replays(step, out)
