@@ -268,3 +268,38 @@ def test_reshape_and_cache_block_size_not_power_of_two(kind, N):
         OC.reshape_and_cache(kb, vb, storage_bits(key), storage_bits(val), ref_slots)
     torch.cuda.synchronize()
     assert _bits_equal(kcd, kb) and _bits_equal(vcd, vb)
+
+
+@pytest.mark.parametrize("kind", ["16-bit", "e4m3", "shared"])
+def test_fused_plan_and_cache_with_no_sequences_only_writes(kind):
+    """A fused plan + cache-write call with no sequences to plan (num_seqs 0) still writes the new
+    tokens: the caches end as after reshape_and_cache (or its 8-bit form) alone."""
+    from workloads import with_8bit_cache
+    case = make_decode_case("c3", num_seqs=6, len_cap=300)
+    if kind == "e4m3":
+        case = with_8bit_cache(case, "e4m3")
+    q0 = case.query[:0].to(DEV)
+    out0 = torch.empty_like(q0)
+    bt0 = case.block_tables[:0].to(DEV)
+    cl0 = case.context_lens[:0].to(DEV)
+    nk, nv, sl = case.new_key.to(DEV), case.new_value.to(DEV), case.slot_mapping.to(DEV)
+    ref_k, ref_v = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    log(f"fused call, no sequences, {nk.shape[0]} tokens: {kind}")
+    if kind == "e4m3":
+        pkv.reshape_and_cache_fp8(nk, nv, ref_k, ref_v, sl, case.k_scale, case.v_scale)
+        pkv.paged_attention_plan_and_cache_fp8(out0, q0, kc, vc, bt0, cl0, case.scale,
+                                               case.k_scale, case.v_scale, 0, nk, nv, sl)
+    else:
+        pkv.reshape_and_cache(nk, nv, ref_k, ref_v, sl)
+        if kind == "shared":
+            gs = torch.zeros(1, dtype=torch.int32, device=DEV)
+            pl = torch.zeros(0, dtype=torch.int32, device=DEV)
+            pkv.paged_attention_plan_and_cache_shared(out0, q0, kc, vc, bt0, cl0, gs, pl,
+                                                      case.scale, 0, nk, nv, sl)
+        else:
+            pkv.paged_attention_plan_and_cache(out0, q0, kc, vc, bt0, cl0, case.scale, 0, nk, nv,
+                                               sl)
+    torch.cuda.synchronize()
+    iv = torch.uint8 if kind == "e4m3" else torch.int16
+    assert torch.equal(kc.view(iv), ref_k.view(iv)) and torch.equal(vc.view(iv), ref_v.view(iv))
