@@ -16,9 +16,9 @@
 // part of a sequence there).
 //
 // Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
-// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (three stage buffers;
-// the loads run two stages ahead), and every wave reads them from there: the stage is fetched
-// once for all 256 columns.  A wave computes the logits of the next stage while its VALU
+// cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (six stage buffers, a
+// stage stored three steps before its values are read, one barrier per two stages), and every
+// wave reads them from there: the stage is fetched once for all 256 columns.  A wave computes the logits of the next stage while its VALU
 // turns the current stage's logits into weights.
 //   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
 //           rows, 16 columns per product), the 32 tokens stored in the row order
@@ -181,14 +181,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int VSTAGE = D * VRS;
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
-  // stage s (values read), s + 1 (keys read), s + 2 (being written)
-  constexpr int NBUF = 3;
+  // Step s reads the values of stage s and the keys of stage s + 1 and stores stage s + AHEAD;
+  // a barrier follows every odd step.  Six buffers make that one barrier per two steps enough:
+  // the keys of stage s + 1 were stored in step s + 1 - AHEAD <= s - 2, before the barrier that
+  // ends step s - 1 or s - 2, and the buffer step s overwrites held stage s + AHEAD - NBUF,
+  // whose values were last read in step s - 3, also before one of those barriers.
+  constexpr int NBUF = 6;
+  constexpr int AHEAD = 3;
   // register sets of stage copies in flight: a stage is loaded R steps before it is stored.
   // Three (on a 16-request chunked-prefill step the loads then run about 3 us ahead of their
-  // use; deeper measured no faster), a multiple of NBUF, so that the buffer of every step of
-  // the unrolled loop is a constant.
+  // use; deeper measured no faster).
   constexpr int R = 3;
-  static_assert(R >= 2 && R % NBUF == 0, "stages 0 and 1 are staged through two sets");
+  // the loop is unrolled by U steps, so that every buffer, register set and logit set index in
+  // it is a constant
+  constexpr int U = 6;
+  static_assert(U % NBUF == 0 && U % R == 0 && U % 2 == 0, "constant indices in the loop");
+  static_assert(R == AHEAD, "the prologue stores stages 0 .. AHEAD - 1 from the R sets");
   __shared__ __align__(16) char s_k[NBUF][KSTAGE];
   __shared__ __align__(16) char s_v[NBUF][VSTAGE];
   __shared__ int s_ids[kPrefillMaxIds];
@@ -243,12 +251,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
 
   const int64_t tile_bytes = (int64_t)D * BS * (KV8 ? 1 : 2);  // one (block, KV head) tile
-  const int64_t block_bytes = tile_bytes * Hkv;
+  const uint32_t block_bytes = uint32_t(tile_bytes * Hkv);      // below 4 GiB (host check)
   const char* kbase = static_cast<const char*>(a.key_cache) + kh * tile_bytes;
   const char* vbase = static_cast<const char*>(a.value_cache) + kh * tile_bytes;
 
-  // Stage s's keys and values go from HBM to registers R steps before step s - 2 stores them to
-  // LDS (its keys are read in step s - 1, its values in step s).  Loads are never skipped (a
+  // Stage s's keys and values go from HBM to registers R steps before step s - AHEAD stores them
+  // to LDS (its keys are read in step s - 1, its values in step s).  Loads are never skipped (a
   // stage past the end reloads the last one, from L2): a load under a branch would make every
   // wait conservative.
   // Per-thread constants of the copies (a stage starts at a multiple of 32 >= k0, which is
@@ -331,9 +339,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float m_run[CB];
+  // running maximum per column (base-2 units) and the lazy test's threshold m_run + margin
+  float m_run[CB], m_thr[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) m_run[cb] = -INFINITY;
+  for (int cb = 0; cb < CB; ++cb) m_run[cb] = m_thr[cb] = -INFINITY;
   // A operand of the row-sum product: row 0 all ones (lanes with col == 0), other rows zero
   const uint32_t ob = (col == 0) ? one_bits(DT()) : 0u;
   const uint4 ones = make_uint4(ob, ob, ob, ob);
@@ -382,14 +391,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   auto rescale = [&](const float (&lm)[CB]) {
     bool any = false;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] * sl2 > m_run[cb] + kLazyRescale;
+    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] * sl2 > m_thr[cb];
     if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float mc = column_max(lm[cb]) * sl2;
-        const float m_new = mc > m_run[cb] + kLazyRescale ? mc : m_run[cb];
+        const float m_new = mc > m_thr[cb] ? mc : m_run[cb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 at first (m = -inf)
         m_run[cb] = m_new;
+        m_thr[cb] = m_new + kLazyRescale;
         lacc[cb] *= alpha;
 #pragma unroll
         for (int i = 0; i < NDT; ++i) oacc[i][cb] *= alpha;
@@ -421,66 +431,64 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // Stages past a wave's last column are computed too: their keys are all masked (zero
   // weights).  The logits of stage nst, past the end, come from a block holding a copy of the
   // last stage and are never used.
-  f32x4 S[2][CB];
-  auto step = [&](int s) {
-    if (needs_mask(s)) mask_stage(k0 + 32 * s, S);
+  // logits: set x holds those of the stages of parity x (the unrolled loop picks constants)
+  f32x4 S[2][2][CB];
+  // step s with s mod U = u (a multiple of U is a multiple of NBUF, R and 2)
+  auto step = [&](int s, int u) {
+    f32x4 (&Sc)[2][CB] = S[u & 1];
+    if (needs_mask(s)) mask_stage(k0 + 32 * s, Sc);
     float lm[CB];
-    stage_max(S, lm);
+    stage_max(Sc, lm);
     rescale(lm);  // before the stage's weights and its P.V
     uint4 vop[NDT];
-    const char* sv = s_v[s % NBUF];
+    const char* sv = s_v[u % NBUF];
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
       vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
-    f32x4 Sn[2][CB];
-    qk((s + 1) % NBUF, Sn);
+    qk((u + 1) % NBUF, S[(u + 1) & 1]);
     uint4 pop[CB];
-    weights(S, pop);
+    weights(Sc, pop);
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) S[tt][cb] = Sn[tt][cb];
+  };
+  // Step s (s mod U = u): store stage s + AHEAD from its register set, loaded R steps before,
+  // and load stage s + AHEAD + R into that set; then the step's attention work; a barrier after
+  // odd steps.  Stores and loads are not skipped past the end (loads of stages past the last
+  // reload it; the buffers they fill are free, and unread after the loop but for stage nst's
+  // discarded logits).
+  auto copy_and_step = [&](int s, int u) {
+    const int set = u % R;
+    store_stage((u + AHEAD) % NBUF, s + AHEAD, kR[set], vR[set]);
+    load_stage(s + AHEAD + R, kR[set], vR[set]);
+    if (active) step(s, u);
+    if (u & 1) __syncthreads();
   };
 
   __syncthreads();  // s_ids
-  load_stage(0, kR[0], vR[0]);
-  load_stage(1, kR[1], vR[1]);
-  store_stage(0, 0, kR[0], vR[0]);
-  store_stage(1, 1, kR[1], vR[1]);
 #pragma unroll
-  for (int u = 2; u < R + 2; ++u) load_stage(u, kR[u % R], vR[u % R]);
-  __syncthreads();
-  if (active) qk(0, S);
-
-  // Steps in groups of R: the only way back to the loop head is the end of a group, so the
-  // wait counters there know exactly which loads are in flight.  Step s stores stage s + 2 to
-  // LDS from its register set, loaded R steps before, and loads stage s + 2 + R into it;
-  // stores and loads are not skipped past the end (the blocks they fill are free, and unread
-  // after the loop but for stage nst's discarded logits).
-  int s = 0;
-  for (; s + R - 1 < nst; s += R) {
+  for (int u = 0; u < R; ++u) load_stage(u, kR[u], vR[u]);
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int set = (u + 2) % R;
-      store_stage((s + u + 2) % NBUF, s + u + 2, kR[set], vR[set]);
-      load_stage(s + u + 2 + R, kR[set], vR[set]);
-      if (active) step(s + u);
-      __syncthreads();
-    }
+  for (int u = 0; u < AHEAD; ++u) {
+    store_stage(u, u, kR[u], vR[u]);
+    load_stage(u + AHEAD, kR[u], vR[u]);
   }
-  // fewer than R stages left: stage s + u + 1 is in LDS before step s + u, s + u + 2 in its
-  // register set
+  __syncthreads();
+  if (active) qk(0, S[0]);
+
+  // Steps in groups of U: the only way back to the loop head is the end of a group, so the
+  // wait counters there know exactly which loads are in flight, and s is a multiple of U at
+  // every step of the group (its buffer, set and parity are those of u).
+  int s = 0;
+  for (; s + U - 1 < nst; s += U) {
 #pragma unroll
-  for (int u = 0; u < R - 1; ++u) {
+    for (int u = 0; u < U; ++u) copy_and_step(s + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < U - 1; ++u) {
     if (s + u >= nst) break;
-    const int set = (u + 2) % R;
-    store_stage((s + u + 2) % NBUF, s + u + 2, kR[set], vR[set]);
-    if (active) step(s + u);
-    __syncthreads();
+    copy_and_step(s + u, u);
   }
   if (!active) return;
 

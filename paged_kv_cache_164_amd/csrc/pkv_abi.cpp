@@ -248,6 +248,8 @@ static int prefill_call(void* out, const void* query, const void* key_cache,
     if (!pkv::prefill_supported(dtype, head_size, block_size, group))
       return fail(PKV_ERR_UNSUPPORTED,
                   "head_size must be 64 or 128, block_size 8, 16 or 32, num_heads/num_kv_heads <= 16");
+    if ((int64_t)head_size * block_size * 2 * num_kv_heads >= (int64_t(1) << 32))
+      return fail(PKV_ERR_UNSUPPORTED, "a cache block (all KV heads) must be below 4 GiB");
     const int P = prefill_partition(partition_size);
     if (P < 0)
       return fail(PKV_ERR_INVALID_ARG, "partition_size must be 0 or a multiple of 32 in [32, 8192]");
