@@ -218,6 +218,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int slot = k0 / P;
   const int nst = (k1 - k0 + 31) / 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int w_uniform = __builtin_amdgcn_readfirstlane(w);
   const int col = lane & 15, quad = lane >> 4;
 
   if (a.slots > 1 && slot == 0 && kh == 0)  // read by the reduce, which runs after this kernel
@@ -350,18 +351,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   // ---- the pieces of a stage's work (LDS buffer buf holds the stage)
   // S^T = K Q^T: 2 key tiles x CB column blocks, KC products each
-  auto qk = [&](int buf, f32x4 (&S)[2][CB]) {
+  auto qk_read = [&](int buf, uint4 (&ka)[KC][2]) {
     const char* sk = s_k[buf];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        ka[kc][tt] = *reinterpret_cast<const uint4*>(sk + ((kc * 4 + quad) * 32 + tt * 16 + col) * 16);
+  };
+  auto qk_mma = [&](const uint4 (&ka)[KC][2], f32x4 (&S)[2][CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) S[0][cb] = S[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(sk + ((kc * 4 + quad) * 32 + tt * 16 + col) * 16);
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) S[tt][cb] = mma(DT(), ka, qop[cb][kc], S[tt][cb]);
-      }
+        for (int cb = 0; cb < CB; ++cb) S[tt][cb] = mma(DT(), ka[kc][tt], qop[cb][kc], S[tt][cb]);
+  };
+  auto qk = [&](int buf, f32x4 (&S)[2][CB]) {
+    uint4 ka[KC][2];
+    qk_read(buf, ka);
+    qk_mma(ka, S);
   };
   // per column and lane: the largest of the lane's 8 logits of the stage (raw units)
   auto stage_max = [&](const f32x4 (&S)[2][CB], float (&mc)[CB]) {
@@ -433,37 +444,63 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // last stage and are never used.
   // logits: set x holds those of the stages of parity x (the unrolled loop picks constants)
   f32x4 S[2][2][CB];
-  // step s with s mod U = u (a multiple of U is a multiple of NBUF, R and 2)
-  auto step = [&](int s, int u) {
+  // step s with s mod U = u (a multiple of U is a multiple of NBUF, R and 2), in two parts.
+  // Part a: the LDS reads of stage s + 1's keys and stage s's values (vop), the mask and lazy
+  // maximum of stage s, the logit products of stage s + 1 and the weights of stage s (pop),
+  // issued so that each logit product is followed by two VALU instructions of the weights and
+  // every second one by a value read.
+  auto step_a = [&](int s, int u, uint4 (&vop)[NDT], uint4 (&pop)[CB]) {
     f32x4 (&Sc)[2][CB] = S[u & 1];
+    uint4 ka[KC][2];
+    qk_read((u + 1) % NBUF, ka);  // in flight while the VALU tests the stage's maximum
     if (needs_mask(s)) mask_stage(k0 + 32 * s, Sc);
     float lm[CB];
     stage_max(Sc, lm);
     rescale(lm);  // before the stage's weights and its P.V
-    uint4 vop[NDT];
     const char* sv = s_v[u % NBUF];
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
       vop[i] = *reinterpret_cast<const uint4*>(sv + (i * 16 + col) * VRS + quad * 16);
-    qk((u + 1) % NBUF, S[(u + 1) & 1]);
-    uint4 pop[CB];
+    qk_mma(ka, S[(u + 1) & 1]);
     weights(Sc, pop);
+#pragma unroll
+    for (int g = 0; g < 2 * KC * CB; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+      if (g % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+  };
+  // Part b: the P.V products of stage s, from registers only, issued at raised wave priority so
+  // that the SIMD's arbiter keeps feeding the matrix core from this wave while the other wave
+  // on the SIMD runs its VALU and memory work.
+  auto step_b = [&](const uint4 (&vop)[NDT], const uint4 (&pop)[CB]) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Step s (s mod U = u): store stage s + AHEAD from its register set, loaded R steps before,
   // and load stage s + AHEAD + R into that set; then the step's attention work; a barrier after
   // odd steps.  Stores and loads are not skipped past the end (loads of stages past the last
   // reload it; the buffers they fill are free, and unread after the loop but for stage nst's
   // discarded logits).
+  // Waves w and w + NW/2 share a SIMD.  The later half of the waves meets the barrier of an
+  // odd step before its part b, the earlier half after it, so the two waves of a SIMD run half
+  // a step apart: one issues its P.V products while the other copies and forms weights.  Both
+  // halves touch the same LDS data between two barriers (part b reads none), so the buffer
+  // reasoning above holds for either.
+  const bool late = w_uniform >= NW / 2;
   auto copy_and_step = [&](int s, int u) {
     const int set = u % R;
     store_stage((u + AHEAD) % NBUF, s + AHEAD, kR[set], vR[set]);
     load_stage(s + AHEAD + R, kR[set], vR[set]);
-    if (active) step(s, u);
-    if (u & 1) __syncthreads();
+    uint4 vop[NDT], pop[CB];
+    if (active) step_a(s, u, vop, pop);
+    if ((u & 1) && late) __syncthreads();
+    if (active) step_b(vop, pop);
+    if ((u & 1) && !late) __syncthreads();
   };
 
   __syncthreads();  // s_ids
