@@ -17,9 +17,11 @@
 //
 // Per 32-key stage the workgroup copies the keys and values of its KV head from the paged
 // cache (the block layout of the "Vllm" page, "CacheEngine") into LDS (six stage buffers, a
-// stage stored three steps before its values are read, one barrier per two stages), and every
-// wave reads them from there: the stage is fetched once for all 256 columns.  A wave computes the logits of the next stage while its VALU
-// turns the current stage's logits into weights.
+// stage stored four steps before its values are read, one barrier per two stages), and every
+// wave reads them from there: the stage is fetched once for all 256 columns.  A wave computes
+// the logits of the next stage while its VALU turns the current stage's logits into weights,
+// and copies a later stage while its matrix core multiplies the weights by the values; the two
+// waves of a SIMD run half a step apart.
 //   keys:   LDS [D/8][32][8], the A operand of S^T = K Q^T (v_mfma_f32_16x16x32, tokens on
 //           rows, 16 columns per product), the 32 tokens stored in the row order
 //           (8q..8q+3 for q = 0..3, then 8q+4..8q+7), so that lane quad q of the two 16x16
@@ -74,6 +76,16 @@ __device__ __forceinline__ uint4 mask8(uint4 v, int base, int limit) {
     return ((base + e < limit) ? 0x0000ffffu : 0u) | ((base + e + 1 < limit) ? 0xffff0000u : 0u);
   };
   return make_uint4(v.x & m(0), v.y & m(2), v.z & m(4), v.w & m(6));
+}
+// The same for an 8-token piece of 8-bit codes (a zero code is the value 0 in both formats).
+__device__ __forceinline__ uint2 mask8(uint2 v, int base, int limit) {
+  auto m = [&](int e) -> uint32_t {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r |= (base + e + k < limit) ? (0xffu << (8 * k)) : 0u;
+    return r;
+  };
+  return make_uint2(v.x & m(0), v.y & m(4));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -182,12 +194,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
   // Step s reads the values of stage s and the keys of stage s + 1 and stores stage s + AHEAD;
-  // a barrier follows every odd step.  Six buffers make that one barrier per two steps enough:
-  // the keys of stage s + 1 were stored in step s + 1 - AHEAD <= s - 2, before the barrier that
-  // ends step s - 1 or s - 2, and the buffer step s overwrites held stage s + AHEAD - NBUF,
-  // whose values were last read in step s - 3, also before one of those barriers.
+  // a barrier follows every odd step.  Six buffers make one barrier per two steps enough (the
+  // step loop below gives the reasoning).
   constexpr int NBUF = 6;
-  constexpr int AHEAD = 3;
+  constexpr int AHEAD = 4;
   // register sets of stage copies in flight: a stage is loaded R steps before it is stored.
   // Three (on a 16-request chunked-prefill step the loads then run about 3 us ahead of their
   // use; deeper measured no faster).
@@ -196,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // it is a constant
   constexpr int U = 6;
   static_assert(U % NBUF == 0 && U % R == 0 && U % 2 == 0, "constant indices in the loop");
-  static_assert(R == AHEAD, "the prologue stores stages 0 .. AHEAD - 1 from the R sets");
+  static_assert(AHEAD >= R, "the prologue stores stages 0 .. AHEAD - 1 through the R sets");
   __shared__ __align__(16) char s_k[NBUF][KSTAGE];
   __shared__ __align__(16) char s_v[NBUF][VSTAGE];
   __shared__ int s_ids[kPrefillMaxIds];
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) qop[cb][kc] = qv[kc * 4 + quad];
   }
-  const int qi_first = (w * CB * 16) / G;
+  const int qi_first = (w_uniform * CB * 16) / G;  // wave-uniform, in a scalar register
   const bool active = qi_first < nqt;                       // the wave has a real column
   const int wave_full = min(k1, qpos0 + qi_first + 1);      // keys before it: seen by all
 
@@ -377,9 +387,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // per column and lane: the largest of the lane's 8 logits of the stage (raw units)
   auto stage_max = [&](const f32x4 (&S)[2][CB], float (&mc)[CB]) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      mc[cb] = fmaxf(fmaxf(fmaxf(S[0][cb][0], S[0][cb][1]), fmaxf(S[0][cb][2], S[0][cb][3])),
-                     fmaxf(fmaxf(S[1][cb][0], S[1][cb][1]), fmaxf(S[1][cb][2], S[1][cb][3])));
+    for (int cb = 0; cb < CB; ++cb) {
+      // a chain of three-input maxima (v_max3_f32): 4 instructions for 8 logits
+      float m = fmaxf(fmaxf(S[0][cb][0], S[0][cb][1]), S[0][cb][2]);
+      m = fmaxf(fmaxf(m, S[0][cb][3]), S[1][cb][0]);
+      m = fmaxf(fmaxf(m, S[1][cb][1]), S[1][cb][2]);
+      mc[cb] = fmaxf(m, S[1][cb][3]);
+    }
   };
   // keys a column must not see (causal, or past the item): logit -inf.  Element r of logit
   // tile tt of lane quad q is the key 8 q + 4 tt + r of the stage.
@@ -470,46 +484,83 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       if (g % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
   };
-  // Part b: the P.V products of stage s, from registers only, issued at raised wave priority so
-  // that the SIMD's arbiter keeps feeding the matrix core from this wave while the other wave
-  // on the SIMD runs its VALU and memory work.
-  auto step_b = [&](const uint4 (&vop)[NDT], const uint4 (&pop)[CB]) {
+  // Part b: the P.V products of stage s (an active wave's; from registers only) and the copy
+  // of stage s + AHEAD: its pieces stored to LDS from their register set, the next load into
+  // that set.  Issued at raised wave priority, so that the SIMD's arbiter keeps feeding the
+  // matrix core from this wave while the other wave on the SIMD forms weights, and interleaved
+  // by hand (the copy between groups of products) so that the copy's LDS and memory traffic
+  // runs in the products' shadow.  Every wave copies; only active waves multiply.
+  auto step_b = [&](int s, int u, const uint4 (&vop)[NDT], const uint4 (&pop)[CB]) {
+    static_assert(PPT == 1 && NDT % 4 == 0, "one piece per thread");
+    const int set = (u + AHEAD) % R, buf = (u + AHEAD) % NBUF;
+    auto pv = [&](int i0) {
+      if (active) {
+#pragma unroll
+        for (int i = i0; i < i0 + NDT / 4; ++i)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
+      }
+    };
+    const bool has = KPIECES % NT == 0 || tid < KPIECES;
+    int c8, krow, tok, d, t8;
+    key_piece(tid, c8, krow, tok);
+    value_piece(tid, d, t8);
     __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < NDT; ++i)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) oacc[i][cb] = mma(DT(), vop[i], pop[cb], oacc[i][cb]);
+    if (has) *reinterpret_cast<uint4*>(&s_k[buf][(c8 * 32 + krow) * 16]) = widen(kR[set][0]);
+    pv(0);
+    if (has) *reinterpret_cast<uint4*>(&s_v[buf][d * VRS + t8 * 2]) = widen(vR[set][0]);
+    pv(NDT / 4);
+    const int sid = min(s + AHEAD + R, nst - 1) * IDS_PER_STAGE;
+    uint32_t ik = 0, iv = 0;
+    if (has) {
+      ik = uint32_t(s_ids[sid + kid[0]]);
+      iv = uint32_t(s_ids[sid + vid[0]]);
+    }
+    pv(NDT / 2);
+    if (has) {
+      kR[set][0] = *reinterpret_cast<const Raw*>(kbase + (uint64_t)ik * block_bytes + koff[0]);
+      vR[set][0] = *reinterpret_cast<const Raw*>(vbase + (uint64_t)iv * block_bytes + voff[0]);
+    }
+    pv(3 * NDT / 4);
     __builtin_amdgcn_s_setprio(0);
   };
-  // Step s (s mod U = u): store stage s + AHEAD from its register set, loaded R steps before,
-  // and load stage s + AHEAD + R into that set; then the step's attention work; a barrier after
-  // odd steps.  Stores and loads are not skipped past the end (loads of stages past the last
-  // reload it; the buffers they fill are free, and unread after the loop but for stage nst's
-  // discarded logits).
-  // Waves w and w + NW/2 share a SIMD.  The later half of the waves meets the barrier of an
-  // odd step before its part b, the earlier half after it, so the two waves of a SIMD run half
-  // a step apart: one issues its P.V products while the other copies and forms weights.  Both
-  // halves touch the same LDS data between two barriers (part b reads none), so the buffer
-  // reasoning above holds for either.
+  // Values of the stage past the item's end zeroed in its register set before part b stores
+  // them (the last stage only: a wave-uniform branch).
+  auto mask_set = [&](int s, Raw* vst) {
+    int d, t8;
+    value_piece(tid, d, t8);
+    vst[0] = mask8(vst[0], k0 + 32 * s + t8, k1);
+  };
+  // Waves w and w + NW/2 share a SIMD.  The later half of the waves meets the barrier of an odd
+  // step between its parts a and b, the earlier half after part b, so the two waves of a SIMD
+  // run half a step apart: one issues its P.V products while the other forms weights.
+  // Buffers: stage X is stored in part b of step X - AHEAD; its keys are read in part a of step
+  // X - 1, its values in part a of step X; the buffer step s stores into last held stage
+  // s + AHEAD - NBUF = s - 2, whose values were read in part a of step s - 2.  Of steps X - 3
+  // and X - 2 one is odd, and its barrier lies after the store and before the keys' read for
+  // both halves of the waves; of steps s - 2 and s - 1 one is odd, and its barrier lies after
+  // that last read and before the store.
   const bool late = w_uniform >= NW / 2;
   auto copy_and_step = [&](int s, int u) {
-    const int set = u % R;
-    store_stage((u + AHEAD) % NBUF, s + AHEAD, kR[set], vR[set]);
-    load_stage(s + AHEAD + R, kR[set], vR[set]);
+    if (k0 + 32 * (s + AHEAD + 1) > k1) mask_set(s + AHEAD, vR[(u + AHEAD) % R]);
     uint4 vop[NDT], pop[CB];
     if (active) step_a(s, u, vop, pop);
     if ((u & 1) && late) __syncthreads();
-    if (active) step_b(vop, pop);
+    step_b(s, u, vop, pop);
     if ((u & 1) && !late) __syncthreads();
   };
 
+  // Prologue: stages 0 .. AHEAD - 1 stored, stages AHEAD .. AHEAD + R - 1 in their register sets
+  // (stage X in set X mod R).  Stores and loads are not skipped past the end (loads of stages
+  // past the last reload it; the buffers they fill are free, and unread after the loop but for
+  // stage nst's discarded logits).
   __syncthreads();  // s_ids
 #pragma unroll
   for (int u = 0; u < R; ++u) load_stage(u, kR[u], vR[u]);
 #pragma unroll
   for (int u = 0; u < AHEAD; ++u) {
-    store_stage(u, u, kR[u], vR[u]);
-    load_stage(u + AHEAD, kR[u], vR[u]);
+    store_stage(u, u, kR[u % R], vR[u % R]);
+    load_stage(u + R, kR[u % R], vR[u % R]);
   }
   __syncthreads();
   if (active) qk(0, S[0]);
