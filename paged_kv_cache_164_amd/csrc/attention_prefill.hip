@@ -189,7 +189,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int NDT = D / 16;       // 16-dim output tiles
   constexpr int KSTAGE = D * 64;    // bytes: [D/8][32 keys][16 B]
   constexpr int VRS = 96;           // value row stride: 64 B of data + 32 B of padding (fewest
-                                    // bank conflicts of the strides measured: 64, 80, 96)
+                                    // bank conflicts of the layouts measured: strides 64, 80,
+                                    // 96, and 64 with the 16-byte chunks XOR-swizzled by row)
   constexpr int VSTAGE = D * VRS;
   constexpr int KPIECES = D * 4;    // 16-byte pieces per stage (keys and values alike)
   constexpr int PPT = (KPIECES + NT - 1) / NT;
