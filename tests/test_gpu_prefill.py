@@ -180,3 +180,49 @@ def test_kv8_cache_mixed_batch_matches_oracle(dtype, shape, P, code):
                              kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
     ok, err, ratio = within_tolerance(_as_f64(out), ref, dtype)
     assert ok, f"max err {err}, worst ratio {ratio}"
+
+
+@pytest.mark.parametrize("code", [None, "e4m3"])
+def test_stage_count_sweep(code):
+    """Requests whose keys take 1..14 stages of 32, each with a partial last stage at another
+    offset, over a cache poisoned (NaN) past every context: every position of the unrolled
+    stage loop and its tail, the stores of the prologue and of the loop, and the zeroing of
+    the last stage's values (in LDS for the prologue's stages, in registers for the loop's)."""
+    from oracle import cache_ops as OC8
+    from workloads import with_8bit_cache
+    reqs = []
+    for nst in range(1, 15):
+        L = 32 * (nst - 1) + 1 + (nst * 11) % 32    # the last stage holds 1..32 keys
+        n = 1 + (nst * 5) % min(L, 9)               # a few query rows: one tile
+        reqs.append((L - n, n))
+    kw = dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=16)
+    case = make_prefill_case(reqs, seed=420, **kw)
+    log(f"stage sweep {code}: {reqs}")
+    if code is None:
+        out, _, _ = _gpu_step(case)
+        torch.cuda.synchronize()
+        ref, _, _ = _oracle(case)
+    else:
+        case = with_8bit_cache(case, code)
+        kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+        pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
+                                  torch.from_numpy(case.slot_mapping).to(DEV), case.k_scale,
+                                  case.v_scale, code=code)
+        q = case.query.to(DEV)
+        out = torch.full_like(q, float("nan"))
+        pkv.paged_attention_prefill(out, q, kc, vc, torch.from_numpy(case.block_tables).to(DEV),
+                                    torch.from_numpy(case.context_lens).to(DEV),
+                                    torch.from_numpy(case.query_start_loc).to(DEV), case.scale,
+                                    case.max_context_len, 0, k_scale=case.k_scale,
+                                    v_scale=case.v_scale, code=code)
+        torch.cuda.synchronize()
+        kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+        OC8.reshape_and_cache_fp8(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value),
+                                  "bf16", case.slot_mapping, case.k_scale, case.v_scale)
+        ref = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
+                                 case.context_lens, case.query_start_loc, case.scale,
+                                 kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
+    got = _as_f64(out)
+    assert np.isfinite(got).all()
+    ok, err, ratio = within_tolerance(got, ref, "bf16")
+    assert ok, f"max err {err}, worst ratio {ratio}"
