@@ -30,8 +30,11 @@
 //           read is the A operand of O^T += V^T P^T with 32 keys per product, and the lane's
 //           own 8 softmax weights are its B operand without any data movement.
 // Online softmax per column in base 2 with a lazy maximum: the running maximum is only moved
-// (and the accumulators rescaled) when a stage's maximum exceeds it by more than 2^8, so most
-// stages skip the rescale; weights are rounded once to the element type, and the row sums
+// (and the accumulators rescaled) when a stage's maximum exceeds it by more than 8 (weights
+// stay below 2^8), so most stages skip the rescale.  The logit scale is applied to the query
+// before it is rounded to the element type (one more rounding of each query element), and the
+// logit products start from -m_run: the matrix cores yield the exponent of each weight, and
+// the VALU only exponentiates.  Weights are rounded once to the element type, and the row sums
 // come out of the matrix cores (a product with a ones row) from the same rounded weights.
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -255,8 +258,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     end_c[cb] = min(k1, qpos0 + qic + 1);
     const int64_t qrow = (int64_t)(row0 + qic) * Hq + kh * G + (c - qi * G);
     const uint4* qv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.query) + qrow * D * 2);
+    // the logit scale (base 2, with the key scale of an 8-bit cache) is applied to the query
+    // once, in fp32, before it is rounded back to the element type: the logit products then
+    // give base-2 logits directly and no per-logit multiply is left
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) qop[cb][kc] = qv[kc * 4 + quad];
+    for (int kc = 0; kc < KC; ++kc) {
+      float f[8];
+      unpack(DT(), qv[kc * 4 + quad], f);
+      const float sl2 = a.scale_log2;
+      qop[cb][kc] = make_uint4(pack2(DT(), f[0] * sl2, f[1] * sl2), pack2(DT(), f[2] * sl2, f[3] * sl2),
+                               pack2(DT(), f[4] * sl2, f[5] * sl2), pack2(DT(), f[6] * sl2, f[7] * sl2));
+    }
   }
   const int qi_first = (w_uniform * CB * 16) / G;  // wave-uniform, in a scalar register
   const bool active = qi_first < nqt;                       // the wave has a real column
@@ -351,14 +363,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // running maximum per column (base-2 units) and the lazy test's threshold m_run + margin
+  // Per column: the running maximum m_run (base-2 units), its negation in all four elements
+  // (the accumulator that the logit products start from, so that they yield z - m_run, the
+  // exponent of the weight, with no VALU), and the lazy test's threshold on z - m_run: -inf
+  // until the column's first maximum is taken (m_run is 0 until then), the margin after.
   float m_run[CB], m_thr[CB];
+  f32x4 negm[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) m_run[cb] = m_thr[cb] = -INFINITY;
+  for (int cb = 0; cb < CB; ++cb) {
+    m_run[cb] = 0.f;
+    m_thr[cb] = -INFINITY;
+    negm[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // A operand of the row-sum product: row 0 all ones (lanes with col == 0), other rows zero
   const uint32_t ob = (col == 0) ? one_bits(DT()) : 0u;
   const uint4 ones = make_uint4(ob, ob, ob, ob);
-  const float sl2 = a.scale_log2;
 
   // ---- the pieces of a stage's work (LDS buffer buf holds the stage)
   // S^T = K Q^T: 2 key tiles x CB column blocks, KC products each
@@ -370,22 +389,22 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int tt = 0; tt < 2; ++tt)
         ka[kc][tt] = *reinterpret_cast<const uint4*>(sk + ((kc * 4 + quad) * 32 + tt * 16 + col) * 16);
   };
+  // (the first product of each chain starts from -m_run instead of zero)
   auto qk_mma = [&](const uint4 (&ka)[KC][2], f32x4 (&S)[2][CB]) {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) S[0][cb] = S[1][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) S[tt][cb] = mma(DT(), ka[kc][tt], qop[cb][kc], S[tt][cb]);
+        for (int cb = 0; cb < CB; ++cb)
+          S[tt][cb] = mma(DT(), ka[kc][tt], qop[cb][kc], kc == 0 ? negm[cb] : S[tt][cb]);
   };
   auto qk = [&](int buf, f32x4 (&S)[2][CB]) {
     uint4 ka[KC][2];
     qk_read(buf, ka);
     qk_mma(ka, S);
   };
-  // per column and lane: the largest of the lane's 8 logits of the stage (raw units)
+  // per column and lane: the largest of the lane's 8 values z - m_run of the stage
   auto stage_max = [&](const f32x4 (&S)[2][CB], float (&mc)[CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -409,23 +428,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
           if (tt * 4 + r >= lim) S[tt][cb][r] = -INFINITY;
     }
   };
-  // lazy maximum: move it (and rescale) only when a column's stage maximum, in base-2 units,
-  // exceeds it by more than the margin; the wave takes the branch if any of its columns needs
-  // it.  The test runs on each lane's own maximum first: rounding x * scale is monotonic for a
-  // positive scale, so some lane of a column passes it exactly when the column's maximum does,
-  // and the column maximum (a cross-lane exchange) is only formed inside the rare branch.
-  auto rescale = [&](const float (&lm)[CB]) {
+  // lazy maximum: move it (and rescale) only when a column's stage maximum exceeds it by more
+  // than the margin (or at the column's first maximum); the wave takes the branch if any of its
+  // columns needs it.  The test runs on each lane's own maximum: some lane of a column passes it
+  // exactly when the column's maximum does, and the column maximum (a cross-lane exchange) is
+  // only formed inside the rare branch.  Moving m_run by d also moves the stage's values
+  // z - m_run, computed against the old m_run, by -d; later stages start from the new -m_run.
+  // At a column's first maximum its accumulators are still zero, and alpha is 0 (not exp2 of
+  // an arbitrary distance, which may overflow).
+  auto rescale = [&](const float (&lm)[CB], f32x4 (&Sc)[2][CB]) {
     bool any = false;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] * sl2 > m_thr[cb];
+    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] > m_thr[cb];
     if (__builtin_amdgcn_ballot_w64(any) != 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const float mc = column_max(lm[cb]) * sl2;
-        const float m_new = mc > m_thr[cb] ? mc : m_run[cb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[cb] - m_new);  // 0 at first (m = -inf)
-        m_run[cb] = m_new;
-        m_thr[cb] = m_new + kLazyRescale;
+        const float mc = column_max(lm[cb]);
+        const bool first = m_thr[cb] == -INFINITY;
+        const float delta = mc > m_thr[cb] ? -mc : 0.f;
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(delta);
+        m_run[cb] -= delta;
+        negm[cb] = f32x4{-m_run[cb], -m_run[cb], -m_run[cb], -m_run[cb]};
+        if (mc > m_thr[cb]) m_thr[cb] = kLazyRescale;
+        Sc[0][cb] += delta;
+        Sc[1][cb] += delta;
         lacc[cb] *= alpha;
 #pragma unroll
         for (int i = 0; i < NDT; ++i) oacc[i][cb] *= alpha;
@@ -441,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)  // v_exp_f32: weights below 2^-126 flush to 0
-          p[tt][r] = __builtin_amdgcn_exp2f(fmaf(S[tt][cb][r], sl2, -m_run[cb]));
+          p[tt][r] = __builtin_amdgcn_exp2f(S[tt][cb][r]);
       pop[cb] = make_uint4(pack2(DT(), p[0][0], p[0][1]), pack2(DT(), p[0][2], p[0][3]),
                            pack2(DT(), p[1][0], p[1][1]), pack2(DT(), p[1][2], p[1][3]));
       lacc[cb] = mma(DT(), ones, pop[cb], lacc[cb]);
@@ -471,7 +497,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     if (needs_mask(s)) mask_stage(k0 + 32 * s, Sc);
     float lm[CB];
     stage_max(Sc, lm);
-    rescale(lm);  // before the stage's weights and its P.V
+    rescale(lm, Sc);  // before the stage's weights and its P.V
     const char* sv = s_v[u % NBUF];
 #pragma unroll
     for (int i = 0; i < NDT; ++i)
