@@ -363,15 +363,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Per column: the running maximum m_run (base-2 units), its negation in all four elements
-  // (the accumulator that the logit products start from, so that they yield z - m_run, the
-  // exponent of the weight, with no VALU), and the lazy test's threshold on z - m_run: -inf
-  // until the column's first maximum is taken (m_run is 0 until then), the margin after.
-  float m_run[CB], m_thr[CB];
+  // Per column: the running maximum m_run (base-2 units), kept as its negation in all four
+  // elements of negm (the accumulator that the logit products start from, so that they yield
+  // z - m_run, the exponent of the weight, with no VALU), and the lazy test's threshold on
+  // z - m_run: -inf until the column's first maximum is taken (m_run is 0 until then), the
+  // margin after.
+  float m_thr[CB];
   f32x4 negm[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    m_run[cb] = 0.f;
     m_thr[cb] = -INFINITY;
     negm[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -447,8 +447,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         const bool first = m_thr[cb] == -INFINITY;
         const float delta = mc > m_thr[cb] ? -mc : 0.f;
         const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(delta);
-        m_run[cb] -= delta;
-        negm[cb] = f32x4{-m_run[cb], -m_run[cb], -m_run[cb], -m_run[cb]};
+        const float nm = negm[cb][0] + delta;  // -m_run moved by delta
+        negm[cb] = f32x4{nm, nm, nm, nm};
         if (mc > m_thr[cb]) m_thr[cb] = kLazyRescale;
         Sc[0][cb] += delta;
         Sc[1][cb] += delta;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<f32x4*>(&a.part_acc[sp * D + i * 16 + quad * 4]) =
             KV8 ? oacc[i][cb] * a.v_scale : oacc[i][cb];
       if (quad == 0) {
-        a.part_m[sp] = m_run[cb];
+        a.part_m[sp] = -negm[cb][0];
         a.part_l[sp] = l_tot;
       }
     }
