@@ -365,16 +365,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   }
   // Per column: the running maximum m_run (base-2 units), kept as its negation in all four
   // elements of negm (the accumulator that the logit products start from, so that they yield
-  // z - m_run, the exponent of the weight, with no VALU), and the lazy test's threshold on
-  // z - m_run: -inf until the column's first maximum is taken (m_run is 0 until then), the
-  // margin after.
-  float m_thr[CB];
+  // z - m_run, the exponent of the weight, with no VALU); m_run is 0 until the first maximum
+  // is taken.  The lazy test's threshold on z - m_run is one value for the wave: -inf before
+  // its first stage, the margin after.  Every column sees the item's first key (a piece starts
+  // at or before its tile's first query), so every column takes its first maximum in the first
+  // stage.
+  float m_thr = -INFINITY;
   f32x4 negm[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    m_thr[cb] = -INFINITY;
-    negm[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int cb = 0; cb < CB; ++cb) negm[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // A operand of the row-sum product: row 0 all ones (lanes with col == 0), other rows zero
   const uint32_t ob = (col == 0) ? one_bits(DT()) : 0u;
   const uint4 ones = make_uint4(ob, ob, ob, ob);
@@ -429,33 +428,33 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
   // lazy maximum: move it (and rescale) only when a column's stage maximum exceeds it by more
-  // than the margin (or at the column's first maximum); the wave takes the branch if any of its
+  // than the margin (or at the first stage); the wave takes the branch if any of its
   // columns needs it.  The test runs on each lane's own maximum: some lane of a column passes it
   // exactly when the column's maximum does, and the column maximum (a cross-lane exchange) is
   // only formed inside the rare branch.  Moving m_run by d also moves the stage's values
   // z - m_run, computed against the old m_run, by -d; later stages start from the new -m_run.
-  // At a column's first maximum its accumulators are still zero, and alpha is 0 (not exp2 of
-  // an arbitrary distance, which may overflow).
+  // At the first maximum the accumulators are still zero, and alpha is 0 (not exp2 of an
+  // arbitrary distance, which may overflow).
   auto rescale = [&](const float (&lm)[CB], f32x4 (&Sc)[2][CB]) {
     bool any = false;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] > m_thr[cb];
+    for (int cb = 0; cb < CB; ++cb) any |= lm[cb] > m_thr;
     if (__builtin_amdgcn_ballot_w64(any) != 0) {
+      const bool first = m_thr == -INFINITY;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const float mc = column_max(lm[cb]);
-        const bool first = m_thr[cb] == -INFINITY;
-        const float delta = mc > m_thr[cb] ? -mc : 0.f;
+        const float delta = mc > m_thr ? -mc : 0.f;
         const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(delta);
         const float nm = negm[cb][0] + delta;  // -m_run moved by delta
         negm[cb] = f32x4{nm, nm, nm, nm};
-        if (mc > m_thr[cb]) m_thr[cb] = kLazyRescale;
         Sc[0][cb] += delta;
         Sc[1][cb] += delta;
         lacc[cb] *= alpha;
 #pragma unroll
         for (int i = 0; i < NDT; ++i) oacc[i][cb] *= alpha;
       }
+      m_thr = kLazyRescale;
     }
   };
   // weights rounded to the element type (the B operand of P.V) and their sums
