@@ -146,6 +146,55 @@ def test_full_chunked_prefill_workload_sampled(P):
 
 
 @pytest.mark.parametrize("code", ["e4m3", "i8"])
+def test_full_chunked_prefill_workload_kv8_sampled(code):
+    """The chunked-prefill workload at full size over an 8-bit cache (E4M3 or INT8 codes with
+    per-cache scales): the chunk quantised into the cache, then the multi-query call; sampled
+    (row, head) pairs against the oracle over the codes, including each request's first and
+    last rows and both sides of a 64-row tile boundary."""
+    from workloads import with_8bit_cache
+    reqs = draw_prefill_requests()
+    case = with_8bit_cache(make_prefill_case(reqs), code)
+    log(f"chunked prefill workload over {code}: {case.num_tokens} rows, max context {case.max_context_len}")
+    kc, vc = case.key_cache.to(DEV), case.value_cache.to(DEV)
+    pkv.reshape_and_cache_fp8(case.new_key.to(DEV), case.new_value.to(DEV), kc, vc,
+                              torch.from_numpy(case.slot_mapping).to(DEV), case.k_scale, case.v_scale,
+                              code=code)
+    q = case.query.to(DEV)
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_prefill(out, q, kc, vc, torch.from_numpy(case.block_tables).to(DEV),
+                                torch.from_numpy(case.context_lens).to(DEV),
+                                torch.from_numpy(case.query_start_loc).to(DEV), case.scale,
+                                case.max_context_len, 0, k_scale=case.k_scale, v_scale=case.v_scale,
+                                code=code)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(6)
+    Hq = case.cfg.num_heads
+    pairs = set()
+    for b in range(len(reqs)):
+        s0, s1 = int(case.query_start_loc[b]), int(case.query_start_loc[b + 1])
+        for r in (s0, s0 + 63, s0 + 64, s1 - 1):
+            pairs.add((r, int(g.integers(Hq))))
+        for r in g.integers(s0, s1, size=4):
+            pairs.add((int(r), int(g.integers(Hq))))
+    pairs = sorted(pairs)
+    from oracle import cache_ops as OC8
+    kb, vb = storage_bits(case.key_cache).copy(), storage_bits(case.value_cache).copy()
+    write = OC8.reshape_and_cache_fp8 if code == "e4m3" else OC8.reshape_and_cache_int8
+    write(kb, vb, storage_bits(case.new_key), storage_bits(case.new_value), "bf16",
+          case.slot_mapping, case.k_scale, case.v_scale)
+    assert np.array_equal(kc.cpu().numpy(), kb) and np.array_equal(vc.cpu().numpy(), vb)
+    ref = OP.chunked_prefill(storage_bits(case.query), kb, vb, "bf16", case.block_tables,
+                             case.context_lens, case.query_start_loc, case.scale, pairs,
+                             kv_dtype=code, k_scale=case.k_scale, v_scale=case.v_scale)
+    got = _as_f64(out)
+    rows = np.array([p[0] for p in pairs])
+    heads = np.array([p[1] for p in pairs])
+    ok, err, ratio = within_tolerance(got[rows, heads], ref[rows, heads], "bf16")
+    assert ok, f"max err {err}, worst ratio {ratio}"
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("code", ["e4m3", "i8"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [0, 2, 3])
 @pytest.mark.parametrize("P", [0, 96])
