@@ -593,17 +593,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   // Steps in groups of U: the only way back to the loop head is the end of a group, so the
   // wait counters there know exactly which loads are in flight, and s is a multiple of U at
-  // every step of the group (its buffer, set and parity are those of u).
-  int s = 0;
-  for (; s + U - 1 < nst; s += U) {
+  // every step of the group (its buffer, set and parity are those of u).  The last group leaves
+  // at its first step past the end.  (One loop: a second unrolled copy for the last group kept
+  // more values live across the two and spilled three registers per lane.)
+  for (int s = 0; s < nst; s += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) copy_and_step(s + u, u);
+    for (int u = 0; u < U; ++u) {
+      if (s + u >= nst) goto stages_done;
+      copy_and_step(s + u, u);
+    }
   }
-#pragma unroll
-  for (int u = 0; u < U - 1; ++u) {
-    if (s + u >= nst) break;
-    copy_and_step(s + u, u);
-  }
+stages_done:
   if (!active) return;
 
   // ---- epilogue: lane holds O^T[d = 16 i + 4 quad + r][column]; the row sum of a column
