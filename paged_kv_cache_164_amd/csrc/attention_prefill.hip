@@ -118,11 +118,21 @@ __device__ __forceinline__ void for_each_item(const PrefillArgs& a, int b, F&& f
   int qs, n, L;
   if (!request_ok(a, b, qs, n, L) || n == 0) return;
   const int QT = a.q_tile, P = a.partition_size;
-  for (int j = (n + QT - 1) / QT - 1; j >= 0; --j) {
-    const int qpos0 = L - n + j * QT;
+  // tiles from the last to the first; the piece count floor(qpos0 / P) + 1 is carried from
+  // tile to tile (qpos0 falls by QT) instead of dividing for each tile
+  int j = (n + QT - 1) / QT - 1;
+  int qpos0 = L - n + j * QT;
+  int q = qpos0 / P, r = qpos0 - q * P;
+  for (; j >= 0; --j) {
     const int end = qpos0 + min(QT, n - j * QT);
-    const int np = qpos0 / P + 1;
+    const int np = q + 1;
     for (int p = 0; p < np; ++p) f(j, p * P, p + 1 == np ? end : (p + 1) * P);
+    qpos0 -= QT;
+    r -= QT;
+    while (r < 0) {
+      r += P;
+      --q;
+    }
   }
 }
 
@@ -138,7 +148,8 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
   // an item spans at most min(P, max_context_len) + q_tile keys
   const int span = min(a.partition_size, a.max_context_len) + a.q_tile + 1;
   auto cls = [&](int len) {
-    return kPlanClasses - 1 - min(kPlanClasses - 1, int((int64_t)len * kPlanClasses / span));
+    // 32-bit: len < span <= the largest partition + a tile (the class only orders the items)
+    return kPlanClasses - 1 - min(kPlanClasses - 1, int(uint32_t(len) * kPlanClasses / uint32_t(span)));
   };
   // a request's item count and its longest item
   auto count = [&](int b, int& longest) {
